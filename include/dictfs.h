@@ -1,0 +1,209 @@
+/*
+ * dictfs.h -- C ABI of the MI355X (gfx950) factored dictionary projection.
+ *
+ * A layer's weight W_l (d_in x d_out, rows of X are tokens) is stored as a
+ * dense dictionary D_g (d_in x k, shared by the layers of a group) times a
+ * sparse per-layer coefficient matrix C_l (k x d_out), and the layer computes
+ *     Z_l = X_l D_g,    Y_l = Z_l C_l
+ * ("DictLLM: Shared Dictionaries for Post-Training Compression", section
+ * "Prerequisites: projections, rank and calibration", Eq. (1)).  Either
+ * factor may be stored in NVFP4: 4-bit E2M1 values with one 8-bit E4M3 scale
+ * per block of sixteen values (same review, "From retained values to measured
+ * decoding"), plus one fp32 tensor scale.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees device memory.  Scratch memory is passed in as
+ *     a caller-owned workspace sized by the matching *_workspace_size call.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *     enqueue their kernels on it and return without synchronising, except
+ *     where a call says it synchronises.
+ *   - Every argument is validated before anything is enqueued; on error the
+ *     call returns a non-zero dfs_status and writes nothing.  No C++
+ *     exception crosses this boundary.  DFS_E_HIP means the HIP runtime
+ *     reported an error; dfs_last_hip_error() returns its hipError_t code.
+ *   - Base pointers of X, Y, D data, CSC arrays and NVFP4 codes must be
+ *     16-byte aligned (DFS_E_ALIGN otherwise); leading dimensions of f16
+ *     activations must be multiples of 8 elements and of f32 ones multiples of
+ *     4, so that every row stays 16-byte aligned.
+ *   - Accumulation is always fp32.  Results are deterministic run to run
+ *     (no floating-point atomics).
+ *   - Thread safety: calls hold no mutable global state beyond a per-thread
+ *     last-HIP-error code; concurrent calls on different streams are safe.
+ */
+#ifndef DICTFS_H
+#define DICTFS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFS_OK = 0,
+  DFS_E_INVALID = 1,     /* null pointer, bad dimension or leading dim, NaN/Inf input */
+  DFS_E_UNSUPPORTED = 2, /* dtype combination or layout the library does not run */
+  DFS_E_RANGE = 3,       /* k > 65536, nnz >= 2^31, capacity too small, > 16 layers */
+  DFS_E_ALIGN = 4,       /* a base pointer or leading dimension is misaligned */
+  DFS_E_WORKSPACE = 5,   /* workspace missing or too small */
+  DFS_E_HIP = 6          /* the HIP runtime returned an error */
+} dfs_status;
+
+/* Element types. */
+enum { DFS_F32 = 0, DFS_F16 = 1, DFS_NVFP4 = 2 };
+
+/* An NVFP4 tensor of n elements (device pointers):
+ *   codes[(n+1)/2]   two E2M1 codes per byte, element 2i in the low nibble;
+ *                    code bit 3 is the sign, bits 2..0 index the magnitudes
+ *                    {0, 0.5, 1, 1.5, 2, 3, 4, 6};
+ *   scales[(n+15)/16] one E4M3 (bias 7, no infinities, max 448) code per
+ *                    block of 16 consecutive elements (last block may be short);
+ *   tensor_scale[1]  fp32.
+ * Element i decodes to e2m1(code_i) * e4m3(scales[i/16]) * tensor_scale[0]. */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tensor_scale;
+} dfs_nvfp4;
+
+/* Dictionary D_g, mathematically d_in x k, stored ATOM-MAJOR: atom a (column a
+ * of D_g) is d_in contiguous elements starting at element a*ldd.  A row-major
+ * (k, d_in) tensor, i.e. D_g transposed, has exactly this layout.
+ *   dtype F16 / F32: `data` holds the elements, ldd >= d_in, ldd % 8 == 0 (F16)
+ *                    or ldd % 4 == 0 (F32).
+ *   dtype NVFP4:     `nv` holds the k*d_in elements in atom-major order,
+ *                    ldd == d_in, d_in % 32 == 0 (so each 16-block lies inside
+ *                    one atom and each atom starts on a 16-byte boundary). */
+typedef struct {
+  int32_t d_in;
+  int32_t k;
+  int32_t dtype;
+  int32_t _pad;
+  const void* data;
+  int64_t ldd;
+  dfs_nvfp4 nv;
+} dfs_dict;
+
+/* Coefficients C_l, k x d_out, column-compressed (CSC):
+ *   colptr[d_out+1] int32, colptr[0] = 0, non-decreasing, colptr[d_out] = nnz;
+ *   rowidx[nnz] uint16 atom indices, strictly increasing within a column;
+ *   values in CSC order: `vals` (F16/F32) or `nv` (NVFP4, blocks of 16 run
+ *   over the flat CSC value array and may straddle column boundaries).
+ * k <= 65536 (16-bit indices), nnz < 2^31. */
+typedef struct {
+  int32_t k;
+  int32_t d_out;
+  int64_t nnz;
+  int32_t dtype;
+  int32_t _pad;
+  const int32_t* colptr;
+  const uint16_t* rowidx;
+  const void* vals;
+  dfs_nvfp4 nv;
+} dfs_csc;
+
+/* ---------------------------------------------------------------------- */
+/* Packing                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* Workspace bytes dict_pack_csc needs for a k x d_out matrix. */
+dfs_status dict_pack_csc_workspace_size(int32_t k, int32_t d_out, size_t* bytes);
+
+/* Dense row-major C (k x d_out, leading dimension ldc >= d_out, dtype F16 or
+ * F32, device) -> CSC.  Column j keeps the rows r, in ascending order, whose
+ * entry compares unequal to zero (+0 and -0 are dropped, NaN is kept); the
+ * row goes to rowidx as uint16 and the value is bit-copied to vals (same
+ * dtype as C).  This is the support-keeping export of the coefficients
+ * ("DictLLM: Shared Dictionaries for Post-Training Compression", Algorithm 2:
+ * export of dictionary, codes, scales and support, zeros preserved).
+ *   rowidx == NULL and vals == NULL: fill colptr[d_out+1] and *nnz_host only.
+ *   otherwise: fill colptr, rowidx, vals; capacity (elements of rowidx/vals)
+ *   < nnz gives DFS_E_RANGE with colptr written and rowidx/vals untouched.
+ * Synchronises `stream` to return *nnz_host (host pointer, required). */
+dfs_status dict_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out, int64_t ldc,
+                         int32_t* colptr, uint16_t* rowidx, void* vals, int64_t capacity,
+                         int64_t* nnz_host, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes nvfp4_pack needs for n elements. */
+dfs_status nvfp4_pack_workspace_size(int64_t n, size_t* bytes);
+
+/* Quantise x[0..n) (fp32, device) to NVFP4 (see dfs_nvfp4).  Recipe, applied
+ * with correctly rounded fp32 operations:
+ *   amax = max|x|;  ts = amax / 2688 (= 6 * 448), or 1 if that is 0;
+ *   per block b: sf = amax_b / (6 * ts); scale code = E4M3 nearest to sf,
+ *     ties to even, saturating at 448; s = its value; denom = s * ts;
+ *   per element: magnitude code = E2M1 nearest to |x / denom| (ties to even,
+ *     saturating at 6; 0 when denom == 0), sign bit = sign bit of x.
+ * x holding NaN or Inf gives DFS_E_INVALID and writes nothing; detecting it
+ * synchronises `stream`.  out.codes needs 16-byte alignment. */
+dfs_status nvfp4_pack(const float* x, int64_t n, dfs_nvfp4 out, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Decode n NVFP4 elements to fp32: y[i] = (e2m1 * e4m3) * tensor_scale, one
+ * fp32 rounding (the first product is exact). */
+dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Forward                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* Workspace bytes for dict_group_forward over n_layers layers of T tokens
+ * (dict_proj_forward: n_layers = 1).  D and C describe the shapes and dtypes
+ * (C may point at any one layer's descriptor; only k/d_out/dtype are read). */
+dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, const dfs_csc* C,
+                               size_t* bytes);
+
+/* One factored projection, Eq. (1): Z = X D_g, Y = Z C_l.
+ *   X: T x d_in row-major, leading dimension ldx, dtype F16 or F32.
+ *   Y: T x d_out row-major, leading dimension ldy, dtype F16 or F32.
+ *   T = 0 is a no-op.  The intermediate Z (T x k) lives in the workspace. */
+dfs_status dict_proj_forward(const void* X, int32_t xdt, int32_t T, int64_t ldx, const dfs_dict* D,
+                             const dfs_csc* C, void* Y, int32_t ydt, int64_t ldy, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* The projections of one layer group that share D_g
+ * (same review, Figure 2: one dictionary, separate activations and codes):
+ * for l in [0, n_layers): Y[l] = (X[l] D_g) C[l].  The n_layers * T rows are
+ * contracted against D_g in one pass, so D_g is read from memory once per
+ * group rather than once per layer; then one launch applies every C_l.
+ *   X, Y: host arrays of n_layers device pointers; C: host array of n_layers
+ *   descriptors sharing k and d_out.  1 <= n_layers <= 16 (the largest
+ *   group the pages study). */
+dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xdt, int32_t T,
+                              int64_t ldx, const dfs_dict* D, const dfs_csc* C, void* const* Y,
+                              int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
+/* The first half of Eq. (1) alone: Z = X D_g for every layer of a group.
+ * Z is (n_layers*T) x k row-major (row l*T + t), dtype F32 or F16, 16-byte
+ * aligned.  Dense-product choice: VALU dot products for n_layers*T <= 16 rows,
+ * MFMA tiles above that (F16 or NVFP4 dictionary, F16 activations). */
+dfs_status dict_xd_forward(int32_t n_layers, const void* const* X, int32_t xdt, int32_t T,
+                           int64_t ldx, const dfs_dict* D, void* Z, int32_t zdt, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Workspace bytes dict_xd_forward needs (non-zero only for an NVFP4
+ * dictionary on the MFMA path, which expands D_g to f16 first). */
+dfs_status dict_xd_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, size_t* bytes);
+
+/* The second half of Eq. (1) alone: Y[l] = Z_l C[l], Z as written by
+ * dict_xd_forward (row l*T + t of a (n_layers*T) x k array, dtype zdt). */
+dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t T,
+                           const dfs_csc* C, void* const* Y, int32_t ydt, int64_t ldy,
+                           void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Diagnostics                                                            */
+/* ---------------------------------------------------------------------- */
+
+const char* dfs_status_str(dfs_status s);
+/* hipError_t of the last DFS_E_HIP returned on this thread (0 if none). */
+int32_t dfs_last_hip_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t dfs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DICTFS_H */

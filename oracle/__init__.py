@@ -1,0 +1,228 @@
+"""CPU oracle for the factored dictionary projection (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP
+library: it loads ``oracle/liboracle.so`` (built from ``oracle/oracle.c`` by
+``oracle/build.py``) and marshals numpy arrays.
+
+Pages (cited by title and section):
+  Review: "DictLLM: Shared Dictionaries for Post-Training Compression".
+
+* ``forward`` -- Eq. (1) of the Review ("Prerequisites: projections, rank and
+  calibration"): Z = X D, Y = Z C, float64, sums in ascending index order.
+* ``pack_csc`` -- support-keeping export of C (Review, Algorithm 2: export of
+  dictionary, codes, scales and support; zeros preserved as absent).
+* ``nvfp4_pack``/``nvfp4_unpack`` -- 4-bit E2M1 values with one 8-bit E4M3
+  scale per 16 values (Review, "From retained values to measured decoding")
+  and one fp32 tensor scale.  The scale recipe is a reading; parity unpinned
+  against the pages, pinned against format definitions and bounds.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+DT_F32, DT_F16, DT_NVFP4 = 0, 1, 2   # element-type codes of oracle.c
+
+
+class _Tensor(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("data", C.c_void_p), ("codes", C.c_void_p),
+                ("scales", C.c_void_p), ("ts", C.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, building it first if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = C.CDLL(_LIB_PATH)
+        L.orc_half_value.restype = C.c_double
+        L.orc_half_value.argtypes = [C.c_uint16]
+        L.orc_e2m1_value.restype = C.c_double
+        L.orc_e2m1_value.argtypes = [C.c_int]
+        L.orc_e4m3_value.restype = C.c_double
+        L.orc_e4m3_value.argtypes = [C.c_int]
+        L.orc_e4m3_nearest.restype = C.c_int
+        L.orc_e4m3_nearest.argtypes = [C.c_float]
+        L.orc_e2m1_nearest.restype = C.c_int
+        L.orc_e2m1_nearest.argtypes = [C.c_float]
+        L.orc_nvfp4_tensor_scale.restype = C.c_float
+        L.orc_nvfp4_tensor_scale.argtypes = [C.c_float]
+        L.orc_nvfp4_pack.restype = C.c_int
+        L.orc_nvfp4_pack.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                     C.POINTER(C.c_float)]
+        L.orc_nvfp4_unpack.restype = None
+        L.orc_nvfp4_unpack.argtypes = [C.c_void_p, C.c_void_p, C.c_float, C.c_int64,
+                                       C.c_void_p]
+        L.orc_pack_csc.restype = C.c_int64
+        L.orc_pack_csc.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int64,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64]
+        L.orc_forward.restype = C.c_int
+        L.orc_forward.argtypes = [C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
+                                  C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
+                                  C.c_void_p, C.c_void_p, C.POINTER(_Tensor), C.c_void_p]
+        L.orc_max_threads.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+# ---------------------------------------------------------------- formats
+
+def half_value(bits: int) -> float:
+    return lib().orc_half_value(int(bits))
+
+
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(int(code))
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(int(code))
+
+
+def e4m3_nearest(s: float) -> int:
+    return lib().orc_e4m3_nearest(float(np.float32(s)))
+
+
+def e2m1_nearest(v: float) -> int:
+    return lib().orc_e2m1_nearest(float(np.float32(v)))
+
+
+def nvfp4_tensor_scale(amax: float) -> float:
+    return lib().orc_nvfp4_tensor_scale(float(np.float32(amax)))
+
+
+@dataclass
+class NVFP4:
+    """An NVFP4 tensor of ``n`` elements: packed codes, block scales, ts."""
+    codes: np.ndarray   # uint8[(n+1)//2], element 2i in the low nibble
+    scales: np.ndarray  # uint8[(n+15)//16], E4M3 codes
+    ts: float           # fp32 tensor scale
+    n: int
+
+
+def nvfp4_pack(x: np.ndarray) -> NVFP4:
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    n = x.size
+    codes = np.zeros((n + 1) // 2, np.uint8)
+    scales = np.zeros((n + 15) // 16, np.uint8)
+    ts = C.c_float(0.0)
+    rc = lib().orc_nvfp4_pack(_ptr(x), n, _ptr(codes), _ptr(scales), C.byref(ts))
+    if rc != 0:
+        raise ValueError("nvfp4_pack: input holds NaN or Inf")
+    return NVFP4(codes, scales, float(ts.value), n)
+
+
+def nvfp4_unpack(q: NVFP4) -> np.ndarray:
+    y = np.empty(q.n, np.float32)
+    lib().orc_nvfp4_unpack(_ptr(q.codes), _ptr(q.scales), q.ts, q.n, _ptr(y))
+    return y
+
+
+# ---------------------------------------------------------------- CSC
+
+@dataclass
+class CSC:
+    """k x d_out coefficient matrix, column-compressed.
+
+    ``vals`` is a float16/float32 array (bit copies of the dense entries) or
+    an ``NVFP4`` holding the values in CSC order."""
+    k: int
+    d_out: int
+    colptr: np.ndarray  # int32[d_out+1]
+    rowidx: np.ndarray  # uint16[nnz]
+    vals: object
+
+    @property
+    def nnz(self) -> int:
+        return int(self.colptr[-1])
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.float16:
+        return DT_F16
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def pack_csc(Cd: np.ndarray) -> CSC:
+    """Dense row-major k x d_out (float16/float32) -> canonical CSC."""
+    Cd = np.ascontiguousarray(Cd)
+    k, d_out = Cd.shape
+    dt = _dtype_code(Cd)
+    colptr = np.zeros(d_out + 1, np.int32)
+    nnz = lib().orc_pack_csc(_ptr(Cd), dt, k, d_out, d_out, _ptr(colptr), None, None, 0)
+    rowidx = np.zeros(max(nnz, 1), np.uint16)
+    vals = np.zeros(max(nnz, 1), Cd.dtype)
+    got = lib().orc_pack_csc(_ptr(Cd), dt, k, d_out, d_out, _ptr(colptr), _ptr(rowidx),
+                             _ptr(vals), nnz)
+    assert got == nnz
+    return CSC(k, d_out, colptr, rowidx[:nnz], vals[:nnz])
+
+
+def csc_to_nvfp4(c: CSC) -> CSC:
+    """Quantise a CSC's values (in CSC order) to NVFP4; support unchanged."""
+    return CSC(c.k, c.d_out, c.colptr, c.rowidx,
+               nvfp4_pack(np.asarray(c.vals, np.float32)))
+
+
+# ---------------------------------------------------------------- forward
+
+def _tensor(t, keep: list) -> _Tensor:
+    if isinstance(t, NVFP4):
+        keep.extend([t.codes, t.scales])
+        return _Tensor(DT_NVFP4, None, _ptr(t.codes), _ptr(t.scales), t.ts)
+    a = np.ascontiguousarray(t)
+    keep.append(a)
+    return _Tensor(_dtype_code(a), _ptr(a), None, None, 0.0)
+
+
+def forward(X: np.ndarray, D, d_in: int, c: CSC) -> np.ndarray:
+    """Y = (X D) C in float64.
+
+    X: T x d_in (float16/float32).  D: the dictionary stored atom by atom,
+    i.e. a k x d_in array (row a is atom a) or an ``NVFP4`` of the k*d_in
+    elements in that order.  c: ``CSC``.  Returns T x d_out float64."""
+    X = np.ascontiguousarray(X)
+    T = X.shape[0]
+    assert X.shape[1] == d_in
+    keep: list = []
+    tx = _tensor(X, keep)
+    td = _tensor(D, keep)
+    tc = _tensor(c.vals, keep)
+    colptr = np.ascontiguousarray(c.colptr, np.int32)
+    rowidx = np.ascontiguousarray(c.rowidx, np.uint16)
+    if rowidx.size == 0:
+        rowidx = np.zeros(1, np.uint16)
+    Y = np.zeros((T, c.d_out), np.float64)
+    rc = lib().orc_forward(T, C.byref(tx), d_in, d_in, c.k, C.byref(td), d_in, c.d_out,
+                           _ptr(colptr), _ptr(rowidx), C.byref(tc), _ptr(Y))
+    if rc != 0:
+        raise MemoryError("oracle forward: allocation failed")
+    return Y
+
+
+def group_forward(Xs, D, d_in: int, cs) -> list:
+    """The group's layers share D; each layer has its own X_l and C_l
+    (Review, Figure 2: shared weights with separate activations)."""
+    return [forward(X, D, d_in, c) for X, c in zip(Xs, cs)]
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())

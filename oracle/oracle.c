@@ -1,0 +1,288 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the factored dictionary projection.
+ *
+ * TEST INFRASTRUCTURE.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The HIP library never
+ * calls it, and the two share no source, header, table or helper.
+ *
+ * Pages followed (cited by title and section):
+ *   [Review]    "DictLLM: Shared Dictionaries for Post-Training Compression"
+ *               (technical review of the DictLLM paper).
+ *   [Explainer] "DictLLM compresses LLaMA-7B 5.1x -- Shared dictionary plus
+ *               sparse coefficients -- What does it mean?"
+ *   [Tables]    "DictLLM: Post-training Compression of Large Language Model
+ *               with Dictionary Kernels" (figures and tables page).
+ *
+ * What it computes:
+ *   forward    Y = (X D) C evaluated in float64 exactly as written in
+ *              [Review] "Prerequisites: projections, rank and calibration",
+ *              Eq. (1): Z = X D (sum over d_in, ascending), then
+ *              Y[t,j] = sum over the stored entries of column j, ascending.
+ *   pack_csc   Column-compressed export of a dense coefficient matrix that
+ *              keeps the support and drops zeros ([Review] Algorithm 2, the
+ *              export of dictionary, codes, scales and support).
+ *   nvfp4      4-bit E2M1 values with one 8-bit (E4M3) scale per block of
+ *              sixteen consecutive values ([Review] "From retained values to
+ *              measured decoding"; [Tables] Table 4) plus one fp32 tensor
+ *              scale.  The scale recipe below is a reading, not printed on
+ *              the pages (parity unpinned against the pages; pinned against
+ *              format definitions, brute force and error bounds).
+ *
+ * Every floating-point step that decides an integer code is done in fp32,
+ * each operation correctly rounded (compile with -ffp-contract=off, no
+ * -ffast-math).  Everything else is float64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_F16 1
+#define ORC_NVFP4 2
+
+/* A read-only view of a stored tensor (flat element index). */
+typedef struct {
+  int32_t dtype;        /* ORC_F32, ORC_F16 or ORC_NVFP4 */
+  const void* data;     /* f32 / f16 elements (unused for NVFP4) */
+  const uint8_t* codes; /* NVFP4: two 4-bit codes per byte, element 2i low */
+  const uint8_t* scales;/* NVFP4: one E4M3 code per 16 elements */
+  float ts;             /* NVFP4: fp32 tensor scale */
+} orc_tensor;
+
+/* IEEE 754 binary16, decoded from its definition: sign, 5-bit exponent with
+ * bias 15, 10-bit fraction; exponent 0 is subnormal. */
+double orc_half_value(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp(1024.0 + m, e - 25);
+  return s ? -v : v;
+}
+
+/* E2M1: sign, 2-bit exponent (bias 1), 1-bit mantissa, no inf/NaN.
+ * Exponent 0 is subnormal (0 or 0.5). */
+double orc_e2m1_value(int code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -mag : mag;
+}
+
+/* E4M3 ("fn" variant): sign, 4-bit exponent (bias 7), 3-bit mantissa; no
+ * infinities; exponent 15 with mantissa 7 is NaN; exponent 0 subnormal. */
+double orc_e4m3_value(int code) {
+  int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m, -9);
+  else
+    mag = ldexp(8.0 + m, e - 10);
+  return s ? -mag : mag;
+}
+
+/* Nearest non-negative finite E4M3 code to s >= 0 (values beyond 448 take
+ * 448), ties to the even code.  Brute force over the 127 candidates; every
+ * difference is exact in float64 for fp32 s in the range that can tie. */
+int orc_e4m3_nearest(float s) {
+  int best = 0;
+  double bestd = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs((double)s - orc_e4m3_value(c));
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* Nearest E2M1 magnitude code (0..7) to |v|, ties to the even code,
+ * values beyond 6 take 6.  Brute force over the 8 candidates. */
+int orc_e2m1_nearest(float v) {
+  double a = fabs((double)v);
+  int best = 0;
+  double bestd = INFINITY;
+  for (int c = 0; c <= 7; ++c) {
+    double d = fabs(a - orc_e2m1_value(c));
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* Tensor scale rule: amax / (6 * 448), so that the largest block scale is
+ * the largest finite E4M3 value; 1 when that quotient is 0. */
+float orc_nvfp4_tensor_scale(float amax) {
+  float ts = amax / 2688.0f;
+  return ts == 0.0f ? 1.0f : ts;
+}
+
+/* Quantise x[0..n) to NVFP4.  Returns 0, or -1 (nothing written) if x holds
+ * a NaN or an infinity.  codes[(n+1)/2], scales[(n+15)/16]. */
+int orc_nvfp4_pack(const float* x, int64_t n, uint8_t* codes, uint8_t* scales,
+                   float* ts_out) {
+  if (n < 0) return -1;
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    if (!isfinite(x[i])) return -1;
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  float ts = orc_nvfp4_tensor_scale(amax);
+  memset(codes, 0, (size_t)((n + 1) / 2));
+  int64_t nb = (n + 15) / 16;
+  for (int64_t b = 0; b < nb; ++b) {
+    int64_t lo = 16 * b, hi = lo + 16 < n ? lo + 16 : n;
+    float bmax = 0.0f;
+    for (int64_t i = lo; i < hi; ++i) {
+      float a = fabsf(x[i]);
+      if (a > bmax) bmax = a;
+    }
+    float six_ts = 6.0f * ts;
+    float sf = bmax / six_ts;               /* wanted block scale */
+    int sc = orc_e4m3_nearest(sf);          /* stored 8-bit scale */
+    float s = (float)orc_e4m3_value(sc);    /* exact */
+    float denom = s * ts;                   /* one fp32 rounding */
+    scales[b] = (uint8_t)sc;
+    for (int64_t i = lo; i < hi; ++i) {
+      int mag = 0;
+      if (denom != 0.0f) {
+        float v = x[i] / denom;             /* one fp32 rounding */
+        mag = orc_e2m1_nearest(v);
+      }
+      int code = mag | (signbit(x[i]) ? 8 : 0);
+      codes[i / 2] |= (uint8_t)((i & 1) ? (code << 4) : code);
+    }
+  }
+  *ts_out = ts;
+  return 0;
+}
+
+static int nibble(const uint8_t* codes, int64_t i) {
+  return (i & 1) ? (codes[i / 2] >> 4) & 15 : codes[i / 2] & 15;
+}
+
+/* y[i] = e2m1(code_i) * e4m3(scale_{i/16}) * ts: the product is exact in
+ * float64 (2 + 4 + 24 significant bits), then rounded once to fp32. */
+void orc_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, float ts,
+                      int64_t n, float* y) {
+  for (int64_t i = 0; i < n; ++i)
+    y[i] = (float)(orc_e2m1_value(nibble(codes, i)) *
+                   orc_e4m3_value(scales[i / 16]) * (double)ts);
+}
+
+/* Exact float64 value of stored element i. */
+static double elem(const orc_tensor* t, int64_t i) {
+  switch (t->dtype) {
+    case ORC_F32:
+      return (double)((const float*)t->data)[i];
+    case ORC_F16:
+      return orc_half_value(((const uint16_t*)t->data)[i]);
+    default:
+      return orc_e2m1_value(nibble(t->codes, i)) *
+             orc_e4m3_value(t->scales[i / 16]) * (double)t->ts;
+  }
+}
+
+/* Dense row-major C (k x d_out, leading dimension ldc, dtype F32 or F16) to
+ * CSC: for each column j, rows r ascending, keep C[r,j] iff it compares
+ * unequal to zero (so +-0 are dropped and NaN is kept); the row index is
+ * stored as uint16 and the value bit-copied.  colptr[0] = 0,
+ * colptr[j+1] = colptr[j] + count_j.  Returns nnz, or -1 if nnz exceeds
+ * capacity (then only colptr is written).  rowidx == NULL: colptr only. */
+int64_t orc_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out,
+                     int64_t ldc, int32_t* colptr, uint16_t* rowidx, void* vals,
+                     int64_t capacity) {
+  orc_tensor t = {dtype, C, NULL, NULL, 0.0f};
+  int64_t nnz = 0;
+  colptr[0] = 0;
+  for (int32_t j = 0; j < d_out; ++j) {
+    for (int32_t r = 0; r < k; ++r)
+      if (elem(&t, (int64_t)r * ldc + j) != 0.0) ++nnz;
+    colptr[j + 1] = (int32_t)nnz;
+  }
+  if (rowidx == NULL) return nnz;
+  if (nnz > capacity) return -1;
+  int64_t p = 0;
+  size_t esz = dtype == ORC_F32 ? 4 : 2;
+  for (int32_t j = 0; j < d_out; ++j)
+    for (int32_t r = 0; r < k; ++r) {
+      int64_t src = (int64_t)r * ldc + j;
+      if (elem(&t, src) != 0.0) {
+        rowidx[p] = (uint16_t)r;
+        memcpy((char*)vals + p * esz, (const char*)C + src * esz, esz);
+        ++p;
+      }
+    }
+  return nnz;
+}
+
+/* Factored projection, Eq. (1) of [Review]:
+ *   Z[t,a] = sum_{i=0..d_in-1} X[t,i] * D[i,a]        (i ascending)
+ *   Y[t,j] = sum_{p=colptr[j]..colptr[j+1]-1} Z[t,rowidx[p]] * C_p  (p asc.)
+ * X: T x d_in row-major (leading dim ldx).  D: d_in x k stored atom by atom
+ * (element (i,a) at flat index a*ldd + i).  C: k x d_out in CSC.
+ * Y: T x d_out row-major float64, leading dimension d_out.
+ * Returns 0, or -1 on allocation failure. */
+int orc_forward(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_in,
+                int32_t k, const orc_tensor* D, int64_t ldd, int32_t d_out,
+                const int32_t* colptr, const uint16_t* rowidx,
+                const orc_tensor* C, double* Y) {
+  if (T <= 0) return 0;
+  double* Z = (double*)malloc(sizeof(double) * (size_t)T * (size_t)k);
+  double* Xd = (double*)malloc(sizeof(double) * (size_t)T * (size_t)d_in);
+  if (!Z || !Xd) {
+    free(Z);
+    free(Xd);
+    return -1;
+  }
+  for (int32_t t = 0; t < T; ++t)
+    for (int32_t i = 0; i < d_in; ++i)
+      Xd[(size_t)t * d_in + i] = elem(X, (int64_t)t * ldx + i);
+
+#pragma omp parallel
+  {
+    double* atom = (double*)malloc(sizeof(double) * (size_t)d_in);
+#pragma omp for schedule(static)
+    for (int32_t a = 0; a < k; ++a) {
+      for (int32_t i = 0; i < d_in; ++i) atom[i] = elem(D, (int64_t)a * ldd + i);
+      for (int32_t t = 0; t < T; ++t) {
+        const double* x = Xd + (size_t)t * d_in;
+        double sum = 0.0;
+        for (int32_t i = 0; i < d_in; ++i) sum += x[i] * atom[i];
+        Z[(size_t)t * k + a] = sum;
+      }
+    }
+    free(atom);
+  }
+
+#pragma omp parallel for schedule(static)
+  for (int32_t j = 0; j < d_out; ++j)
+    for (int32_t t = 0; t < T; ++t) {
+      double sum = 0.0;
+      for (int32_t p = colptr[j]; p < colptr[j + 1]; ++p)
+        sum += Z[(size_t)t * k + rowidx[p]] * elem(C, p);
+      Y[(size_t)t * d_out + j] = sum;
+    }
+
+  free(Z);
+  free(Xd);
+  return 0;
+}
+
+/* Threads the OpenMP runtime will use for the parallel loops above. */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
