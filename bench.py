@@ -1,0 +1,258 @@
+"""Benchmark of the factored projection on one MI355X.
+
+Headline workload: the LLaMA-7B q_proj-shaped decode group -- 2 layers sharing
+one dictionary, d_in = d_out = 4096, k = 2048, C fp16 at 30% unstructured
+density in CSC with uint16 row indices, 1 fp16 token per layer.  One step is
+one dict_group_forward over the group (Z = X D_g for both layers in one pass
+over D_g, then Y_l = Z_l C_l for both layers in one launch).
+
+Inputs are resident in HBM before timing starts.  To measure HBM rather than
+the 256 MB MALL, every step uses the next of R replicas of (D_g, C_1, C_2)
+whose total exceeds 1.2 GB (same bytes, different addresses).  K steps are
+captured in a HIP graph and replayed; the timed region is bracketed by
+torch.cuda.synchronize().
+
+value = algorithmic bytes per step (D once, both C's, X's and Y's; Z not
+counted) / seconds per step, in GB/s.  The roofline object reports the
+dominant kernel alone, timed with HIP events on the launch stream over K
+back-to-back launches.  cpu_baseline times the oracle (CPU, float64) on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs and HBM GB/s per factored projection (b=1 decode); TFLOP/s at prefill"
+HBM_PEAK_GBS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the factored projection is measured on one "
+              "MI355X (see DESIGN.md for how it would shard); --gpus must be 1.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from dictionary_factored_sparse_amd import binding as B
+    from dictionary_factored_sparse_amd import ledger as L
+    from dictionary_factored_sparse_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    g = synth.make_group("qproj")
+    D0 = B.to_device_dict(g.D, dev)
+    C0 = [B.to_device_csc(Cd, dev) for Cd in g.Cs]
+    Xs = [torch.from_numpy(X).to(dev) for X in g.Xs]
+    nnzs = [c.nnz for c in C0]
+    step_bytes = L.group_bytes(d_in=g.d_in, d_out=g.d_out, k=g.k, T=g.T, nnzs=nnzs, wdtype="f16",
+                               cdtype="f16", xdtype="f16", ydtype="f16")
+    xd_bytes = L.dict_bytes(g.d_in, g.k, "f16") + sum(L.act_bytes(g.T, g.d_in, "f16") for _ in nnzs)
+    zc_bytes = sum(L.csc_bytes(g.d_out, n, "f16") + L.act_bytes(g.T, g.d_out, "f16") for n in nnzs)
+    R = max(2, math.ceil(1.2e9 / step_bytes))
+    reps = []
+    for r in range(R):
+        D = B.DeviceDict(g.d_in, g.k, data=D0.data.clone())
+        Cs = [B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(), vals=c.vals.clone())
+              for c in C0]
+        reps.append((D, Cs))
+    Ys = [torch.empty(g.T, g.d_out, dtype=torch.float16, device=dev) for _ in range(2)]
+    ws = B.workspace(2, g.T, D0, C0[0], dev)
+    Z = torch.empty(2 * g.T, g.k, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    _log(f"inputs ready in {time.time() - t0:.1f}s: {R} replicas x {step_bytes / 1e6:.2f} MB")
+
+    def step(i):
+        D, Cs = reps[i % R]
+        B.dict_group_forward(Xs, D, Cs, Ys=Ys, ws=ws)
+
+    # eager reference result (deterministic kernels: every replay must match)
+    step(0)
+    torch.cuda.synchronize()
+    Y_ref = [y.clone() for y in Ys]
+
+    # ---------------------------------------------------------------- graph timing
+    def capture(fn, n):
+        gr = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)  # warm the launch path on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for i in range(n):
+                fn(i)
+        return gr
+
+    K, W = args.steps, args.warmup
+    g_main = capture(step, K)
+    for _ in range(max(1, W // max(K, 1) + 1)):
+        g_main.replay()
+    torch.cuda.synchronize()
+    for y, yr in zip(Ys, Y_ref):
+        assert torch.equal(y, yr), "graph replay differs from the eager result"
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    g_main.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / K
+    for y, yr in zip(Ys, Y_ref):
+        assert torch.equal(y, yr), "graph replay differs from the eager result"
+
+    # eager launches (host launch path included), for information
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(K):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step_eager = ev0.elapsed_time(ev1) / K
+
+    # ---------------------------------------------------------------- per kernel
+    def xd(i):
+        D, _ = reps[i % R]
+        B.dict_xd_forward(Xs, D, Z=Z)
+
+    def zc(i):
+        _, Cs = reps[i % R]
+        B.dict_zc_forward(Z, g.T, Cs, Ys=Ys)
+
+    kern = {}
+    for name, fn, nbytes in (("gemv_xd", xd, xd_bytes), ("spmv_csc", zc, zc_bytes)):
+        gr = capture(fn, K)
+        gr.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        gr.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) / K * 1e3
+        kern[name] = dict(us=us, bytes=nbytes, gbs=nbytes / (us * 1e-6) / 1e9)
+        _log(f"{name}: {us:.2f} us/launch, {kern[name]['gbs']:.0f} GB/s")
+    dom = max(kern, key=lambda n: kern[n]["us"])
+
+    # ---------------------------------------------------------------- prefill (extra)
+    extras = {}
+    if not args.no_prefill:
+        gp = synth.make_group("qproj_prefill")
+        Xp = [torch.from_numpy(X).to(dev) for X in gp.Xs]
+        Zp = torch.empty(2 * gp.T, gp.k, dtype=torch.float16, device=dev)
+        Yp = [torch.empty(gp.T, gp.d_out, dtype=torch.float16, device=dev) for _ in range(2)]
+        wsp = B.workspace(2, gp.T, D0, C0[0], dev)
+        reps_p = min(R, 8)
+        nrep = 10
+        res = {}
+        for name, fn in (
+                ("gemm_xd_mfma", lambda i: B.dict_xd_forward(Xp, reps[i % reps_p][0], Z=Zp)),
+                ("spmm_csc", lambda i: B.dict_zc_forward(Zp, gp.T, reps[i % reps_p][1], Ys=Yp)),
+                ("group_forward", lambda i: B.dict_group_forward(Xp, reps[i % reps_p][0],
+                                                                 reps[i % reps_p][1], Ys=Yp,
+                                                                 ws=wsp))):
+            gr = capture(fn, nrep)
+            gr.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            gr.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            res[name] = ev0.elapsed_time(ev1) / nrep
+        gemm_flop, spmm_flop = L.group_flops(d_in=gp.d_in, k=gp.k, T=gp.T, nnzs=nnzs)
+        extras["prefill_T2048_group2"] = {
+            "gemm_xd_mfma_us": round(res["gemm_xd_mfma"] * 1e3, 2),
+            "gemm_tflops": round(gemm_flop / (res["gemm_xd_mfma"] * 1e-3) / 1e12, 1),
+            "gemm_frac_of_fp16_mfma_peak": round(
+                gemm_flop / (res["gemm_xd_mfma"] * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+            "spmm_csc_us": round(res["spmm_csc"] * 1e3, 2),
+            "spmm_useful_tflops": round(spmm_flop / (res["spmm_csc"] * 1e-3) / 1e12, 2),
+            "group_forward_ms": round(res["group_forward"], 4),
+        }
+        _log(f"prefill: {extras['prefill_T2048_group2']}")
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+        cs = [O.pack_csc(Cd) for Cd in g.Cs]
+        n_done, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and n_done < 10000:
+            t1 = time.perf_counter()
+            O.group_forward(g.Xs, g.D, g.d_in, cs)
+            t_cpu += time.perf_counter() - t1
+            n_done += 1
+        cpu = {"value": round(step_bytes * n_done / t_cpu / 1e9, 3), "unit": "GB/s",
+               "cores": O.max_threads(), "kind": "oracle",
+               "sample": f"{n_done} group forwards of the same q_proj decode group "
+                         f"(float64 oracle, {t_cpu:.1f} s)"}
+        _log(f"cpu oracle: {cpu}")
+
+    d = kern[dom]
+    out = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_projection": round(ms_step * 1e3 / 2, 3),
+        "eager_ms_per_step": round(ms_step_eager, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "q_proj decode group: 2 layers, d_in=d_out=4096, k=2048, "
+                               "C density 0.30 CSC uint16 f16, T=1 f16",
+                   "bytes_per_step": step_bytes, "replicas": R, "timing": "hip graph replay"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(d["gbs"], 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(d["us"], 3), "bytes_per_launch": d["bytes"]},
+        "kernels": {n: {"us_per_launch": round(v["us"], 3), "GB/s": round(v["gbs"], 1)}
+                    for n, v in kern.items()},
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,337 @@
+"""Thin ctypes binding of ``libdictfs.so`` (C ABI in include/dictfs.h).
+
+Argument marshalling only: every step of the projection runs in the HIP
+library.  Device memory and streams come from PyTorch (tensors on a ROCm
+device; the current torch stream is passed as the hipStream_t).  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+
+The functions carry the C names.  Small holder classes (``DeviceDict``,
+``DeviceCSC``, ``DeviceNVFP4``) keep the tensors a descriptor points at alive.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdictfs.so")
+
+DFS_F32, DFS_F16, DFS_NVFP4 = 0, 1, 2
+STATUS = {0: "DFS_OK", 1: "DFS_E_INVALID", 2: "DFS_E_UNSUPPORTED", 3: "DFS_E_RANGE",
+          4: "DFS_E_ALIGN", 5: "DFS_E_WORKSPACE", 6: "DFS_E_HIP"}
+
+# symbols declared in include/dictfs.h
+SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspace_size",
+           "nvfp4_pack", "nvfp4_unpack", "dict_workspace_size", "dict_proj_forward",
+           "dict_group_forward", "dict_xd_forward", "dict_xd_workspace_size", "dict_zc_forward",
+           "dfs_status_str", "dfs_last_hip_error", "dfs_version")
+
+
+class NV(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("tensor_scale", C.c_void_p)]
+
+
+class Dict(C.Structure):
+    _fields_ = [("d_in", C.c_int32), ("k", C.c_int32), ("dtype", C.c_int32), ("_pad", C.c_int32),
+                ("data", C.c_void_p), ("ldd", C.c_int64), ("nv", NV)]
+
+
+class Csc(C.Structure):
+    _fields_ = [("k", C.c_int32), ("d_out", C.c_int32), ("nnz", C.c_int64), ("dtype", C.c_int32),
+                ("_pad", C.c_int32), ("colptr", C.c_void_p), ("rowidx", C.c_void_p),
+                ("vals", C.c_void_p), ("nv", NV)]
+
+
+class DfsError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        self.hip_error = int(lib().dfs_last_hip_error()) if status == 6 else 0
+        msg = lib().dfs_status_str(status).decode()
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})"
+                         + (f", hipError {self.hip_error}" if self.hip_error else ""))
+
+
+_lib = None
+
+
+def lib():
+    """Load libdictfs.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        psz = C.POINTER(C.c_size_t)
+        sig = {
+            "dict_pack_csc_workspace_size": [i32, i32, psz],
+            "dict_pack_csc": [vp, i32, i32, i32, i64, vp, vp, vp, i64, C.POINTER(C.c_int64), vp,
+                              sz, vp],
+            "nvfp4_pack_workspace_size": [i64, psz],
+            "nvfp4_pack": [vp, i64, NV, vp, sz, vp],
+            "nvfp4_unpack": [NV, i64, vp, vp],
+            "dict_workspace_size": [i32, i32, C.POINTER(Dict), C.POINTER(Csc), psz],
+            "dict_proj_forward": [vp, i32, i32, i64, C.POINTER(Dict), C.POINTER(Csc), vp, i32,
+                                  i64, vp, sz, vp],
+            "dict_group_forward": [i32, C.POINTER(vp), i32, i32, i64, C.POINTER(Dict),
+                                   C.POINTER(Csc), C.POINTER(vp), i32, i64, vp, sz, vp],
+            "dict_xd_forward": [i32, C.POINTER(vp), i32, i32, i64, C.POINTER(Dict), vp, i32, vp,
+                                sz, vp],
+            "dict_xd_workspace_size": [i32, i32, C.POINTER(Dict), psz],
+            "dict_zc_forward": [i32, vp, i32, i32, C.POINTER(Csc), C.POINTER(vp), i32, i64, vp],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = C.c_int
+        L.dfs_status_str.argtypes = [C.c_int]
+        L.dfs_status_str.restype = C.c_char_p
+        L.dfs_last_hip_error.restype = C.c_int32
+        L.dfs_version.restype = C.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DfsError(fn, status)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return DFS_F16
+    if t.dtype == torch.float32:
+        return DFS_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dt(code: int):
+    return {DFS_F16: torch.float16, DFS_F32: torch.float32}[code]
+
+
+# ----------------------------------------------------------------- holders
+
+@dataclass
+class DeviceNVFP4:
+    codes: torch.Tensor    # uint8[(n+1)//2]
+    scales: torch.Tensor   # uint8[(n+15)//16]
+    ts: torch.Tensor       # float32[1]
+    n: int
+
+    def nv(self) -> NV:
+        return NV(self.codes.data_ptr(), self.scales.data_ptr(), self.ts.data_ptr())
+
+    @staticmethod
+    def empty(n: int, device) -> "DeviceNVFP4":
+        # codes padded to 16 bytes so 16-byte chunk reads stay in bounds
+        nc = ((n + 1) // 2 + 15) // 16 * 16
+        return DeviceNVFP4(torch.zeros(max(nc, 16), dtype=torch.uint8, device=device),
+                           torch.zeros(max((n + 15) // 16, 1), dtype=torch.uint8, device=device),
+                           torch.zeros(1, dtype=torch.float32, device=device), n)
+
+
+@dataclass
+class DeviceDict:
+    """D_g stored atom-major: ``data`` is (k, d_in), or ``nv`` holds k*d_in
+    NVFP4 elements in that order."""
+    d_in: int
+    k: int
+    data: torch.Tensor | None = None
+    nv: DeviceNVFP4 | None = None
+
+    def desc(self) -> Dict:
+        if self.nv is not None:
+            return Dict(self.d_in, self.k, DFS_NVFP4, 0, None, self.d_in, self.nv.nv())
+        return Dict(self.d_in, self.k, _dt(self.data), 0, self.data.data_ptr(),
+                    self.data.stride(0), NV())
+
+    @staticmethod
+    def from_atoms(atoms: torch.Tensor) -> "DeviceDict":
+        assert atoms.dim() == 2 and atoms.stride(1) == 1
+        return DeviceDict(atoms.shape[1], atoms.shape[0], data=atoms)
+
+
+@dataclass
+class DeviceCSC:
+    k: int
+    d_out: int
+    nnz: int
+    colptr: torch.Tensor          # int32[d_out+1]
+    rowidx: torch.Tensor          # uint16 storage (int16 tensor) [>= nnz]
+    vals: torch.Tensor | None = None
+    nv: DeviceNVFP4 | None = None
+
+    def desc(self) -> Csc:
+        if self.nv is not None:
+            return Csc(self.k, self.d_out, self.nnz, DFS_NVFP4, 0, self.colptr.data_ptr(),
+                       self.rowidx.data_ptr(), None, self.nv.nv())
+        return Csc(self.k, self.d_out, self.nnz, _dt(self.vals), 0, self.colptr.data_ptr(),
+                   self.rowidx.data_ptr(), self.vals.data_ptr(), NV())
+
+
+def _pad16(n: int, esz: int) -> int:
+    per = 16 // esz
+    return max((n + per - 1) // per * per, per)
+
+
+# ----------------------------------------------------------------- packing
+
+def dict_pack_csc(Cd: torch.Tensor, stream=None) -> DeviceCSC:
+    """Dense (k, d_out) f16/f32 device tensor -> DeviceCSC (two calls: count,
+    then fill into buffers sized from the count)."""
+    assert Cd.dim() == 2 and Cd.stride(1) == 1
+    k, d_out = Cd.shape
+    dev = Cd.device
+    ws_n = C.c_size_t(0)
+    _check("dict_pack_csc_workspace_size",
+           lib().dict_pack_csc_workspace_size(k, d_out, C.byref(ws_n)))
+    ws = torch.empty(ws_n.value, dtype=torch.uint8, device=dev)
+    colptr = torch.empty(d_out + 1, dtype=torch.int32, device=dev)
+    nnz = C.c_int64(0)
+    st = _stream(stream)
+    _check("dict_pack_csc", lib().dict_pack_csc(Cd.data_ptr(), _dt(Cd), k, d_out, Cd.stride(0),
+                                                colptr.data_ptr(), None, None, 0, C.byref(nnz),
+                                                ws.data_ptr(), ws_n.value, st))
+    n = nnz.value
+    rowidx = torch.zeros(_pad16(n, 2), dtype=torch.int16, device=dev)
+    vals = torch.zeros(_pad16(n, Cd.element_size()), dtype=Cd.dtype, device=dev)
+    _check("dict_pack_csc", lib().dict_pack_csc(Cd.data_ptr(), _dt(Cd), k, d_out, Cd.stride(0),
+                                                colptr.data_ptr(), rowidx.data_ptr(),
+                                                vals.data_ptr(), rowidx.numel(), C.byref(nnz),
+                                                ws.data_ptr(), ws_n.value, st))
+    return DeviceCSC(k, d_out, n, colptr, rowidx, vals=vals)
+
+
+def nvfp4_pack(x: torch.Tensor, stream=None) -> DeviceNVFP4:
+    """fp32 device tensor (any shape, contiguous) -> DeviceNVFP4 of x.numel()."""
+    assert x.dtype == torch.float32 and x.is_contiguous()
+    n = x.numel()
+    q = DeviceNVFP4.empty(n, x.device)
+    ws_n = C.c_size_t(0)
+    _check("nvfp4_pack_workspace_size", lib().nvfp4_pack_workspace_size(n, C.byref(ws_n)))
+    ws = torch.empty(ws_n.value, dtype=torch.uint8, device=x.device)
+    _check("nvfp4_pack", lib().nvfp4_pack(x.data_ptr(), n, q.nv(), ws.data_ptr(), ws_n.value,
+                                          _stream(stream)))
+    return q
+
+
+def nvfp4_unpack(q: DeviceNVFP4, stream=None) -> torch.Tensor:
+    y = torch.empty(q.n, dtype=torch.float32, device=q.codes.device)
+    _check("nvfp4_unpack", lib().nvfp4_unpack(q.nv(), q.n, y.data_ptr(), _stream(stream)))
+    return y
+
+
+def csc_to_nvfp4(c: DeviceCSC, stream=None) -> DeviceCSC:
+    """Quantise a DeviceCSC's values (CSC order) to NVFP4, support unchanged."""
+    v = c.vals[:c.nnz].float().contiguous()
+    return DeviceCSC(c.k, c.d_out, c.nnz, c.colptr, c.rowidx, nv=nvfp4_pack(v, stream))
+
+
+# ----------------------------------------------------------------- forward
+
+def dict_workspace_size(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC) -> int:
+    n = C.c_size_t(0)
+    d, c = D.desc(), Cs.desc()
+    _check("dict_workspace_size",
+           lib().dict_workspace_size(n_layers, T, C.byref(d), C.byref(c), C.byref(n)))
+    return n.value
+
+
+def workspace(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC, device) -> torch.Tensor:
+    return torch.empty(dict_workspace_size(n_layers, T, D, Cs), dtype=torch.uint8, device=device)
+
+
+def dict_group_forward(Xs, D: DeviceDict, Cs, Ys=None, ydtype=torch.float16, ws=None,
+                       stream=None):
+    """Y_l = (X_l D) C_l for every layer of a group sharing D."""
+    n = len(Xs)
+    T, d_in = Xs[0].shape
+    d_out = Cs[0].d_out
+    dev = Xs[0].device
+    if Ys is None:
+        Ys = [torch.empty(T, d_out, dtype=ydtype, device=dev) for _ in range(n)]
+    if ws is None:
+        ws = workspace(n, T, D, Cs[0], dev)
+    xp = (C.c_void_p * n)(*[x.data_ptr() for x in Xs])
+    yp = (C.c_void_p * n)(*[y.data_ptr() for y in Ys])
+    cs = (Csc * n)(*[c.desc() for c in Cs])
+    d = D.desc()
+    _check("dict_group_forward",
+           lib().dict_group_forward(n, xp, _dt(Xs[0]), T, Xs[0].stride(0), C.byref(d), cs, yp,
+                                    _dt(Ys[0]), Ys[0].stride(0), ws.data_ptr(), ws.numel(),
+                                    _stream(stream)))
+    return Ys
+
+
+def dict_proj_forward(X, D: DeviceDict, Cs: DeviceCSC, Y=None, ydtype=torch.float16, ws=None,
+                      stream=None):
+    T = X.shape[0]
+    if Y is None:
+        Y = torch.empty(T, Cs.d_out, dtype=ydtype, device=X.device)
+    if ws is None:
+        ws = workspace(1, T, D, Cs, X.device)
+    d, c = D.desc(), Cs.desc()
+    _check("dict_proj_forward",
+           lib().dict_proj_forward(X.data_ptr(), _dt(X), T, X.stride(0), C.byref(d), C.byref(c),
+                                   Y.data_ptr(), _dt(Y), Y.stride(0), ws.data_ptr(), ws.numel(),
+                                   _stream(stream)))
+    return Y
+
+
+def dict_xd_forward(Xs, D: DeviceDict, zdtype=torch.float32, Z=None, ws=None, stream=None):
+    n = len(Xs)
+    T = Xs[0].shape[0]
+    if Z is None:
+        Z = torch.empty(n * T, D.k, dtype=zdtype, device=Xs[0].device)
+    d = D.desc()
+    need = C.c_size_t(0)
+    _check("dict_xd_workspace_size",
+           lib().dict_xd_workspace_size(n, T, C.byref(d), C.byref(need)))
+    if ws is None and need.value:
+        ws = torch.empty(need.value, dtype=torch.uint8, device=Xs[0].device)
+    xp = (C.c_void_p * n)(*[x.data_ptr() for x in Xs])
+    _check("dict_xd_forward",
+           lib().dict_xd_forward(n, xp, _dt(Xs[0]), T, Xs[0].stride(0), C.byref(d),
+                                 Z.data_ptr(), _dt(Z), None if ws is None else ws.data_ptr(),
+                                 0 if ws is None else ws.numel(), _stream(stream)))
+    return Z
+
+
+def dict_zc_forward(Z, T: int, Cs, Ys=None, ydtype=torch.float16, stream=None):
+    n = len(Cs)
+    d_out = Cs[0].d_out
+    if Ys is None:
+        Ys = [torch.empty(T, d_out, dtype=ydtype, device=Z.device) for _ in range(n)]
+    yp = (C.c_void_p * n)(*[y.data_ptr() for y in Ys])
+    cs = (Csc * n)(*[c.desc() for c in Cs])
+    _check("dict_zc_forward",
+           lib().dict_zc_forward(n, Z.data_ptr(), _dt(Z), T, cs, yp, _dt(Ys[0]),
+                                 Ys[0].stride(0), _stream(stream)))
+    return Ys
+
+
+# ----------------------------------------------------------------- host -> device helpers
+
+def to_device_dict(atoms_np, device, nvfp4: bool = False) -> DeviceDict:
+    """Atom-major numpy dictionary (k, d_in) -> DeviceDict (NVFP4 via the
+    library's own packer when ``nvfp4``)."""
+    t = torch.from_numpy(atoms_np).to(device)
+    k, d_in = atoms_np.shape
+    if nvfp4:
+        return DeviceDict(d_in, k, nv=nvfp4_pack(t.float().contiguous()))
+    return DeviceDict.from_atoms(t)
+
+
+def to_device_csc(dense_np, device, nvfp4: bool = False) -> DeviceCSC:
+    """Dense numpy coefficients (k, d_out) -> DeviceCSC packed on the GPU."""
+    c = dict_pack_csc(torch.from_numpy(dense_np).to(device))
+    return csc_to_nvfp4(c) if nvfp4 else c

@@ -1,0 +1,382 @@
+// api.hip -- the C ABI of include/dictfs.h: validation, workspace layout,
+// path choice and kernel launches on the caller's stream.
+//
+// Forward ("DictLLM: Shared Dictionaries for Post-Training Compression",
+// Eq. (1)): Z = X D_g on VALU dot products for <= 16 stacked rows and on
+// MFMA above that; Y_l = Z_l C_l on the CSC SpMV for T <= 16 tokens per
+// layer and on the token-tiled SpMM above that.  Every argument is checked
+// before anything is enqueued.
+#include <cstring>
+
+#include "dfs_internal.hpp"
+
+using namespace dfs;
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+dfs_status hip_fail(hipError_t e) {
+  g_last_hip = (int32_t)e;
+  return DFS_E_HIP;
+}
+
+#define DFS_HIP(x)                                  \
+  do {                                              \
+    hipError_t _e = (x);                            \
+    if (_e != hipSuccess) return hip_fail(_e);      \
+  } while (0)
+
+#define DFS_TRY(x)                                  \
+  do {                                              \
+    dfs_status _s = (x);                            \
+    if (_s != DFS_OK) return _s;                    \
+  } while (0)
+
+constexpr int32_t kMaxK = 65536;         // 16-bit row indices
+constexpr int32_t kMaxKForward = 16384;  // Z tiles staged in LDS
+constexpr int64_t kMaxNnz = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t esize(int32_t dt) { return dt == DFS_F32 ? 4 : 2; }
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+bool is_act_dtype(int32_t dt) { return dt == DFS_F16 || dt == DFS_F32; }
+
+dfs_status check_nvfp4(const dfs_nvfp4& nv) {
+  if (!nv.codes || !nv.scales || !nv.tensor_scale) return DFS_E_INVALID;
+  if (!aligned16(nv.codes)) return DFS_E_ALIGN;
+  return DFS_OK;
+}
+
+dfs_status check_dict(const dfs_dict* D) {
+  if (!D) return DFS_E_INVALID;
+  if (D->d_in <= 0 || D->k <= 0) return DFS_E_INVALID;
+  if (D->k > kMaxKForward) return DFS_E_RANGE;
+  if (D->dtype == DFS_NVFP4) {
+    DFS_TRY(check_nvfp4(D->nv));
+    if (D->ldd != D->d_in) return DFS_E_UNSUPPORTED;
+    if (D->d_in % 32 != 0) return DFS_E_UNSUPPORTED;
+    return DFS_OK;
+  }
+  if (!is_act_dtype(D->dtype)) return DFS_E_UNSUPPORTED;
+  if (!D->data) return DFS_E_INVALID;
+  if (D->ldd < D->d_in) return DFS_E_INVALID;
+  if (!aligned16(D->data) || (D->ldd * (int64_t)esize(D->dtype)) % 16 != 0) return DFS_E_ALIGN;
+  return DFS_OK;
+}
+
+dfs_status check_csc(const dfs_csc* C, int32_t k, int32_t d_out) {
+  if (!C) return DFS_E_INVALID;
+  if (C->k != k || C->d_out != d_out || d_out <= 0) return DFS_E_INVALID;
+  if (C->nnz < 0) return DFS_E_INVALID;
+  if (C->nnz >= kMaxNnz) return DFS_E_RANGE;
+  if (!C->colptr) return DFS_E_INVALID;
+  if (C->nnz > 0) {
+    if (!C->rowidx) return DFS_E_INVALID;
+    if (!aligned16(C->rowidx)) return DFS_E_ALIGN;
+  }
+  if (C->dtype == DFS_NVFP4) {
+    if (C->nnz > 0) DFS_TRY(check_nvfp4(C->nv));
+    else if (!C->nv.tensor_scale) return DFS_E_INVALID;
+    return DFS_OK;
+  }
+  if (!is_act_dtype(C->dtype)) return DFS_E_UNSUPPORTED;
+  if (C->nnz > 0) {
+    if (!C->vals) return DFS_E_INVALID;
+    if (!aligned16(C->vals)) return DFS_E_ALIGN;
+  }
+  return DFS_OK;
+}
+
+dfs_status check_x(const void* const* X, int32_t n, int32_t xdt, int64_t ldx, int32_t d_in) {
+  if (!is_act_dtype(xdt)) return DFS_E_UNSUPPORTED;
+  if (ldx < d_in) return DFS_E_INVALID;
+  if ((ldx * (int64_t)esize(xdt)) % 16 != 0) return DFS_E_ALIGN;
+  for (int i = 0; i < n; ++i) {
+    if (!X[i]) return DFS_E_INVALID;
+    if (!aligned16(X[i])) return DFS_E_ALIGN;
+  }
+  return DFS_OK;
+}
+
+dfs_status check_y(void* const* Y, int32_t n, int32_t ydt, int64_t ldy, int32_t d_out) {
+  if (!is_act_dtype(ydt)) return DFS_E_UNSUPPORTED;
+  if (ldy < d_out) return DFS_E_INVALID;
+  for (int i = 0; i < n; ++i)
+    if (!Y[i]) return DFS_E_INVALID;
+  return DFS_OK;
+}
+
+bool mfma_path(int64_t rows, int32_t xdt, const dfs_dict* D) {
+  return rows > kGemvMaxRows && xdt == DFS_F16 && D->dtype != DFS_F32 && D->d_in % 8 == 0;
+}
+
+// Bytes of the f16 expansion of an NVFP4 dictionary that the MFMA path needs.
+size_t xd_ws_bytes(int64_t rows, int32_t xdt, const dfs_dict* D) {
+  if (D->dtype == DFS_NVFP4 && mfma_path(rows, xdt, D))
+    return round256((size_t)D->k * D->d_in * 2);
+  return 0;
+}
+
+// Z = X D for the stacked rows; Z row-major (rows x k) of dtype zdt.
+dfs_status run_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64_t ldx,
+                  const dfs_dict* D, void* Z, int32_t zdt, void* ws, hipStream_t s) {
+  XdLaunch a;
+  std::memset(&a, 0, sizeof(a));
+  for (int i = 0; i < n; ++i) a.X[i] = X[i];
+  a.n_layers = n;
+  a.T = T;
+  a.ldx = ldx;
+  a.xdt = xdt;
+  a.d_in = D->d_in;
+  a.k = D->k;
+  a.ddt = D->dtype;
+  a.D = D->data;
+  a.ldd = D->ldd;
+  a.dcodes = D->nv.codes;
+  a.dscales = D->nv.scales;
+  a.dts = D->nv.tensor_scale;
+  a.Z = Z;
+  a.zdt = zdt;
+  const int64_t rows = (int64_t)n * T;
+  if (mfma_path(rows, xdt, D)) {
+    if (D->dtype == DFS_NVFP4) {
+      _Float16* dh = (_Float16*)ws;
+      DFS_HIP(launch_nvfp4_to_f16(D->nv.codes, D->nv.scales, D->nv.tensor_scale,
+                                  (int64_t)D->k * D->d_in, dh, s));
+      a.D = dh;
+      a.ldd = D->d_in;
+      a.ddt = DFS_F16;
+    }
+    DFS_HIP(launch_gemm_xd_mfma(a, s));
+  } else {
+    DFS_HIP(launch_gemv_xd(a, s));
+  }
+  return DFS_OK;
+}
+
+dfs_status run_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc* C,
+                  void* const* Y, int32_t ydt, int64_t ldy, hipStream_t s) {
+  ZcLaunch a;
+  std::memset(&a, 0, sizeof(a));
+  a.Z = Z;
+  a.zdt = zdt;
+  a.n_layers = n;
+  a.T = T;
+  a.k = C[0].k;
+  a.d_out = C[0].d_out;
+  a.vdt = C[0].dtype;
+  for (int i = 0; i < n; ++i) {
+    a.colptr[i] = C[i].colptr;
+    a.nnz[i] = C[i].nnz;
+    a.rowidx[i] = C[i].rowidx;
+    if (C[i].dtype == DFS_NVFP4) {
+      a.vals[i] = C[i].nv.codes;
+      a.vscales[i] = C[i].nv.scales;
+      a.vts[i] = C[i].nv.tensor_scale;
+    } else {
+      a.vals[i] = C[i].vals;
+    }
+    a.Y[i] = Y[i];
+  }
+  a.ydt = ydt;
+  a.ldy = ldy;
+  if (T <= kGemvMaxRows)
+    DFS_HIP(launch_spmv_csc(a, s));
+  else
+    DFS_HIP(launch_spmm_csc(a, s));
+  return DFS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dfs_status_str(dfs_status st) {
+  switch (st) {
+    case DFS_OK:
+      return "ok";
+    case DFS_E_INVALID:
+      return "invalid argument";
+    case DFS_E_UNSUPPORTED:
+      return "unsupported dtype or layout";
+    case DFS_E_RANGE:
+      return "value out of range";
+    case DFS_E_ALIGN:
+      return "misaligned pointer or leading dimension";
+    case DFS_E_WORKSPACE:
+      return "workspace missing or too small";
+    case DFS_E_HIP:
+      return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t dfs_last_hip_error(void) { return g_last_hip; }
+
+int32_t dfs_version(void) { return 100; }
+
+// ------------------------------------------------------------------ packing
+
+dfs_status dict_pack_csc_workspace_size(int32_t k, int32_t d_out, size_t* bytes) {
+  if (!bytes) return DFS_E_INVALID;
+  if (k <= 0 || d_out <= 0) return DFS_E_INVALID;
+  if (k > kMaxK) return DFS_E_RANGE;
+  *bytes = pack_csc_ws_bytes(k, d_out);
+  return DFS_OK;
+}
+
+dfs_status dict_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out, int64_t ldc,
+                         int32_t* colptr, uint16_t* rowidx, void* vals, int64_t capacity,
+                         int64_t* nnz_host, void* ws, size_t ws_bytes, void* stream) {
+  if (!C || !colptr || !nnz_host) return DFS_E_INVALID;
+  if (dtype != DFS_F16 && dtype != DFS_F32) return DFS_E_UNSUPPORTED;
+  if (k <= 0 || d_out <= 0 || ldc < d_out) return DFS_E_INVALID;
+  if (k > kMaxK) return DFS_E_RANGE;
+  if ((rowidx == nullptr) != (vals == nullptr)) return DFS_E_INVALID;
+  if (capacity < 0) return DFS_E_INVALID;
+  if (!ws || ws_bytes < pack_csc_ws_bytes(k, d_out)) return DFS_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  DFS_HIP(launch_pack_csc_count(C, dtype, k, d_out, ldc, colptr, ws, s));
+  int64_t total = 0;
+  DFS_HIP(hipMemcpyAsync(&total, ws, sizeof(total), hipMemcpyDeviceToHost, s));
+  DFS_HIP(hipStreamSynchronize(s));
+  *nnz_host = total;
+  if (total >= kMaxNnz) return DFS_E_RANGE;
+  if (!rowidx) return DFS_OK;
+  if (total > capacity) return DFS_E_RANGE;
+  DFS_HIP(launch_pack_csc_scatter(C, dtype, k, d_out, ldc, rowidx, vals, ws, s));
+  return DFS_OK;
+}
+
+dfs_status nvfp4_pack_workspace_size(int64_t n, size_t* bytes) {
+  if (!bytes || n < 0) return DFS_E_INVALID;
+  *bytes = nvfp4_ws_bytes(n);
+  return DFS_OK;
+}
+
+dfs_status nvfp4_pack(const float* x, int64_t n, dfs_nvfp4 out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (n < 0) return DFS_E_INVALID;
+  if (!out.tensor_scale) return DFS_E_INVALID;
+  if (n > 0) {
+    if (!x) return DFS_E_INVALID;
+    DFS_TRY(check_nvfp4(out));
+  }
+  if (!ws || ws_bytes < nvfp4_ws_bytes(n)) return DFS_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (n == 0) {
+    DFS_HIP(hipMemsetD32Async((hipDeviceptr_t)out.tensor_scale, 0x3F800000u, 1, s));  // 1.0f
+    return DFS_OK;
+  }
+  DFS_HIP(launch_nvfp4_amax(x, n, ws, s));
+  uint32_t res[2] = {0, 0};
+  DFS_HIP(hipMemcpyAsync(res, ws, sizeof(res), hipMemcpyDeviceToHost, s));
+  DFS_HIP(hipStreamSynchronize(s));
+  if (res[1] != 0) return DFS_E_INVALID;
+  DFS_HIP(launch_nvfp4_encode(x, n, out, ws, s));
+  return DFS_OK;
+}
+
+dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream) {
+  if (n < 0) return DFS_E_INVALID;
+  if (n == 0) return DFS_OK;
+  if (!y) return DFS_E_INVALID;
+  DFS_TRY(check_nvfp4(in));
+  DFS_HIP(launch_nvfp4_decode(in, n, y, (hipStream_t)stream));
+  return DFS_OK;
+}
+
+// ------------------------------------------------------------------ forward
+
+dfs_status dict_xd_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, size_t* bytes) {
+  if (!bytes || n_layers <= 0 || T < 0) return DFS_E_INVALID;
+  if (n_layers > kMaxLayers) return DFS_E_RANGE;
+  DFS_TRY(check_dict(D));
+  *bytes = xd_ws_bytes((int64_t)n_layers * T, DFS_F16, D);
+  return DFS_OK;
+}
+
+dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, const dfs_csc* C,
+                               size_t* bytes) {
+  if (!bytes || n_layers <= 0 || T < 0) return DFS_E_INVALID;
+  if (n_layers > kMaxLayers) return DFS_E_RANGE;
+  DFS_TRY(check_dict(D));
+  if (!C || C->k != D->k || C->d_out <= 0) return DFS_E_INVALID;
+  const int64_t rows = (int64_t)n_layers * T;
+  *bytes = round256((size_t)rows * D->k * 4) + xd_ws_bytes(rows, DFS_F16, D) + 256;
+  return DFS_OK;
+}
+
+dfs_status dict_xd_forward(int32_t n_layers, const void* const* X, int32_t xdt, int32_t T,
+                           int64_t ldx, const dfs_dict* D, void* Z, int32_t zdt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (n_layers <= 0 || T < 0 || !X) return DFS_E_INVALID;
+  if (n_layers > kMaxLayers) return DFS_E_RANGE;
+  DFS_TRY(check_dict(D));
+  DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
+  if (zdt != DFS_F16 && zdt != DFS_F32) return DFS_E_UNSUPPORTED;
+  if (T == 0) return DFS_OK;
+  if (!Z) return DFS_E_INVALID;
+  if (!aligned16(Z)) return DFS_E_ALIGN;
+  const size_t need = xd_ws_bytes((int64_t)n_layers * T, xdt, D);
+  if (need && (!ws || ws_bytes < need)) return DFS_E_WORKSPACE;
+  if (need && !aligned16(ws)) return DFS_E_ALIGN;
+  return run_xd(n_layers, X, xdt, T, ldx, D, Z, zdt, ws, (hipStream_t)stream);
+}
+
+dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t T,
+                           const dfs_csc* C, void* const* Y, int32_t ydt, int64_t ldy,
+                           void* stream) {
+  if (n_layers <= 0 || T < 0 || !C || !Y) return DFS_E_INVALID;
+  if (n_layers > kMaxLayers) return DFS_E_RANGE;
+  if (zdt != DFS_F16 && zdt != DFS_F32) return DFS_E_UNSUPPORTED;
+  if (C[0].k <= 0) return DFS_E_INVALID;
+  if (C[0].k > kMaxKForward) return DFS_E_RANGE;
+  for (int i = 0; i < n_layers; ++i) {
+    DFS_TRY(check_csc(&C[i], C[0].k, C[0].d_out));
+    if (C[i].dtype != C[0].dtype) return DFS_E_UNSUPPORTED;
+  }
+  DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
+  if (T == 0) return DFS_OK;
+  if (!Z) return DFS_E_INVALID;
+  return run_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy, (hipStream_t)stream);
+}
+
+dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xdt, int32_t T,
+                              int64_t ldx, const dfs_dict* D, const dfs_csc* C, void* const* Y,
+                              int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (n_layers <= 0 || T < 0 || !X || !C || !Y) return DFS_E_INVALID;
+  if (n_layers > kMaxLayers) return DFS_E_RANGE;
+  DFS_TRY(check_dict(D));
+  DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
+  for (int i = 0; i < n_layers; ++i) {
+    DFS_TRY(check_csc(&C[i], D->k, C[0].d_out));
+    if (C[i].dtype != C[0].dtype) return DFS_E_UNSUPPORTED;
+  }
+  DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
+  if (T == 0) return DFS_OK;
+  const int64_t rows = (int64_t)n_layers * T;
+  const bool mfma = mfma_path(rows, xdt, D);
+  const int32_t zdt = mfma ? DFS_F16 : DFS_F32;
+  const size_t zbytes = round256((size_t)rows * D->k * esize(zdt));
+  const size_t need = zbytes + xd_ws_bytes(rows, xdt, D);
+  if (!ws || ws_bytes < need) return DFS_E_WORKSPACE;
+  if (!aligned16(ws)) return DFS_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  void* Z = ws;
+  void* xws = (char*)ws + zbytes;
+  DFS_TRY(run_xd(n_layers, X, xdt, T, ldx, D, Z, zdt, xws, s));
+  return run_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy, s);
+}
+
+dfs_status dict_proj_forward(const void* X, int32_t xdt, int32_t T, int64_t ldx, const dfs_dict* D,
+                             const dfs_csc* C, void* Y, int32_t ydt, int64_t ldy, void* ws,
+                             size_t ws_bytes, void* stream) {
+  const void* xs[1] = {X};
+  void* ys[1] = {Y};
+  return dict_group_forward(1, xs, xdt, T, ldx, D, C, ys, ydt, ldy, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// dfs_internal.hpp -- device helpers and kernel-launcher interfaces shared by
+// the translation units of libdictfs (the HIP path only).
+//
+// Target: gfx950 (CDNA4), wave64.  Nothing here is used by the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dictfs.h"
+
+namespace dfs {
+
+constexpr int kWave = 64;
+constexpr int kMaxLayers = 16;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ DPP
+// Cross-lane moves inside a 16-lane DPP row.  Controls: quad_perm [1,0,3,2]
+// = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
+// row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of each DPP row; every lane of the row gets the sum.
+// The combination order is fixed, so results are run-to-run identical.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return v;
+}
+
+// Sum over the whole wave; every lane gets the sum.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// ------------------------------------------------------------------ formats
+// E4M3 (bias 7, no infinities) code -> fp32, from the format definition.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = e == 0 ? (float)m * 0x1p-9f : __builtin_ldexpf((float)(8u + m), (int)e - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Two E2M1 codes (byte SEL of `word`: low nibble -> .x, high nibble -> .y)
+// to f16 / f32, unscaled: the hardware conversion with scale 1.0 is exact
+// because every E2M1 value is an f16 value.
+template <int SEL>
+__device__ __forceinline__ h2 e2m1x2_h2(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ f2 e2m1x2_f2(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+}
+
+__device__ __forceinline__ float h2f(_Float16 h) { return (float)h; }
+
+// 16-byte global load through the vector path.
+template <typename T>
+__device__ __forceinline__ T ld16(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+// ------------------------------------------------------------------ launches
+// Rows of the stacked X: row r = l*T + t is token t of layer l.
+struct XdLaunch {
+  const void* X[kMaxLayers];
+  int32_t n_layers, T;
+  int64_t ldx;
+  int32_t xdt;
+  int32_t d_in, k;
+  int32_t ddt;
+  const void* D;        // f16 / f32 atom-major, or f16 expansion for MFMA
+  int64_t ldd;
+  const uint8_t* dcodes;
+  const uint8_t* dscales;
+  const float* dts;
+  void* Z;              // (n_layers*T) x k row-major
+  int32_t zdt;
+};
+
+struct ZcLaunch {
+  const void* Z;        // (n_layers*T) x k row-major
+  int32_t zdt;
+  int32_t n_layers, T, k, d_out;
+  int32_t vdt;
+  const int32_t* colptr[kMaxLayers];
+  int64_t nnz[kMaxLayers];
+  const uint16_t* rowidx[kMaxLayers];
+  const void* vals[kMaxLayers];       // f16/f32 values, or NVFP4 codes
+  const uint8_t* vscales[kMaxLayers]; // NVFP4 block scales
+  const float* vts[kMaxLayers];       // NVFP4 tensor scale
+  void* Y[kMaxLayers];
+  int32_t ydt;
+  int64_t ldy;
+};
+
+// Rows at or below which X.D runs on VALU dot products instead of MFMA.
+constexpr int kGemvMaxRows = 16;
+
+hipError_t launch_gemv_xd(const XdLaunch& a, hipStream_t s);
+hipError_t launch_gemm_xd_mfma(const XdLaunch& a, hipStream_t s);
+hipError_t launch_nvfp4_to_f16(const uint8_t* codes, const uint8_t* scales, const float* ts,
+                               int64_t n, _Float16* out, hipStream_t s);
+hipError_t launch_spmv_csc(const ZcLaunch& a, hipStream_t s);
+// Tokens per LDS pass of the SpMV (power of two, <= 16, Z tile <= 64 KiB).
+int spmv_token_tile(int T, int k);
+hipError_t launch_spmm_csc(const ZcLaunch& a, hipStream_t s);
+// Tokens per workgroup tile of the SpMM (32, 16, 8 or 4; f16 Z tile <= 128 KiB).
+int spmm_token_tile(int k);
+
+// CSC packing
+size_t pack_csc_ws_bytes(int32_t k, int32_t d_out);
+hipError_t launch_pack_csc_count(const void* C, int32_t dtype, int32_t k, int32_t d_out,
+                                 int64_t ldc, int32_t* colptr, void* ws, hipStream_t s);
+hipError_t launch_pack_csc_scatter(const void* C, int32_t dtype, int32_t k, int32_t d_out,
+                                   int64_t ldc, uint16_t* rowidx, void* vals, const void* ws,
+                                   hipStream_t s);
+
+// NVFP4 packing
+size_t nvfp4_ws_bytes(int64_t n);
+hipError_t launch_nvfp4_amax(const float* x, int64_t n, void* ws, hipStream_t s);
+hipError_t launch_nvfp4_encode(const float* x, int64_t n, dfs_nvfp4 out, const void* ws,
+                               hipStream_t s);
+hipError_t launch_nvfp4_decode(dfs_nvfp4 in, int64_t n, float* y, hipStream_t s);
+
+}  // namespace dfs

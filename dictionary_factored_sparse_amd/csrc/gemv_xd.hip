@@ -1,0 +1,295 @@
+// gemv_xd.hip -- Z = X D_g for a few stacked rows (decode), on VALU.
+//
+// First half of the factored projection ("DictLLM: Shared Dictionaries for
+// Post-Training Compression", Eq. (1): Z_l = X_l D_g).  At decode a group
+// has n_layers * T <= 16 rows, so every dictionary element is used at most
+// 16 times: the kernel is a bandwidth-bound stream of D_g, which is read
+// exactly once per launch however many layers share it (the group reuse of
+// the review's Figure 2).
+//
+// Layout: D_g atom-major (atom a = d_in contiguous elements), X rows
+// row-major.  One wave owns A atoms; lane l reads 16-byte chunks
+// l, l+64, l+128, ... of each atom, so a wave-wide load is one fully
+// coalesced 1 KiB segment.  All chunk loads of a d_in segment are issued
+// before the X segment is staged into LDS, so HBM latency overlaps the
+// staging.  The lane partial sums are reduced across the wave with DPP.
+//
+// Products: f16 x f16 (and E2M1 decoded to f16 x f16) use v_dot2_f32_f16,
+// which multiplies exactly and accumulates in fp32; f32 operands use FMA.
+#include "dfs_internal.hpp"
+
+namespace dfs {
+namespace {
+
+template <int DT>
+struct DTraits;
+template <>
+struct DTraits<DFS_F32> {
+  static constexpr int CE = 4;       // elements per 16-byte chunk
+  static constexpr int A = 2;        // atoms per wave
+  static constexpr int kMaxRT = 16;  // rows per launch tile
+};
+template <>
+struct DTraits<DFS_F16> {
+  static constexpr int CE = 8;
+  static constexpr int A = 2;
+  static constexpr int kMaxRT = 16;
+};
+template <>
+struct DTraits<DFS_NVFP4> {
+  static constexpr int CE = 32;
+  static constexpr int A = 4;
+  static constexpr int kMaxRT = 4;   // 32-element chunks: keep registers and LDS bounded
+};
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kLdsBudget = 64 * 1024;
+
+template <int DT, int XT, int RT>
+struct Cfg {
+  static constexpr bool kDot2 = (DT != DFS_F32) && (XT == DFS_F16);
+  using XS = typename std::conditional<kDot2, _Float16, float>::type;
+  static constexpr int CE = DTraits<DT>::CE;
+  static constexpr int A = DTraits<DT>::A;
+  static constexpr int kSegcDefault = DT == DFS_NVFP4 ? 2 : 8;
+  static constexpr int kSegcFit = kLdsBudget / (RT * (int)sizeof(XS) * kWave * CE);
+  static constexpr int SEGC = kSegcFit < 1 ? 1 : (kSegcFit < kSegcDefault ? kSegcFit : kSegcDefault);
+  static constexpr int SEG = kWave * SEGC * CE;  // elements of d_in per segment
+};
+
+// Elementwise-guarded load of the last, partial chunk of an atom.
+template <int DT>
+__device__ __forceinline__ u4 load_chunk_tail(const void* base, int valid) {
+  u4 r = {0u, 0u, 0u, 0u};
+  if constexpr (DT == DFS_F32) {
+    const uint32_t* p = (const uint32_t*)base;
+    for (int i = 0; i < valid; ++i) r[i] = p[i];
+  } else if constexpr (DT == DFS_F16) {
+    const uint16_t* p = (const uint16_t*)base;
+    uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < valid; ++i) tmp[i] = p[i];
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)tmp[2 * i] | ((uint32_t)tmp[2 * i + 1] << 16);
+  }
+  return r;  // NVFP4 dictionaries have d_in % 32 == 0: no partial chunk
+}
+
+// Dot product of one 16-byte D chunk with the matching X elements in LDS.
+template <int DT, bool kDot2, typename XS>
+__device__ __forceinline__ float dot_chunk(u4 d, uint32_t sc2, const XS* x, float acc) {
+  if constexpr (DT == DFS_F16 && kDot2) {
+    const h8 xv = *reinterpret_cast<const h8*>(x);
+    const h2* dh = reinterpret_cast<const h2*>(&d);
+    acc = __builtin_amdgcn_fdot2(dh[0], h2{xv[0], xv[1]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(dh[1], h2{xv[2], xv[3]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(dh[2], h2{xv[4], xv[5]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(dh[3], h2{xv[6], xv[7]}, acc, false);
+    return acc;
+  } else if constexpr (DT == DFS_F16) {
+    const f4 x0 = *reinterpret_cast<const f4*>(x);
+    const f4 x1 = *reinterpret_cast<const f4*>(x + 4);
+    const _Float16* dh = reinterpret_cast<const _Float16*>(&d);
+    acc = __builtin_fmaf((float)dh[0], x0[0], acc);
+    acc = __builtin_fmaf((float)dh[1], x0[1], acc);
+    acc = __builtin_fmaf((float)dh[2], x0[2], acc);
+    acc = __builtin_fmaf((float)dh[3], x0[3], acc);
+    acc = __builtin_fmaf((float)dh[4], x1[0], acc);
+    acc = __builtin_fmaf((float)dh[5], x1[1], acc);
+    acc = __builtin_fmaf((float)dh[6], x1[2], acc);
+    acc = __builtin_fmaf((float)dh[7], x1[3], acc);
+    return acc;
+  } else if constexpr (DT == DFS_F32) {
+    const f4 x0 = *reinterpret_cast<const f4*>(x);
+    acc = __builtin_fmaf(__uint_as_float(d[0]), x0[0], acc);
+    acc = __builtin_fmaf(__uint_as_float(d[1]), x0[1], acc);
+    acc = __builtin_fmaf(__uint_as_float(d[2]), x0[2], acc);
+    acc = __builtin_fmaf(__uint_as_float(d[3]), x0[3], acc);
+    return acc;
+  } else {
+    // NVFP4: 32 elements = two 16-element blocks, words 0-1 and 2-3.
+    const float s0 = e4m3_to_f32(sc2 & 0xFFu);
+    const float s1 = e4m3_to_f32((sc2 >> 8) & 0xFFu);
+    float b[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float p = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t word = d[2 * h + w];
+        const XS* xw = x + 16 * h + 8 * w;
+        if constexpr (kDot2) {
+          const h8 xv = *reinterpret_cast<const h8*>(xw);
+          p = __builtin_amdgcn_fdot2(e2m1x2_h2<0>(word), h2{xv[0], xv[1]}, p, false);
+          p = __builtin_amdgcn_fdot2(e2m1x2_h2<1>(word), h2{xv[2], xv[3]}, p, false);
+          p = __builtin_amdgcn_fdot2(e2m1x2_h2<2>(word), h2{xv[4], xv[5]}, p, false);
+          p = __builtin_amdgcn_fdot2(e2m1x2_h2<3>(word), h2{xv[6], xv[7]}, p, false);
+        } else {
+          const f4 x0 = *reinterpret_cast<const f4*>(xw);
+          const f4 x1 = *reinterpret_cast<const f4*>(xw + 4);
+          f2 v;
+          v = e2m1x2_f2<0>(word);
+          p = __builtin_fmaf(v[0], x0[0], p);
+          p = __builtin_fmaf(v[1], x0[1], p);
+          v = e2m1x2_f2<1>(word);
+          p = __builtin_fmaf(v[0], x0[2], p);
+          p = __builtin_fmaf(v[1], x0[3], p);
+          v = e2m1x2_f2<2>(word);
+          p = __builtin_fmaf(v[0], x1[0], p);
+          p = __builtin_fmaf(v[1], x1[1], p);
+          v = e2m1x2_f2<3>(word);
+          p = __builtin_fmaf(v[0], x1[2], p);
+          p = __builtin_fmaf(v[1], x1[3], p);
+        }
+      }
+      b[h] = p;
+    }
+    acc = __builtin_fmaf(b[0], s0, acc);
+    acc = __builtin_fmaf(b[1], s1, acc);
+    return acc;
+  }
+}
+
+template <int DT, int XT, int RT>
+__global__ __launch_bounds__(kThreads) void gemv_xd_kernel(XdLaunch a) {
+  using C = Cfg<DT, XT, RT>;
+  using XS = typename C::XS;
+  constexpr int CE = C::CE, A = C::A, SEGC = C::SEGC, SEG = C::SEG;
+  __shared__ __attribute__((aligned(16))) XS xs[RT * SEG];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int atom0 = (blockIdx.x * kWaves + wave) * A;
+  const int R = a.n_layers * a.T;
+  const int row0 = blockIdx.y * RT;
+  const int d_in = a.d_in;
+
+  float acc[A][RT];
+#pragma unroll
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[i][r] = 0.0f;
+
+  for (int seg = 0; seg < d_in; seg += SEG) {
+    // 1. issue every D chunk load of this segment
+    u4 dreg[A][SEGC];
+    uint32_t sreg[A][SEGC];
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+      const int atom = atom0 + i;
+#pragma unroll
+      for (int c = 0; c < SEGC; ++c) {
+        const int e0 = seg + (c * kWave + lane) * CE;
+        dreg[i][c] = u4{0u, 0u, 0u, 0u};
+        sreg[i][c] = 0u;
+        if (atom < a.k && e0 < d_in) {
+          if constexpr (DT == DFS_NVFP4) {
+            const int64_t el = (int64_t)atom * d_in + e0;
+            dreg[i][c] = ld16<u4>(a.dcodes + el / 2);
+            sreg[i][c] = (uint32_t)a.dscales[el / 16] | ((uint32_t)a.dscales[el / 16 + 1] << 8);
+          } else {
+            const char* p = (const char*)a.D + ((int64_t)atom * a.ldd + e0) * (DT == DFS_F32 ? 4 : 2);
+            if (e0 + CE <= d_in)
+              dreg[i][c] = ld16<u4>(p);
+            else
+              dreg[i][c] = load_chunk_tail<DT>(p, d_in - e0);
+          }
+        }
+      }
+    }
+
+    // 2. stage the X segment of every row of this tile (zero padded)
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < RT * SEG; idx += kThreads) {
+      const int r = idx / SEG, e = idx - r * SEG;
+      const int row = row0 + r;
+      const int ge = seg + e;
+      float v = 0.0f;
+      if (row < R && ge < d_in) {
+        const int l = row / a.T, t = row - l * a.T;
+        if (a.xdt == DFS_F16)
+          v = (float)(((const _Float16*)a.X[l])[(int64_t)t * a.ldx + ge]);
+        else
+          v = ((const float*)a.X[l])[(int64_t)t * a.ldx + ge];
+      }
+      xs[idx] = (XS)v;
+    }
+    __syncthreads();
+
+    // 3. accumulate
+#pragma unroll
+    for (int c = 0; c < SEGC; ++c) {
+      const int el = (c * kWave + lane) * CE;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+#pragma unroll
+        for (int i = 0; i < A; ++i)
+          acc[i][r] = dot_chunk<DT, C::kDot2, XS>(dreg[i][c], sreg[i][c], xs + r * SEG + el, acc[i][r]);
+      }
+    }
+  }
+
+  float ts = 1.0f;
+  if constexpr (DT == DFS_NVFP4) ts = *a.dts;
+#pragma unroll
+  for (int i = 0; i < A; ++i) {
+    const int atom = atom0 + i;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const float v = wave_sum(acc[i][r]) * ts;
+      const int row = row0 + r;
+      if (lane == r && atom < a.k && row < R) {
+        if (a.zdt == DFS_F32)
+          ((float*)a.Z)[(int64_t)row * a.k + atom] = v;
+        else
+          ((_Float16*)a.Z)[(int64_t)row * a.k + atom] = (_Float16)v;
+      }
+    }
+  }
+}
+
+template <int DT, int XT, int RT>
+hipError_t launch_rt(const XdLaunch& a, hipStream_t s) {
+  constexpr int A = DTraits<DT>::A;
+  const int R = a.n_layers * a.T;
+  dim3 grid((a.k + kWaves * A - 1) / (kWaves * A), (R + RT - 1) / RT);
+  hipLaunchKernelGGL((gemv_xd_kernel<DT, XT, RT>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int XT>
+hipError_t launch_xt(const XdLaunch& a, hipStream_t s) {
+  // NVFP4 with f32 activations keeps 32 fp32 X values per chunk in flight:
+  // cap its row tile at 2 so that nothing spills.
+  constexpr int kMax = (DT == DFS_NVFP4 && XT == DFS_F32) ? 2 : DTraits<DT>::kMaxRT;
+  const int R = a.n_layers * a.T;
+  if (R <= 1) return launch_rt<DT, XT, 1>(a, s);
+  if (R <= 2 || kMax == 2) return launch_rt<DT, XT, 2>(a, s);
+  if constexpr (kMax >= 4) {
+    if (R <= 4 || kMax == 4) return launch_rt<DT, XT, 4>(a, s);
+  }
+  if constexpr (kMax >= 16) {
+    if (R <= 8) return launch_rt<DT, XT, 8>(a, s);
+    return launch_rt<DT, XT, 16>(a, s);  // tiles of 16 rows over grid.y
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t launch_dt(const XdLaunch& a, hipStream_t s) {
+  return a.xdt == DFS_F16 ? launch_xt<DT, DFS_F16>(a, s) : launch_xt<DT, DFS_F32>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_xd(const XdLaunch& a, hipStream_t s) {
+  switch (a.ddt) {
+    case DFS_F16:
+      return launch_dt<DFS_F16>(a, s);
+    case DFS_F32:
+      return launch_dt<DFS_F32>(a, s);
+    default:
+      return launch_dt<DFS_NVFP4>(a, s);
+  }
+}
+
+}  // namespace dfs

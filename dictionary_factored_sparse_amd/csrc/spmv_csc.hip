@@ -1,0 +1,211 @@
+// spmv_csc.hip -- Y_l = Z_l C_l for a few tokens (decode), C_l in CSC.
+//
+// Second half of the factored projection ("DictLLM: Shared Dictionaries for
+// Post-Training Compression", Eq. (1): Y_l = Z_l C_l).  Each output column
+// uses its own subset of atoms, so the access is irregular (same review,
+// "Prerequisites: projections, rank and calibration"): the kernel streams
+// the column's row indices and values from HBM with coalesced 16-byte loads
+// and gathers the matching Z entries from LDS.
+//
+// Mapping: a workgroup is 4 waves; each wave serves 4 columns at once, one
+// per 16-lane DPP row.  Lane g of a row reads the 8-entry chunks g, g+16, ...
+// of its column (128 entries per step), U steps in flight per batch.  The
+// first batch is issued before Z is staged into LDS (C does not depend on
+// Z).  The Z tile is [k][TT] fp32 (TT tokens per pass); the partial sums are
+// reduced over the 16 lanes of the row with DPP, in a fixed order.
+// grid = (ceil(d_out / 16), n_layers); one launch covers a whole group.
+#include "csc_chunks.hpp"
+
+namespace dfs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kColsPerBlock = 16;  // 4 waves x 4 DPP rows
+
+template <int VT>
+struct Unroll {
+  static constexpr int U = VT == DFS_F32 ? 2 : 4;
+};
+
+template <int ZT, int TT>
+__device__ __forceinline__ void stage_z(float* zs, const void* Z, int64_t row0, int rows, int k) {
+  if constexpr (TT == 1) {
+    const int64_t off = row0 * k;
+    if (rows > 0) {
+      if constexpr (ZT == DFS_F32) {
+        const float* z = (const float*)Z + off;
+        for (int i = threadIdx.x; i < k; i += kThreads) zs[i] = z[i];
+      } else {
+        const _Float16* z = (const _Float16*)Z + off;
+        for (int i = threadIdx.x; i < k; i += kThreads) zs[i] = (float)z[i];
+      }
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < k * TT; idx += kThreads) {
+      const int t = idx / k, at = idx - t * k;  // read rows contiguously
+      float v = 0.0f;
+      if (t < rows) {
+        const int64_t g = (row0 + t) * k + at;
+        v = ZT == DFS_F32 ? ((const float*)Z)[g] : (float)((const _Float16*)Z)[g];
+      }
+      zs[at * TT + t] = v;
+    }
+  }
+}
+
+template <int VT, int ZT, int TT>
+__global__ __launch_bounds__(kThreads) void spmv_csc_kernel(ZcLaunch a) {
+  constexpr int U = Unroll<VT>::U;
+  extern __shared__ __attribute__((aligned(16))) float zs[];  // [k][TT]
+
+  const int layer = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int g = lane & 15;
+  const int col = blockIdx.x * kColsPerBlock + wave * 4 + (lane >> 4);
+  const bool col_ok = col < a.d_out;
+  const int64_t nnz = a.nnz[layer];
+  int s = 0, e = 0;
+  if (col_ok) {  // clamp to [0, nnz] so a malformed colptr cannot index out of bounds
+    s = (int)min<int64_t>(max(a.colptr[layer][col], 0), nnz);
+    e = (int)min<int64_t>(max(a.colptr[layer][col + 1], s), nnz);
+  }
+  const uint16_t* rowidx = a.rowidx[layer];
+  const void* vals = a.vals[layer];
+  const uint8_t* vsc = a.vscales[layer];
+  const int first = (s & ~7) + g * 8;
+  float ts = 1.0f;
+  if constexpr (VT == DFS_NVFP4) ts = *a.vts[layer];
+
+  for (int t0 = 0; t0 < a.T; t0 += TT) {
+    IdxChunk ic[U];
+    ValChunk<VT> vc[U];
+    int p0 = first;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + 128 * u;
+      if (p < e) {
+        ic[u].load(rowidx, p, nnz);
+        vc[u].load(vals, vsc, p, nnz);
+      }
+    }
+    if (t0 > 0) __syncthreads();
+    const int rows = a.T - t0 < TT ? a.T - t0 : TT;
+    stage_z<ZT, TT>(zs, a.Z, (int64_t)layer * a.T + t0, rows, a.k);
+    __syncthreads();
+
+    float acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+    while (p0 < e) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + 128 * u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int q = p + i;
+          if (q >= s && q < e) {
+            const float v = vc[u].get(i);
+            const float* zr = zs + ic[u].get(i) * TT;
+            if constexpr (TT % 4 == 0) {
+#pragma unroll
+              for (int t = 0; t < TT; t += 4) {
+                const f4 z4 = *reinterpret_cast<const f4*>(zr + t);
+                acc[t] = __builtin_fmaf(z4[0], v, acc[t]);
+                acc[t + 1] = __builtin_fmaf(z4[1], v, acc[t + 1]);
+                acc[t + 2] = __builtin_fmaf(z4[2], v, acc[t + 2]);
+                acc[t + 3] = __builtin_fmaf(z4[3], v, acc[t + 3]);
+              }
+            } else {
+#pragma unroll
+              for (int t = 0; t < TT; ++t) acc[t] = __builtin_fmaf(zr[t], v, acc[t]);
+            }
+          }
+        }
+      }
+      p0 += 128 * U;
+      if (p0 < e) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int p = p0 + 128 * u;
+          if (p < e) {
+            ic[u].load(rowidx, p, nnz);
+            vc[u].load(vals, vsc, p, nnz);
+          }
+        }
+      }
+    }
+
+    float out = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const float r = row16_sum(acc[t]);
+      if (g == t) out = r;
+    }
+    if (col_ok && g < rows) {
+      const int64_t o = (int64_t)(t0 + g) * a.ldy + col;
+      out *= ts;
+      if (a.ydt == DFS_F16)
+        ((_Float16*)a.Y[layer])[o] = (_Float16)out;
+      else
+        ((float*)a.Y[layer])[o] = out;
+    }
+  }
+}
+
+template <int VT, int ZT, int TT>
+hipError_t launch3(const ZcLaunch& a, hipStream_t s) {
+  const size_t smem = (size_t)a.k * TT * sizeof(float);
+  auto kern = spmv_csc_kernel<VT, ZT, TT>;
+  if (smem > 64 * 1024) {
+    hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (err != hipSuccess) return err;
+  }
+  dim3 grid((a.d_out + kColsPerBlock - 1) / kColsPerBlock, a.n_layers);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
+  return hipGetLastError();
+}
+
+template <int VT, int ZT>
+hipError_t launch2(const ZcLaunch& a, hipStream_t s) {
+  const int tt = spmv_token_tile(a.T, a.k);
+  switch (tt) {
+    case 1:
+      return launch3<VT, ZT, 1>(a, s);
+    case 2:
+      return launch3<VT, ZT, 2>(a, s);
+    case 4:
+      return launch3<VT, ZT, 4>(a, s);
+    case 8:
+      return launch3<VT, ZT, 8>(a, s);
+    default:
+      return launch3<VT, ZT, 16>(a, s);
+  }
+}
+
+template <int VT>
+hipError_t launch1(const ZcLaunch& a, hipStream_t s) {
+  return a.zdt == DFS_F32 ? launch2<VT, DFS_F32>(a, s) : launch2<VT, DFS_F16>(a, s);
+}
+
+}  // namespace
+
+int spmv_token_tile(int T, int k) {
+  int tt = 1;
+  while (tt < T && tt < 16 && (size_t)k * (tt * 2) * sizeof(float) <= 64 * 1024) tt *= 2;
+  return tt;
+}
+
+hipError_t launch_spmv_csc(const ZcLaunch& a, hipStream_t s) {
+  switch (a.vdt) {
+    case DFS_F16:
+      return launch1<DFS_F16>(a, s);
+    case DFS_F32:
+      return launch1<DFS_F32>(a, s);
+    default:
+      return launch1<DFS_NVFP4>(a, s);
+  }
+}
+
+}  // namespace dfs

@@ -30,7 +30,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-WORKLOAD_IDS = {"tiny": 1, "qproj": 2, "qproj_prefill": 3, "mlp": 4, "stack_nvfp4": 5}
+# The prefill workload is the decode group with 2048 tokens: same D and C.
+WORKLOAD_IDS = {"tiny": 1, "qproj": 2, "qproj_prefill": 2, "mlp": 4, "stack_nvfp4": 5}
 
 PROJ_TYPES = ("q", "k", "v", "o", "gate", "up", "down")
 

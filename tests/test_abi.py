@@ -1,0 +1,166 @@
+"""The C ABI library loads without a GPU, exports every symbol declared in
+include/dictfs.h, and rejects bad arguments in host code before any HIP call.
+
+Every call here fails validation (or is a T = 0 no-op), so nothing reaches
+the GPU even when this file runs on a GPU machine: the pointers passed are
+placeholders that are never dereferenced.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from dictionary_factored_sparse_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dictfs.h")
+
+OK, INVALID, UNSUPPORTED, RANGE, ALIGN, WORKSPACE = 0, 1, 2, 3, 4, 5
+P = 0x10000  # 16-byte aligned placeholder address, never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:dfs_status|const char\*|int32_t)\s+(\w+)\s*\(", src, re.M))
+
+
+def test_header_declares_the_north_star_calls():
+    fns = header_functions()
+    for name in ("dict_pack_csc", "dict_proj_forward", "dict_group_forward", "nvfp4_pack",
+                 "nvfp4_unpack"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    fns = header_functions()
+    assert fns == set(B.SYMBOLS)
+    for name in fns:
+        assert hasattr(L, name), name
+    assert L.dfs_version() == 100
+    assert L.dfs_status_str(0) == b"ok"
+    assert L.dfs_status_str(6) == b"HIP runtime error"
+
+
+def _dict(d_in=256, k=128, dtype=B.DFS_F16, data=P, ldd=None, nv=None):
+    return B.Dict(d_in, k, dtype, 0, data, d_in if ldd is None else ldd, nv or B.NV())
+
+
+def _csc(k=128, d_out=64, nnz=100, dtype=B.DFS_F16, colptr=P, rowidx=P, vals=P, nv=None):
+    return B.Csc(k, d_out, nnz, dtype, 0, colptr, rowidx, vals, nv or B.NV())
+
+
+def _group(n=1, X=P, xdt=B.DFS_F16, T=1, ldx=256, D=None, Cs=None, Y=P, ydt=B.DFS_F16, ldy=64,
+           ws=P, ws_bytes=1 << 30):
+    D = D or _dict()
+    Cs = Cs or [_csc() for _ in range(n)]
+    m = max(n, len(Cs))
+    xp = (C.c_void_p * m)(*([X] * m))
+    yp = (C.c_void_p * m)(*([Y] * m))
+    cs = (B.Csc * len(Cs))(*Cs)
+    return B.lib().dict_group_forward(n, xp, xdt, T, ldx, C.byref(D), cs, yp, ydt, ldy, ws,
+                                      ws_bytes, None)
+
+
+def test_group_forward_validation():
+    assert _group(T=0) == OK                         # empty batch: nothing to do
+    assert _group(D=_dict(d_in=0)) == INVALID
+    assert _group(D=_dict(k=20000)) == RANGE        # Z must fit in LDS
+    assert _group(D=_dict(data=None)) == INVALID
+    assert _group(D=_dict(data=P + 4)) == ALIGN
+    assert _group(D=_dict(ldd=100)) == INVALID      # ldd < d_in
+    assert _group(D=_dict(ldd=260)) == ALIGN        # rows not 16-byte aligned
+    assert _group(D=_dict(dtype=7)) == UNSUPPORTED
+    assert _group(X=P + 2) == ALIGN
+    assert _group(X=0) == INVALID
+    assert _group(ldx=100) == INVALID
+    assert _group(xdt=B.DFS_NVFP4) == UNSUPPORTED
+    assert _group(ydt=B.DFS_NVFP4) == UNSUPPORTED
+    assert _group(ldy=10) == INVALID
+    assert _group(Y=0) == INVALID
+    assert _group(Cs=[_csc(k=64)]) == INVALID       # k mismatch with D
+    assert _group(Cs=[_csc(nnz=-1)]) == INVALID
+    assert _group(Cs=[_csc(nnz=1 << 31)]) == RANGE
+    assert _group(Cs=[_csc(rowidx=P + 2)]) == ALIGN
+    assert _group(Cs=[_csc(colptr=0)]) == INVALID
+    assert _group(Cs=[_csc(dtype=5)]) == UNSUPPORTED
+    assert _group(n=2, Cs=[_csc(), _csc(d_out=65)]) == INVALID
+    assert _group(n=2, Cs=[_csc(), _csc(dtype=B.DFS_F32)]) == UNSUPPORTED
+    assert _group(ws=0) == WORKSPACE
+    assert _group(ws_bytes=16) == WORKSPACE
+    assert _group(n=17, Cs=[_csc()] * 17) == RANGE
+    assert _group(n=0, Cs=[_csc()]) == INVALID
+    # NVFP4 dictionary: d_in must be a multiple of 32 and ldd == d_in
+    nv = B.NV(P, P, P)
+    assert _group(D=_dict(d_in=272, dtype=B.DFS_NVFP4, data=None, nv=nv), ldx=272) == UNSUPPORTED
+    assert _group(D=_dict(dtype=B.DFS_NVFP4, data=None, nv=B.NV(P + 1, P, P))) == ALIGN
+    assert _group(D=_dict(dtype=B.DFS_NVFP4, data=None, nv=B.NV(P, 0, P))) == INVALID
+
+
+def test_proj_forward_validation():
+    L = B.lib()
+    D, c = _dict(), _csc()
+    assert L.dict_proj_forward(P, B.DFS_F16, 0, 256, C.byref(D), C.byref(c), P, B.DFS_F16, 64,
+                               P, 1 << 20, None) == OK
+    assert L.dict_proj_forward(P, B.DFS_F16, -1, 256, C.byref(D), C.byref(c), P, B.DFS_F16, 64,
+                               P, 1 << 20, None) == INVALID
+    assert L.dict_proj_forward(P, B.DFS_F16, 1, 256, None, C.byref(c), P, B.DFS_F16, 64, P,
+                               1 << 20, None) == INVALID
+
+
+def test_pack_csc_validation():
+    L = B.lib()
+    nnz = C.c_int64(0)
+    args = dict(C=P, dt=B.DFS_F16, k=128, d_out=64, ldc=64, colptr=P, rowidx=P, vals=P, cap=10,
+                nnz=C.byref(nnz), ws=P, wsb=1 << 20)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.dict_pack_csc(a["C"], a["dt"], a["k"], a["d_out"], a["ldc"], a["colptr"],
+                               a["rowidx"], a["vals"], a["cap"], a["nnz"], a["ws"], a["wsb"],
+                               None)
+    assert call(C=0) == INVALID
+    assert call(colptr=0) == INVALID
+    assert call(nnz=None) == INVALID
+    assert call(dt=B.DFS_NVFP4) == UNSUPPORTED
+    assert call(k=0) == INVALID
+    assert call(k=65537) == RANGE
+    assert call(ldc=10) == INVALID
+    assert call(rowidx=0) == INVALID          # rowidx and vals both or neither
+    assert call(cap=-1) == INVALID
+    assert call(ws=0) == WORKSPACE
+    assert call(wsb=8) == WORKSPACE
+    n = C.c_size_t(0)
+    assert L.dict_pack_csc_workspace_size(65536, 11008, C.byref(n)) == OK and n.value > 0
+    assert L.dict_pack_csc_workspace_size(65537, 11008, C.byref(n)) == RANGE
+
+
+def test_nvfp4_validation():
+    L = B.lib()
+    assert L.nvfp4_pack(P, -1, B.NV(P, P, P), P, 1 << 20, None) == INVALID
+    assert L.nvfp4_pack(0, 10, B.NV(P, P, P), P, 1 << 20, None) == INVALID
+    assert L.nvfp4_pack(P, 10, B.NV(P + 4, P, P), P, 1 << 20, None) == ALIGN
+    assert L.nvfp4_pack(P, 10, B.NV(P, P, 0), P, 1 << 20, None) == INVALID
+    assert L.nvfp4_pack(P, 10, B.NV(P, P, P), P, 4, None) == WORKSPACE
+    assert L.nvfp4_unpack(B.NV(P, P, P), -5, P, None) == INVALID
+    assert L.nvfp4_unpack(B.NV(P, P, P), 0, P, None) == OK
+    assert L.nvfp4_unpack(B.NV(P, 0, P), 7, P, None) == INVALID
+    n = C.c_size_t(0)
+    assert L.nvfp4_pack_workspace_size(1 << 20, C.byref(n)) == OK and n.value >= 256
+
+
+def test_workspace_sizes():
+    L = B.lib()
+    D, c = _dict(d_in=4096, k=2048), _csc(k=2048, d_out=4096)
+    n = C.c_size_t(0)
+    assert L.dict_workspace_size(2, 1, C.byref(D), C.byref(c), C.byref(n)) == OK
+    assert n.value >= 2 * 2048 * 4
+    assert L.dict_workspace_size(2, 2048, C.byref(D), C.byref(c), C.byref(n)) == OK
+    assert n.value >= 2 * 2048 * 2048 * 2
+    assert L.dict_workspace_size(17, 1, C.byref(D), C.byref(c), C.byref(n)) == RANGE
+    Dn = _dict(d_in=4096, k=2048, dtype=B.DFS_NVFP4, data=None, nv=B.NV(P, P, P))
+    assert L.dict_xd_workspace_size(1, 2048, C.byref(Dn), C.byref(n)) == OK
+    assert n.value >= 4096 * 2048 * 2      # f16 expansion for the MFMA path
+    assert L.dict_xd_workspace_size(1, 1, C.byref(Dn), C.byref(n)) == OK and n.value == 0

@@ -1,0 +1,214 @@
+"""GPU parity of the factored projection Y_l = (X_l D_g) C_l against the
+oracle, through the C ABI, on the seeded workloads (full sizes where the
+oracle is quick, sampled tokens otherwise) and on edge cases.
+
+Bound: max|Y_gpu - Y_ref| <= 2e-3 * max|Y_ref| (fp32 accumulation, fp16 or
+fp32 storage; for NVFP4 factors the reference uses the oracle's own
+dequantised factors)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dictionary_factored_sparse_amd import binding as B
+from dictionary_factored_sparse_amd import synth
+from tests.gpu_helpers import DEV, assert_close, device_group, oracle_group, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_group(g, nvfp4=False, ydtype=torch.float16):
+    D, Cs, Xs = device_group(g, nvfp4=nvfp4)
+    Ys = B.dict_group_forward(Xs, D, Cs, ydtype=ydtype)
+    torch.cuda.synchronize()
+    return Ys, (D, Cs, Xs)
+
+
+@pytest.mark.parametrize("ydtype", [torch.float32, torch.float16])
+def test_tiny_group(ydtype):
+    say(f"case: tiny group, Y {ydtype}")
+    g = synth.make_group("tiny")
+    Ys, _ = _run_group(g, ydtype=ydtype)
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(Ys[l], ref, f"tiny layer {l}")
+
+
+def test_tiny_group_f16_storage():
+    say("case: tiny group stored in f16")
+    g = synth.make_group("tiny", wdtype=np.float16, xdtype=np.float16)
+    Ys, _ = _run_group(g)
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(Ys[l], ref, f"tiny f16 layer {l}")
+
+
+def test_qproj_decode_group_full():
+    say("case: q_proj decode group (2 x 4096->4096, k=2048, density 0.3, T=1)")
+    g = synth.make_group("qproj")
+    Ys, _ = _run_group(g)
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(Ys[l], ref, f"qproj layer {l}")
+
+
+def test_qproj_single_projection_matches_group():
+    say("case: dict_proj_forward vs dict_group_forward")
+    g = synth.make_group("qproj", n_layers=2)
+    D, Cs, Xs = device_group(g)
+    Ys = B.dict_group_forward(Xs, D, Cs)
+    Y1 = B.dict_proj_forward(Xs[1], D, Cs[1])
+    torch.cuda.synchronize()
+    assert torch.equal(Ys[1], Y1)
+
+
+def test_qproj_prefill_full_size_sampled():
+    say("case: q_proj prefill (2 x T=2048), sampled tokens")
+    g = synth.make_group("qproj_prefill")
+    Ys, _ = _run_group(g)
+    rows = np.array([0, 1, 31, 32, 33, 127, 128, 129, 1000, 1023, 1024, 1500, 2015, 2046, 2047])
+    for l, ref in enumerate(oracle_group(g, rows=rows)):
+        assert_close(Ys[l][torch.from_numpy(rows).to(DEV)], ref, f"prefill layer {l}")
+
+
+@pytest.mark.parametrize("T", [17, 100, 300])
+def test_prefill_ragged_tiles_full(T):
+    say(f"case: mid-size prefill T={T} (MFMA + SpMM, ragged tiles)")
+    g = synth.make_group("qproj", d_in=512, d_out=400, k=320, T=T, n_layers=2)
+    Ys, _ = _run_group(g)
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(Ys[l], ref, f"T={T} layer {l}")
+
+
+@pytest.mark.parametrize("ptype", ["gate", "down"])
+def test_mlp_group_b1_full(ptype):
+    say(f"case: MLP {ptype} group of 4, T=1")
+    g = synth.make_group("mlp", ptype=ptype)
+    Ys, _ = _run_group(g)
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(Ys[l], ref, f"mlp {ptype} layer {l}")
+
+
+@pytest.mark.parametrize("ptype", ["up", "down"])
+def test_mlp_group_b16_full(ptype):
+    say(f"case: MLP {ptype} group of 4, T=16 (64 stacked rows, MFMA)")
+    g = synth.make_group("mlp", ptype=ptype, T=16)
+    Ys, _ = _run_group(g)
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(Ys[l], ref, f"mlp b16 {ptype} layer {l}")
+
+
+@pytest.mark.parametrize("ptype", ["q", "gate", "down"])
+def test_stack_nvfp4_group_b1(ptype):
+    say(f"case: NVFP4 {ptype} group of 2, T=1")
+    g = synth.make_group("stack_nvfp4", ptype=ptype, group=3)
+    Ys, _ = _run_group(g, nvfp4=True)
+    for l, ref in enumerate(oracle_group(g, nvfp4=True)):
+        assert_close(Ys[l], ref, f"nvfp4 {ptype} layer {l}")
+
+
+@pytest.mark.parametrize("T", [3, 40])
+def test_nvfp4_small_and_prefill(T):
+    say(f"case: NVFP4 factors, T={T}")
+    g = synth.make_group("stack_nvfp4", d_in=512, d_out=352, k=256, T=T)
+    Ys, _ = _run_group(g, nvfp4=True)
+    for l, ref in enumerate(oracle_group(g, nvfp4=True)):
+        assert_close(Ys[l], ref, f"nvfp4 T={T} layer {l}")
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 9, 16])
+def test_gemv_row_tiles(R):
+    say(f"case: VALU path with {R} stacked rows")
+    g = synth.make_group("qproj", d_in=1024, d_out=256, k=192, T=R, n_layers=1)
+    Ys, _ = _run_group(g)
+    assert_close(Ys[0], oracle_group(g)[0], f"rows={R}")
+
+
+def test_ragged_dims_on_valu_path():
+    say("case: d_in=100 (ragged chunk), d_out=37, k=40, ldx padded")
+    rng = np.random.default_rng(9)
+    d_in, d_out, k, T = 100, 37, 40, 3
+    Dn = rng.standard_normal((k, d_in)).astype(np.float16)
+    Dpad = np.zeros((k, 104), np.float16)
+    Dpad[:, :d_in] = Dn
+    Cd = synth.coefficients(rng, k, d_out, 0.4, np.float16)
+    X = rng.standard_normal((T, d_in)).astype(np.float16)
+    Xpad = np.zeros((T, 104), np.float16)
+    Xpad[:, :d_in] = X
+    Dt = torch.from_numpy(Dpad).to(DEV)
+    D = B.DeviceDict(d_in, k, data=Dt)
+    c = B.to_device_csc(Cd, DEV)
+    Xt = torch.from_numpy(Xpad).to(DEV)[:, :d_in]
+    Y = B.dict_proj_forward(Xt, D, c)
+    torch.cuda.synchronize()
+    ref = O.forward(X, Dn, d_in, O.pack_csc(Cd))
+    assert_close(Y, ref, "ragged")
+
+
+def test_density_zero_and_empty_columns_exact():
+    say("case: density 0 and empty columns give exact zeros")
+    g = synth.make_group("qproj", d_in=256, d_out=96, k=64, T=2, n_layers=2, density=0.0)
+    Ys, _ = _run_group(g)
+    assert all(bool((Y == 0).all()) for Y in Ys)
+    g = synth.make_group("qproj", d_in=256, d_out=96, k=64, T=2, n_layers=1, density=0.5)
+    g.Cs[0][:, [0, 5, 95]] = 0
+    Ys, _ = _run_group(g)
+    assert bool((Ys[0][:, [0, 5, 95]] == 0).all())
+    assert_close(Ys[0], oracle_group(g)[0], "empty columns")
+
+
+def test_density_one_and_one_entry_per_column():
+    say("case: dense C and one entry per column")
+    g = synth.make_group("qproj", d_in=256, d_out=130, k=72, T=5, n_layers=1, density=1.0)
+    Ys, _ = _run_group(g)
+    assert_close(Ys[0], oracle_group(g)[0], "dense C")
+    rng = np.random.default_rng(1)
+    Cd = np.zeros((72, 130), np.float16)
+    Cd[rng.integers(0, 72, 130), np.arange(130)] = rng.standard_normal(130).astype(np.float16) + 3
+    g.Cs[0] = Cd
+    Ys, _ = _run_group(g)
+    assert_close(Ys[0], oracle_group(g)[0], "one entry per column")
+
+
+def test_sixteen_layer_group():
+    say("case: group of 16 layers, T=1")
+    g = synth.make_group("qproj", d_in=512, d_out=256, k=128, T=1, n_layers=16)
+    Ys, _ = _run_group(g)
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(Ys[l], ref, f"16-layer group layer {l}")
+
+
+def test_zero_tokens_is_a_no_op():
+    say("case: T=0")
+    g = synth.make_group("tiny", T=1)
+    D, Cs, Xs = device_group(g)
+    X0 = torch.empty(0, g.d_in, dtype=torch.float32, device=DEV)
+    Y0 = torch.empty(0, g.d_out, dtype=torch.float32, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    B.dict_group_forward([X0, X0], D, Cs, Ys=[Y0, Y0], ws=ws)
+    torch.cuda.synchronize()
+
+
+def test_xd_and_zc_entry_points():
+    say("case: dict_xd_forward then dict_zc_forward")
+    g = synth.make_group("qproj", d_in=1024, d_out=512, k=256, T=4, n_layers=2)
+    D, Cs, Xs = device_group(g)
+    for zdt in (torch.float32, torch.float16):
+        Z = B.dict_xd_forward(Xs, D, zdtype=zdt)
+        Ys = B.dict_zc_forward(Z, g.T, Cs)
+        torch.cuda.synchronize()
+        eye = O.pack_csc(np.eye(g.k, dtype=np.float32))
+        for l in range(2):
+            zref = O.forward(g.Xs[l], g.D, g.d_in, eye)
+            assert_close(Z[l * g.T:(l + 1) * g.T], zref, f"Z layer {l} {zdt}")
+        for l, ref in enumerate(oracle_group(g)):
+            assert_close(Ys[l], ref, f"zc layer {l} {zdt}")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    say("case: determinism")
+    for wl, T in (("qproj", 1), ("qproj", 64)):
+        g = synth.make_group(wl, d_in=2048, d_out=1024, k=512, T=T, n_layers=2)
+        D, Cs, Xs = device_group(g)
+        a = B.dict_group_forward(Xs, D, Cs)
+        b = B.dict_group_forward(Xs, D, Cs)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
