@@ -314,9 +314,10 @@ dfs_status dict_xd_forward(int32_t n_layers, const void* const* X, int32_t xdt, 
   if (n_layers <= 0 || T < 0 || !X) return DFS_E_INVALID;
   if (n_layers > kMaxLayers) return DFS_E_RANGE;
   DFS_TRY(check_dict(D));
-  DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
   if (zdt != DFS_F16 && zdt != DFS_F32) return DFS_E_UNSUPPORTED;
+  if (!is_act_dtype(xdt)) return DFS_E_UNSUPPORTED;
   if (T == 0) return DFS_OK;
+  DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
   if (!Z) return DFS_E_INVALID;
   if (!aligned16(Z)) return DFS_E_ALIGN;
   const size_t need = xd_ws_bytes((int64_t)n_layers * T, xdt, D);
@@ -337,8 +338,9 @@ dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t
     DFS_TRY(check_csc(&C[i], C[0].k, C[0].d_out));
     if (C[i].dtype != C[0].dtype) return DFS_E_UNSUPPORTED;
   }
-  DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
+  if (!is_act_dtype(ydt)) return DFS_E_UNSUPPORTED;
   if (T == 0) return DFS_OK;
+  DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
   if (!Z) return DFS_E_INVALID;
   return run_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy, (hipStream_t)stream);
 }
@@ -350,13 +352,14 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
   if (n_layers <= 0 || T < 0 || !X || !C || !Y) return DFS_E_INVALID;
   if (n_layers > kMaxLayers) return DFS_E_RANGE;
   DFS_TRY(check_dict(D));
-  DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
   for (int i = 0; i < n_layers; ++i) {
     DFS_TRY(check_csc(&C[i], D->k, C[0].d_out));
     if (C[i].dtype != C[0].dtype) return DFS_E_UNSUPPORTED;
   }
+  if (!is_act_dtype(xdt) || !is_act_dtype(ydt)) return DFS_E_UNSUPPORTED;
+  if (T == 0) return DFS_OK;  // no rows: the activation pointers may be null
+  DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
   DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
-  if (T == 0) return DFS_OK;
   const int64_t rows = (int64_t)n_layers * T;
   const bool mfma = mfma_path(rows, xdt, D);
   const int32_t zdt = mfma ? DFS_F16 : DFS_F32;

@@ -76,6 +76,13 @@ def test_pack_of_qproj_coefficients_bit_exact():
     assert np.array_equal(scales, ref.scales) and np.array_equal(codes, ref.codes)
 
 
+def _ws_bytes(n):
+    import ctypes as C
+    b = C.c_size_t(0)
+    assert B.lib().nvfp4_pack_workspace_size(n, C.byref(b)) == 0
+    return b.value
+
+
 def test_pack_rejects_non_finite_and_writes_nothing():
     say("case: nvfp4_pack with NaN / Inf")
     for bad in (np.nan, np.inf):
@@ -83,7 +90,7 @@ def test_pack_rejects_non_finite_and_writes_nothing():
         x[37] = bad
         q = B.DeviceNVFP4.empty(100, DEV)
         q.codes.fill_(0xAB)
-        ws = torch.empty(4096, dtype=torch.uint8, device=DEV)
+        ws = torch.empty(_ws_bytes(100), dtype=torch.uint8, device=DEV)
         xt = torch.from_numpy(x).to(DEV)
         st = B.lib().nvfp4_pack(xt.data_ptr(), 100, q.nv(), ws.data_ptr(), ws.numel(),
                                 torch.cuda.current_stream().cuda_stream)
@@ -95,7 +102,7 @@ def test_pack_rejects_non_finite_and_writes_nothing():
 def test_pack_empty_tensor_sets_unit_scale():
     say("case: nvfp4_pack n=0")
     q = B.DeviceNVFP4.empty(0, DEV)
-    ws = torch.empty(4096, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(_ws_bytes(0), dtype=torch.uint8, device=DEV)
     st = B.lib().nvfp4_pack(None, 0, q.nv(), ws.data_ptr(), ws.numel(),
                             torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
