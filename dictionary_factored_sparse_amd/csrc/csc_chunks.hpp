@@ -73,14 +73,15 @@ struct ValChunk<DFS_F32> {
 };
 
 // NVFP4: decoded value = e2m1 * e4m3(block scale); the tensor scale is
-// applied once to the finished dot product.
+// applied once to the finished dot product.  The chunk keeps the raw code
+// word and decodes on use (hardware E2M1 conversion, exact with scale 1).
 template <>
 struct ValChunk<DFS_NVFP4> {
-  float v[8];
+  uint32_t word;
+  float s;
   __device__ __forceinline__ void load(const void* vals, const uint8_t* scales, int64_t p,
                                        int64_t nnz) {
     const uint8_t* codes = (const uint8_t*)vals;
-    uint32_t word;
     if (p + 8 <= nnz) {
       word = *reinterpret_cast<const uint32_t*>(codes + p / 2);
     } else {
@@ -88,13 +89,19 @@ struct ValChunk<DFS_NVFP4> {
       for (int i = 0; i < 8; i += 2)
         if (p + i < nnz) word |= (uint32_t)codes[(p + i) / 2] << (4 * i);
     }
-    const float s = e4m3_to_f32(scales[p / 16]);
-    const f2 a = e2m1x2_f2<0>(word), b = e2m1x2_f2<1>(word), c = e2m1x2_f2<2>(word),
-             d = e2m1x2_f2<3>(word);
-    v[0] = a[0] * s; v[1] = a[1] * s; v[2] = b[0] * s; v[3] = b[1] * s;
-    v[4] = c[0] * s; v[5] = c[1] * s; v[6] = d[0] * s; v[7] = d[1] * s;
+    s = e4m3_to_f32(scales[p / 16]);
   }
-  __device__ __forceinline__ float get(int i) const { return v[i]; }
+  // i is a compile-time constant after unrolling, so the switch folds away.
+  __device__ __forceinline__ float get(int i) const {
+    f2 v;
+    switch (i >> 1) {
+      case 0: v = e2m1x2_f2<0>(word); break;
+      case 1: v = e2m1x2_f2<1>(word); break;
+      case 2: v = e2m1x2_f2<2>(word); break;
+      default: v = e2m1x2_f2<3>(word); break;
+    }
+    return v[i & 1] * s;
+  }
 };
 
 }  // namespace dfs

@@ -149,12 +149,102 @@ __device__ __forceinline__ float dot_chunk(u4 d, uint32_t sc2, const XS* x, floa
   }
 }
 
-template <int DT, int XT, int RT>
+// Stage rows [row0, row0 + RT) x elements [e_begin, e_begin + n_el) of the
+// stacked X into LDS rows of stride `ld` (zero padded past d_in and past the
+// last row), 8 elements per item, kUnr items per thread in flight.  Row base
+// pointers are wave-uniform and come from scalar loads, so the vector-memory
+// counter only ever waits on these X loads here.
+template <int XT, int RT, typename XS>
+__device__ __forceinline__ void stage_x(XS* xs, const XdLaunch& a, int row0, int e_begin,
+                                        int n_el, int ld) {
+  constexpr int kUnr = 4;
+  constexpr int kWords = XT == DFS_F16 ? 4 : 8;  // 32-bit words per 8 elements
+  constexpr int esz = XT == DFS_F16 ? 2 : 4;
+  const int R = a.n_layers * a.T;
+  const char* rowp[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int row = row0 + r;
+    rowp[r] = nullptr;
+    if (row < R) {
+      const int l = row / a.T, t = row - l * a.T;
+      rowp[r] = (const char*)a.X[l] + (int64_t)t * a.ldx * esz;
+    }
+  }
+  const int per_row = n_el / 8;
+  const int n_items = RT * per_row;
+  for (int base = 0; base < n_items; base += kThreads * kUnr) {
+    uint32_t v[kUnr][kWords];
+#pragma unroll
+    for (int j = 0; j < kUnr; ++j) {
+      const int item = base + j * kThreads + threadIdx.x;
+      const int r = item / per_row;
+      const int ge = e_begin + (item - r * per_row) * 8;
+      const char* p = rowp[0];
+#pragma unroll
+      for (int rr = 1; rr < RT; ++rr)
+        if (r == rr) p = rowp[rr];
+#pragma unroll
+      for (int w = 0; w < kWords; ++w) v[j][w] = 0u;
+      if (item < n_items && p != nullptr && ge < a.d_in) {
+        p += (int64_t)ge * esz;
+        if (ge + 8 <= a.d_in) {
+          const u4 q0 = ld16<u4>(p);
+          v[j][0] = q0[0]; v[j][1] = q0[1]; v[j][2] = q0[2]; v[j][3] = q0[3];
+          if constexpr (XT == DFS_F32) {
+            const u4 q1 = ld16<u4>(p + 16);
+            v[j][4] = q1[0]; v[j][5] = q1[1]; v[j][6] = q1[2]; v[j][7] = q1[3];
+          }
+        } else {
+          for (int e = 0; e < a.d_in - ge; ++e) {
+            if constexpr (XT == DFS_F16) {
+              const uint32_t h = ((const uint16_t*)p)[e];
+              v[j][e >> 1] |= (e & 1) ? (h << 16) : h;
+            } else {
+              v[j][e] = ((const uint32_t*)p)[e];
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kUnr; ++j) {
+      const int item = base + j * kThreads + threadIdx.x;
+      if (item < n_items) {
+        const int r = item / per_row;
+        XS* dst = xs + r * ld + (item - r * per_row) * 8;
+        if constexpr (sizeof(XS) == 2) {
+          *reinterpret_cast<u4*>(dst) = u4{v[j][0], v[j][1], v[j][2], v[j][3]};
+        } else if constexpr (XT == DFS_F16) {  // f16 -> f32 in LDS
+          f4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wl = v[j][e >> 1], wh = v[j][2 + (e >> 1)];
+            lo[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)((e & 1) ? wl >> 16 : wl));
+            hi[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)((e & 1) ? wh >> 16 : wh));
+          }
+          *reinterpret_cast<f4*>(dst) = lo;
+          *reinterpret_cast<f4*>(dst + 4) = hi;
+        } else {  // f32 -> f32
+          *reinterpret_cast<u4*>(dst) = u4{v[j][0], v[j][1], v[j][2], v[j][3]};
+          *reinterpret_cast<u4*>(dst + 4) = u4{v[j][4], v[j][5], v[j][6], v[j][7]};
+        }
+      }
+    }
+  }
+}
+
+// kWholeX: all of X[row0 .. row0+RT) is staged once (LDS row stride = d_in
+// rounded up to SEG); otherwise one SEG-wide slice is staged per segment.
+// In both cases the X loads complete before any D load is issued, and the D
+// loads of a segment are all in flight before its first multiply.
+template <int DT, int XT, int RT, bool kTail, bool kWholeX>
 __global__ __launch_bounds__(kThreads) void gemv_xd_kernel(XdLaunch a) {
   using C = Cfg<DT, XT, RT>;
   using XS = typename C::XS;
   constexpr int CE = C::CE, A = C::A, SEGC = C::SEGC, SEG = C::SEG;
-  __shared__ __attribute__((aligned(16))) XS xs[RT * SEG];
+  extern __shared__ __attribute__((aligned(16))) char xs_raw[];
+  XS* xs = reinterpret_cast<XS*>(xs_raw);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -162,6 +252,12 @@ __global__ __launch_bounds__(kThreads) void gemv_xd_kernel(XdLaunch a) {
   const int R = a.n_layers * a.T;
   const int row0 = blockIdx.y * RT;
   const int d_in = a.d_in;
+  const int ld = kWholeX ? (d_in + SEG - 1) / SEG * SEG : SEG;
+
+  if constexpr (kWholeX) {
+    stage_x<XT, RT, XS>(xs, a, row0, 0, ld, ld);
+    __syncthreads();
+  }
 
   float acc[A][RT];
 #pragma unroll
@@ -170,7 +266,11 @@ __global__ __launch_bounds__(kThreads) void gemv_xd_kernel(XdLaunch a) {
     for (int r = 0; r < RT; ++r) acc[i][r] = 0.0f;
 
   for (int seg = 0; seg < d_in; seg += SEG) {
-    // 1. issue every D chunk load of this segment
+    if constexpr (!kWholeX) {
+      if (seg > 0) __syncthreads();
+      stage_x<XT, RT, XS>(xs, a, row0, seg, SEG, SEG);
+    }
+    // issue every D chunk load of this segment
     u4 dreg[A][SEGC];
     uint32_t sreg[A][SEGC];
 #pragma unroll
@@ -188,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xd_kernel(XdLaunch a) {
             sreg[i][c] = (uint32_t)a.dscales[el / 16] | ((uint32_t)a.dscales[el / 16 + 1] << 8);
           } else {
             const char* p = (const char*)a.D + ((int64_t)atom * a.ldd + e0) * (DT == DFS_F32 ? 4 : 2);
-            if (e0 + CE <= d_in)
+            if (!kTail || e0 + CE <= d_in)
               dreg[i][c] = ld16<u4>(p);
             else
               dreg[i][c] = load_chunk_tail<DT>(p, d_in - e0);
@@ -196,26 +296,9 @@ __global__ __launch_bounds__(kThreads) void gemv_xd_kernel(XdLaunch a) {
         }
       }
     }
+    if constexpr (!kWholeX) __syncthreads();
 
-    // 2. stage the X segment of every row of this tile (zero padded)
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < RT * SEG; idx += kThreads) {
-      const int r = idx / SEG, e = idx - r * SEG;
-      const int row = row0 + r;
-      const int ge = seg + e;
-      float v = 0.0f;
-      if (row < R && ge < d_in) {
-        const int l = row / a.T, t = row - l * a.T;
-        if (a.xdt == DFS_F16)
-          v = (float)(((const _Float16*)a.X[l])[(int64_t)t * a.ldx + ge]);
-        else
-          v = ((const float*)a.X[l])[(int64_t)t * a.ldx + ge];
-      }
-      xs[idx] = (XS)v;
-    }
-    __syncthreads();
-
-    // 3. accumulate
+    const XS* xseg = xs + (kWholeX ? seg : 0);
 #pragma unroll
     for (int c = 0; c < SEGC; ++c) {
       const int el = (c * kWave + lane) * CE;
@@ -223,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xd_kernel(XdLaunch a) {
       for (int r = 0; r < RT; ++r) {
 #pragma unroll
         for (int i = 0; i < A; ++i)
-          acc[i][r] = dot_chunk<DT, C::kDot2, XS>(dreg[i][c], sreg[i][c], xs + r * SEG + el, acc[i][r]);
+          acc[i][r] = dot_chunk<DT, C::kDot2, XS>(dreg[i][c], sreg[i][c], xseg + r * ld + el, acc[i][r]);
       }
     }
   }
@@ -247,13 +330,26 @@ __global__ __launch_bounds__(kThreads) void gemv_xd_kernel(XdLaunch a) {
   }
 }
 
+template <int DT, int XT, int RT, bool kTail>
+hipError_t launch_w(const XdLaunch& a, hipStream_t s, dim3 grid) {
+  using C = Cfg<DT, XT, RT>;
+  const size_t whole = (size_t)RT * ((a.d_in + C::SEG - 1) / C::SEG * C::SEG) * sizeof(typename C::XS);
+  if (whole <= (size_t)kLdsBudget) {
+    hipLaunchKernelGGL((gemv_xd_kernel<DT, XT, RT, kTail, true>), grid, dim3(kThreads), whole, s, a);
+  } else {
+    const size_t seg = (size_t)RT * C::SEG * sizeof(typename C::XS);
+    hipLaunchKernelGGL((gemv_xd_kernel<DT, XT, RT, kTail, false>), grid, dim3(kThreads), seg, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int DT, int XT, int RT>
 hipError_t launch_rt(const XdLaunch& a, hipStream_t s) {
   constexpr int A = DTraits<DT>::A;
   const int R = a.n_layers * a.T;
   dim3 grid((a.k + kWaves * A - 1) / (kWaves * A), (R + RT - 1) / RT);
-  hipLaunchKernelGGL((gemv_xd_kernel<DT, XT, RT>), grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  if (a.d_in % DTraits<DT>::CE == 0) return launch_w<DT, XT, RT, false>(a, s, grid);
+  return launch_w<DT, XT, RT, true>(a, s, grid);
 }
 
 template <int DT, int XT>

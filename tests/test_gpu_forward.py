@@ -212,3 +212,31 @@ def test_repeat_runs_are_bitwise_identical():
         torch.cuda.synchronize()
         for x, y in zip(a, b):
             assert torch.equal(x, y)
+
+
+def test_graph_replays_match_eager():
+    say("case: HIP graph capture of dict_group_forward, replayed with eager work between")
+    g = synth.make_group("qproj", d_in=1024, d_out=768, k=512, T=1, n_layers=2)
+    D, Cs, Xs = device_group(g)
+    Ys = [torch.empty(1, g.d_out, dtype=torch.float16, device=DEV) for _ in range(2)]
+    ws = B.workspace(2, 1, D, Cs[0], DEV)
+    B.dict_group_forward(Xs, D, Cs, Ys=Ys, ws=ws)
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in Ys]
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.dict_group_forward(Xs, D, Cs, Ys=Ys, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        B.dict_group_forward(Xs, D, Cs, Ys=Ys, ws=ws)
+    for i in range(4):
+        for y in Ys:
+            y.fill_(float(i + 7))        # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for y, r in zip(Ys, ref):
+            assert torch.equal(y, r), f"replay {i}"
