@@ -147,6 +147,8 @@ def main():
     ms_step_eager = ev0.elapsed_time(ev1) / K
 
     # ---------------------------------------------------------------- per kernel
+    # The step above is one kernel (the one-launch decode).  For comparison,
+    # the same group on the two-launch path, and each of its kernels alone.
     def xd(i):
         D, _ = reps[i % R]
         B.dict_xd_forward(Xs, D, Z=Z)
@@ -155,19 +157,29 @@ def main():
         _, Cs = reps[i % R]
         B.dict_zc_forward(Z, g.T, Cs, Ys=Ys)
 
-    kern = {}
-    for name, fn, nbytes in (("gemv_xd", xd, xd_bytes), ("spmv_csc", zc, zc_bytes)):
-        gr = capture(fn, K)
+    def timed_graph(fn, n):
+        gr = capture(fn, n)
         gr.replay()
         torch.cuda.synchronize()
         ev0.record()
         gr.replay()
         ev1.record()
         torch.cuda.synchronize()
-        us = ev0.elapsed_time(ev1) / K * 1e3
+        return ev0.elapsed_time(ev1) / n * 1e3  # us per call
+
+    kern = {"fused_decode": dict(us=ms_step * 1e3, bytes=step_bytes,
+                                 gbs=step_bytes / (ms_step * 1e-3) / 1e9)}
+    for name, fn, nbytes in (("gemv_xd", xd, xd_bytes), ("spmv_csc", zc, zc_bytes)):
+        us = timed_graph(fn, K)
         kern[name] = dict(us=us, bytes=nbytes, gbs=nbytes / (us * 1e-6) / 1e9)
-        _log(f"{name}: {us:.2f} us/launch, {kern[name]['gbs']:.0f} GB/s")
-    dom = max(kern, key=lambda n: kern[n]["us"])
+    os.environ["DFS_DECODE_PATH"] = "two"
+    us_two = timed_graph(step, K)
+    os.environ.pop("DFS_DECODE_PATH")
+    for n, v in kern.items():
+        _log(f"{n}: {v['us']:.2f} us/launch, {v['gbs']:.0f} GB/s")
+    _log(f"two-launch step: {us_two:.2f} us")
+    dom = "fused_decode"
+    assert B.workspace_error_word(ws) == 0, "grid barrier timed out"
 
     # ---------------------------------------------------------------- prefill (extra)
     extras = {}
@@ -234,6 +246,7 @@ def main():
         "ms_per_step": round(ms_step, 5),
         "us_per_projection": round(ms_step * 1e3 / 2, 3),
         "eager_ms_per_step": round(ms_step_eager, 5),
+        "two_launch_ms_per_step": round(us_two * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -241,7 +254,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "q_proj decode group: 2 layers, d_in=d_out=4096, k=2048, "
                                "C density 0.30 CSC uint16 f16, T=1 f16",
-                   "bytes_per_step": step_bytes, "replicas": R, "timing": "hip graph replay"},
+                   "bytes_per_step": step_bytes, "replicas": R, "timing": "hip graph replay",
+                   "path": "one-launch decode (Z = X D, grid barrier, Y_l = Z_l C_l)"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(d["gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,

@@ -247,7 +247,15 @@ def dict_workspace_size(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC) -> 
 
 
 def workspace(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC, device) -> torch.Tensor:
-    return torch.empty(dict_workspace_size(n_layers, T, D, Cs), dtype=torch.uint8, device=device)
+    """Forward workspace.  Zeroed: its first 256 bytes are the control block
+    the library requires to be zero before first use (it leaves them zero)."""
+    return torch.zeros(dict_workspace_size(n_layers, T, D, Cs), dtype=torch.uint8, device=device)
+
+
+def workspace_error_word(ws: torch.Tensor) -> int:
+    """Word 32 of the control block: non-zero if a one-launch decode timed
+    out at its grid barrier (results of that call are invalid)."""
+    return int(ws[128:132].view(torch.int32).item())
 
 
 def dict_group_forward(Xs, D: DeviceDict, Cs, Ys=None, ydtype=torch.float16, ws=None,

@@ -6,6 +6,7 @@
 // MFMA above that; Y_l = Z_l C_l on the CSC SpMV for T <= 16 tokens per
 // layer and on the token-tiled SpMM above that.  Every argument is checked
 // before anything is enqueued.
+#include <cstdlib>
 #include <cstring>
 
 #include "dfs_internal.hpp"
@@ -118,9 +119,8 @@ size_t xd_ws_bytes(int64_t rows, int32_t xdt, const dfs_dict* D) {
   return 0;
 }
 
-// Z = X D for the stacked rows; Z row-major (rows x k) of dtype zdt.
-dfs_status run_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64_t ldx,
-                  const dfs_dict* D, void* Z, int32_t zdt, void* ws, hipStream_t s) {
+XdLaunch make_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64_t ldx,
+                 const dfs_dict* D, void* Z, int32_t zdt) {
   XdLaunch a;
   std::memset(&a, 0, sizeof(a));
   for (int i = 0; i < n; ++i) a.X[i] = X[i];
@@ -138,25 +138,11 @@ dfs_status run_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64
   a.dts = D->nv.tensor_scale;
   a.Z = Z;
   a.zdt = zdt;
-  const int64_t rows = (int64_t)n * T;
-  if (mfma_path(rows, xdt, D)) {
-    if (D->dtype == DFS_NVFP4) {
-      _Float16* dh = (_Float16*)ws;
-      DFS_HIP(launch_nvfp4_to_f16(D->nv.codes, D->nv.scales, D->nv.tensor_scale,
-                                  (int64_t)D->k * D->d_in, dh, s));
-      a.D = dh;
-      a.ldd = D->d_in;
-      a.ddt = DFS_F16;
-    }
-    DFS_HIP(launch_gemm_xd_mfma(a, s));
-  } else {
-    DFS_HIP(launch_gemv_xd(a, s));
-  }
-  return DFS_OK;
+  return a;
 }
 
-dfs_status run_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc* C,
-                  void* const* Y, int32_t ydt, int64_t ldy, hipStream_t s) {
+ZcLaunch make_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc* C,
+                 void* const* Y, int32_t ydt, int64_t ldy) {
   ZcLaunch a;
   std::memset(&a, 0, sizeof(a));
   a.Z = Z;
@@ -181,12 +167,47 @@ dfs_status run_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_cs
   }
   a.ydt = ydt;
   a.ldy = ldy;
+  return a;
+}
+
+// Z = X D for the stacked rows; Z row-major (rows x k) of dtype zdt.
+dfs_status run_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64_t ldx,
+                  const dfs_dict* D, void* Z, int32_t zdt, void* ws, hipStream_t s) {
+  XdLaunch a = make_xd(n, X, xdt, T, ldx, D, Z, zdt);
+  const int64_t rows = (int64_t)n * T;
+  if (mfma_path(rows, xdt, D)) {
+    if (D->dtype == DFS_NVFP4) {
+      _Float16* dh = (_Float16*)ws;
+      DFS_HIP(launch_nvfp4_to_f16(D->nv.codes, D->nv.scales, D->nv.tensor_scale,
+                                  (int64_t)D->k * D->d_in, dh, s));
+      a.D = dh;
+      a.ldd = D->d_in;
+      a.ddt = DFS_F16;
+    }
+    DFS_HIP(launch_gemm_xd_mfma(a, s));
+  } else {
+    DFS_HIP(launch_gemv_xd(a, s));
+  }
+  return DFS_OK;
+}
+
+dfs_status run_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc* C,
+                  void* const* Y, int32_t ydt, int64_t ldy, hipStream_t s) {
+  ZcLaunch a = make_zc(n, Z, zdt, T, C, Y, ydt, ldy);
   if (T <= kGemvMaxRows)
     DFS_HIP(launch_spmv_csc(a, s));
   else
     DFS_HIP(launch_spmm_csc(a, s));
   return DFS_OK;
 }
+
+// DFS_DECODE_PATH=two forces the two-launch decode (for comparisons).
+bool fused_allowed() {
+  const char* v = std::getenv("DFS_DECODE_PATH");
+  return !(v && std::strcmp(v, "two") == 0);
+}
+
+constexpr size_t kCtrlBytes = 256;  // grid-barrier words at the start of the workspace
 
 }  // namespace
 
@@ -304,7 +325,7 @@ dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, c
   DFS_TRY(check_dict(D));
   if (!C || C->k != D->k || C->d_out <= 0) return DFS_E_INVALID;
   const int64_t rows = (int64_t)n_layers * T;
-  *bytes = round256((size_t)rows * D->k * 4) + xd_ws_bytes(rows, DFS_F16, D) + 256;
+  *bytes = kCtrlBytes + round256((size_t)rows * D->k * 4) + xd_ws_bytes(rows, DFS_F16, D);
   return DFS_OK;
 }
 
@@ -364,12 +385,21 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
   const bool mfma = mfma_path(rows, xdt, D);
   const int32_t zdt = mfma ? DFS_F16 : DFS_F32;
   const size_t zbytes = round256((size_t)rows * D->k * esize(zdt));
-  const size_t need = zbytes + xd_ws_bytes(rows, xdt, D);
+  const size_t need = kCtrlBytes + zbytes + xd_ws_bytes(rows, xdt, D);
   if (!ws || ws_bytes < need) return DFS_E_WORKSPACE;
   if (!aligned16(ws)) return DFS_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  void* Z = ws;
-  void* xws = (char*)ws + zbytes;
+  uint32_t* ctrl = (uint32_t*)ws;
+  void* Z = (char*)ws + kCtrlBytes;
+  void* xws = (char*)Z + zbytes;
+  if (!mfma && fused_allowed()) {
+    XdLaunch xa = make_xd(n_layers, X, xdt, T, ldx, D, Z, zdt);
+    ZcLaunch za = make_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy);
+    if (fused_decode_supported(xa, za)) {
+      DFS_HIP(launch_fused_decode(xa, za, (float*)Z, ctrl, s));
+      return DFS_OK;
+    }
+  }
   DFS_TRY(run_xd(n_layers, X, xdt, T, ldx, D, Z, zdt, xws, s));
   return run_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy, s);
 }

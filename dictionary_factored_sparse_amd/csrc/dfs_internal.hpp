@@ -113,6 +113,20 @@ struct ZcLaunch {
 // Rows at or below which X.D runs on VALU dot products instead of MFMA.
 constexpr int kGemvMaxRows = 16;
 
+// One-launch decode of a group (T == 1, up to 4 layers).
+constexpr int kFusedMaxLayers = 4;
+struct FusedLaunch {
+  XdLaunch xd;
+  ZcLaunch zc;
+  float* zws;          // n_layers x k fp32 scratch for Z
+  uint32_t* ctrl;      // grid-barrier words (zero before first use)
+  uint32_t spin_limit; // polls before a waiting workgroup gives up
+  int32_t col_bytes;   // LDS bytes of the column-range table
+};
+bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc);
+hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, float* zws,
+                               uint32_t* ctrl, hipStream_t s);
+
 hipError_t launch_gemv_xd(const XdLaunch& a, hipStream_t s);
 hipError_t launch_gemm_xd_mfma(const XdLaunch& a, hipStream_t s);
 hipError_t launch_nvfp4_to_f16(const uint8_t* codes, const uint8_t* scales, const float* ts,

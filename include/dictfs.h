@@ -151,7 +151,15 @@ dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream);
 
 /* Workspace bytes for dict_group_forward over n_layers layers of T tokens
  * (dict_proj_forward: n_layers = 1).  D and C describe the shapes and dtypes
- * (C may point at any one layer's descriptor; only k/d_out/dtype are read). */
+ * (C may point at any one layer's descriptor; only k/d_out/dtype are read).
+ *
+ * Forward workspace contract: its first 256 bytes are a control block that
+ * must be ZERO before the first forward call that uses the workspace (e.g.
+ * hipMemset once after allocation); every call leaves it zero again.  Calls
+ * sharing one workspace must not run concurrently.  After a call, the 32-bit
+ * word at byte offset 128 is non-zero only if the one-launch decode path
+ * (T = 1, <= 4 layers) gave up waiting at its grid barrier, in which case
+ * that call's outputs are invalid. */
 dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, const dfs_csc* C,
                                size_t* bytes);
 
@@ -168,6 +176,9 @@ dfs_status dict_proj_forward(const void* X, int32_t xdt, int32_t T, int64_t ldx,
  * for l in [0, n_layers): Y[l] = (X[l] D_g) C[l].  The n_layers * T rows are
  * contracted against D_g in one pass, so D_g is read from memory once per
  * group rather than once per layer; then one launch applies every C_l.
+ * Decode (T = 1, <= 4 layers, f16 X, f16/NVFP4 D and C) runs both halves in
+ * a single launch with a grid barrier between them (environment variable
+ * DFS_DECODE_PATH=two selects the two-launch path instead).
  *   X, Y: host arrays of n_layers device pointers; C: host array of n_layers
  *   descriptors sharing k and d_out.  1 <= n_layers <= 16 (the largest
  *   group the pages study). */

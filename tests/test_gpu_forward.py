@@ -240,3 +240,52 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for y, r in zip(Ys, ref):
             assert torch.equal(y, r), f"replay {i}"
+
+
+def _both_paths(g, nvfp4=False):
+    import os
+    D, Cs, Xs = device_group(g, nvfp4=nvfp4)
+    ws = B.workspace(g.n_layers, g.T, D, Cs[0], DEV)
+    out = {}
+    for path in ("fused", "two"):
+        if path == "two":
+            os.environ["DFS_DECODE_PATH"] = "two"
+        try:
+            out[path] = B.dict_group_forward(Xs, D, Cs, ws=ws)
+            torch.cuda.synchronize()
+        finally:
+            os.environ.pop("DFS_DECODE_PATH", None)
+        assert B.workspace_error_word(ws) == 0
+        assert bool((ws[:256] == 0).all()), "control block not left at zero"
+    return out
+
+
+@pytest.mark.parametrize("wl,ptype,nvfp4,n", [("qproj", "q", False, 2), ("qproj", "q", False, 1),
+                                              ("mlp", "up", False, 4), ("mlp", "down", False, 3),
+                                              ("stack_nvfp4", "q", True, 2),
+                                              ("stack_nvfp4", "down", True, 2)])
+def test_one_launch_decode_matches_two_launch_and_oracle(wl, ptype, nvfp4, n):
+    say(f"case: one-launch decode vs two launches, {wl} {ptype} n={n} nvfp4={nvfp4}")
+    g = synth.make_group(wl, ptype=ptype, n_layers=n, T=1)
+    out = _both_paths(g, nvfp4=nvfp4)
+    refs = oracle_group(g, nvfp4=nvfp4)
+    for l, ref in enumerate(refs):
+        assert_close(out["fused"][l], ref, f"fused layer {l}")
+        assert_close(out["two"][l], ref, f"two-launch layer {l}")
+
+
+def test_one_launch_decode_repeated_launches_identical():
+    say("case: one-launch decode, 50 back-to-back launches on one workspace")
+    g = synth.make_group("qproj", d_in=2048, d_out=3000, k=1024, T=1, n_layers=2)
+    D, Cs, Xs = device_group(g)
+    ws = B.workspace(2, 1, D, Cs[0], DEV)
+    first = [y.clone() for y in B.dict_group_forward(Xs, D, Cs, ws=ws)]
+    Ys = [torch.empty_like(y) for y in first]
+    for _ in range(50):
+        B.dict_group_forward(Xs, D, Cs, Ys=Ys, ws=ws)
+    torch.cuda.synchronize()
+    assert B.workspace_error_word(ws) == 0
+    for y, f in zip(Ys, first):
+        assert torch.equal(y, f)
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(first[l], ref, f"layer {l}")
