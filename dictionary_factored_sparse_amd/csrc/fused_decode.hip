@@ -17,8 +17,8 @@
 // barrier instead of a second launch.
 //
 // Grid barrier: a counter and a generation word in the workspace control
-// block (zero before first use; the last arriver resets the counter, so the
-// block is zero again after every launch).  The grid never exceeds one
+// block (the counter is zero before first use; the last arriver resets it,
+// so it is zero again after every launch; the generation word only grows).  The grid never exceeds one
 // workgroup per CU, so every workgroup is resident; the wait is bounded
 // anyway: after `spin_limit` polls a workgroup sets the error word and goes
 // on, so the kernel always terminates.
