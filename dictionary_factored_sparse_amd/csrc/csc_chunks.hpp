@@ -19,7 +19,7 @@ struct IdxChunk {
     } else {
       uint32_t t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int i = 0; i < 8; ++i)
-        if (p + i < nnz) t[i] = rowidx[p + i];
+        if (p + i < nnz) t[i] = gptr(rowidx)[p + i];
       w = u4{t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16)};
     }
   }
@@ -41,7 +41,7 @@ struct ValChunk<DFS_F16> {
     } else {
       uint32_t t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int i = 0; i < 8; ++i)
-        if (p + i < nnz) t[i] = v[p + i];
+        if (p + i < nnz) t[i] = gptr(v)[p + i];
       w = u4{t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16)};
     }
   }
@@ -62,7 +62,7 @@ struct ValChunk<DFS_F32> {
     } else {
       uint32_t t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int i = 0; i < 8; ++i)
-        if (p + i < nnz) t[i] = v[p + i];
+        if (p + i < nnz) t[i] = gptr(v)[p + i];
       w0 = u4{t[0], t[1], t[2], t[3]};
       w1 = u4{t[4], t[5], t[6], t[7]};
     }
@@ -83,13 +83,13 @@ struct ValChunk<DFS_NVFP4> {
                                        int64_t nnz) {
     const uint8_t* codes = (const uint8_t*)vals;
     if (p + 8 <= nnz) {
-      word = *reinterpret_cast<const uint32_t*>(codes + p / 2);
+      word = *gptr(reinterpret_cast<const uint32_t*>(codes + p / 2));
     } else {
       word = 0;
       for (int i = 0; i < 8; i += 2)
-        if (p + i < nnz) word |= (uint32_t)codes[(p + i) / 2] << (4 * i);
+        if (p + i < nnz) word |= (uint32_t)gptr(codes)[(p + i) / 2] << (4 * i);
     }
-    s = e4m3_to_f32(scales[p / 16]);
+    s = e4m3_to_f32(gptr(scales)[p / 16]);
   }
   // i is a compile-time constant after unrolling, so the switch folds away.
   __device__ __forceinline__ float get(int i) const {

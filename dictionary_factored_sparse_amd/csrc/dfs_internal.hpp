@@ -70,10 +70,23 @@ __device__ __forceinline__ f2 e2m1x2_f2(uint32_t word) {
 
 __device__ __forceinline__ float h2f(_Float16 h) { return (float)h; }
 
+// View of a pointer in the global address space.  Loads through it are
+// global_load (vector-memory counter only); through a generic pointer whose
+// origin the compiler cannot see (e.g. read back from LDS) they would be
+// flat_load, which also holds the LDS counter.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gptr(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gptr_w(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 // 16-byte global load through the vector path.
 template <typename T>
 __device__ __forceinline__ T ld16(const void* p) {
-  return *reinterpret_cast<const T*>(p);
+  return *gptr(reinterpret_cast<const T*>(p));
 }
 
 // ------------------------------------------------------------------ launches

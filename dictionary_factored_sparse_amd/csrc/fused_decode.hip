@@ -31,31 +31,42 @@ namespace {
 using namespace gemv;
 
 constexpr int kU = 6;  // 8-entry C chunks per lane per batch
+constexpr int kLayerTableBytes = 256;
 
-template <typename T>
-__device__ __forceinline__ T pick(const T (&arr)[kMaxLayers], int l) {
-  T v = arr[0];
-#pragma unroll
-  for (int i = 1; i < kFusedMaxLayers; ++i)
-    if (l == i) v = arr[i];
-  return v;
-}
+// Per-layer pointers live in a small LDS table: looking one up for a
+// lane-dependent layer is an LDS read (LGKM counter), not a vector load
+// from the kernel arguments that would have to wait behind the C stream.
+struct LayerRow {
+  const int32_t* colptr;
+  const uint16_t* rowidx;
+  const void* vals;
+  const uint8_t* vsc;
+  const float* vts;
+  void* Y;
+  int64_t nnz;
+};
 
+// Release: every wave waits for its own Z stores to complete (they reach the
+// XCD's L2; L1 is write-through), then one thread per workgroup performs the
+// agent-scope release (write back the L2 for other XCDs) with its arrival.
+// Acquire: the same thread's agent-scope acquire invalidates this CU's L1
+// and the XCD's L2 before any wave reads Z.  One fence pair per workgroup,
+// not per thread: agent-scope fences are cache-wide operations.
 __device__ void grid_barrier(uint32_t* ctrl, uint32_t G, uint32_t spin_limit) {
   uint32_t* count = ctrl;
   uint32_t* gen = ctrl + 16;
   uint32_t* err = ctrl + 32;
-  __threadfence();  // this thread's Z stores visible at agent scope
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are done
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t old = __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (old == G - 1) {
       __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       uint32_t it = 0;
-      while (__hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+      while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
         if (++it > spin_limit) {
           __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
@@ -63,9 +74,9 @@ __device__ void grid_barrier(uint32_t* ctrl, uint32_t G, uint32_t spin_limit) {
         __builtin_amdgcn_s_sleep(1);
       }
     }
+    __atomic_thread_fence(__ATOMIC_ACQUIRE);  // agent-scope acquire (system in HIP => >= agent)
   }
   __syncthreads();
-  __threadfence();  // acquire side for every wave before it reads Z
 }
 
 template <int DT, int VT, int RT, int A>
@@ -75,8 +86,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const XdLaunch& a = f.xd;
   const ZcLaunch& z = f.zc;
-  int2* cse = reinterpret_cast<int2*>(smem);                   // [ncols] column [start, end)
-  char* big = smem + f.col_bytes;                               // X rows, later all of Z
+  LayerRow* lt = reinterpret_cast<LayerRow*>(smem);            // [kFusedMaxLayers]
+  int2* cse = reinterpret_cast<int2*>(smem + kLayerTableBytes);  // [ncols] column [start, end)
+  char* big = smem + kLayerTableBytes + f.col_bytes;           // X rows, later all of Z
   _Float16* xs = reinterpret_cast<_Float16*>(big);
   float* zs = reinterpret_cast<float*>(big);
 
@@ -92,11 +104,16 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   const int rounds = (ncols + 15) / 16;
   const int ld = (d_in + SEG - 1) / SEG * SEG;
 
-  // ---- 1. column ranges and X rows into LDS
+  // ---- 1. layer table, column ranges and X rows into LDS
+  if (threadIdx.x < kFusedMaxLayers) {
+    const int l = threadIdx.x;
+    lt[l] = LayerRow{z.colptr[l], z.rowidx[l], z.vals[l], z.vscales[l], z.vts[l], z.Y[l], z.nnz[l]};
+  }
+  __syncthreads();
   for (int i = threadIdx.x; i < ncols; i += kThreads) {
     const int c = c0 + i, l = c / d_out, j = c - l * d_out;
-    const int32_t* cp = pick(z.colptr, l);
-    const int64_t nnz = pick(z.nnz, l);
+    const auto* cp = gptr(lt[l].colptr);
+    const int64_t nnz = lt[l].nnz;
     const int s = (int)min<int64_t>(max(cp[j], 0), nnz);
     const int e = (int)min<int64_t>(max(cp[j + 1], s), nnz);
     cse[i] = make_int2(s, e);
@@ -110,11 +127,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
     const int ci = r * 16 + slot;
     if (ci < ncols) {
       const int2 se = cse[ci];
-      const int l = (c0 + ci) / d_out;
-      const uint16_t* rowidx = pick(z.rowidx, l);
-      const void* vals = pick(z.vals, l);
-      const uint8_t* vsc = pick(z.vscales, l);
-      const int64_t nnz = pick(z.nnz, l);
+      const LayerRow& L = lt[(c0 + ci) / d_out];
+      const uint16_t* rowidx = L.rowidx;
+      const void* vals = L.vals;
+      const uint8_t* vsc = L.vsc;
+      const int64_t nnz = L.nnz;
       const int p0 = (se.x & ~7) + g * 8;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -232,10 +249,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
     // columns longer than one batch continue with plain loads
     p0 += 128 * kU;
     if (p0 < e) {
-      const uint16_t* rowidx = pick(z.rowidx, l);
-      const void* vals = pick(z.vals, l);
-      const uint8_t* vsc = pick(z.vscales, l);
-      const int64_t nnz = pick(z.nnz, l);
+      const uint16_t* rowidx = lt[l].rowidx;
+      const void* vals = lt[l].vals;
+      const uint8_t* vsc = lt[l].vsc;
+      const int64_t nnz = lt[l].nnz;
       while (p0 < e) {
         IdxChunk tc[kU];
         ValChunk<VT> tv[kU];
@@ -258,13 +275,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
     sum = row16_sum(sum);
     if (ci < ncols && g == 0) {
       float ts = 1.0f;
-      if constexpr (VT == DFS_NVFP4) ts = *pick(z.vts, l);
+      if constexpr (VT == DFS_NVFP4) ts = *gptr(lt[l].vts);
       const int j = c0 + ci - l * d_out;
-      void* y = pick(z.Y, l);
+      void* y = lt[l].Y;
       if (z.ydt == DFS_F16)
-        ((_Float16*)y)[j] = (_Float16)(sum * ts);
+        gptr_w((_Float16*)y)[j] = (_Float16)(sum * ts);
       else
-        ((float*)y)[j] = sum * ts;
+        gptr_w((float*)y)[j] = sum * ts;
     }
   };
   for (int r = 0; r < rounds; r += 2) {
@@ -311,7 +328,7 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   p->A = A;
   p->RT = RT;
   p->col_bytes = ((size_t)max_cols * 8 + 15) / 16 * 16;
-  p->smem = p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
+  p->smem = kLayerTableBytes + p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
   return p->smem <= 128 * 1024;
 }
 
