@@ -247,8 +247,8 @@ def dict_workspace_size(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC) -> 
 
 
 def workspace(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC, device) -> torch.Tensor:
-    """Forward workspace.  Zeroed: its first 256 bytes are the control block
-    the library requires to be zero before first use (it leaves them zero)."""
+    """Forward workspace.  Zeroed: its first 4096 bytes are the control block
+    the library requires to be zero before first use."""
     return torch.zeros(dict_workspace_size(n_layers, T, D, Cs), dtype=torch.uint8, device=device)
 
 

@@ -128,6 +128,8 @@ constexpr int kGemvMaxRows = 16;
 
 // One-launch decode of a group (T == 1, up to 4 layers).
 constexpr int kFusedMaxLayers = 4;
+constexpr int kCtrlBlockBytes = 4096;   // forward workspace control block
+constexpr int kMaxBarrierGroups = 768;  // arrival flags from byte 1024
 struct FusedLaunch {
   XdLaunch xd;
   ZcLaunch zc;

@@ -16,12 +16,11 @@
 // So the C stream overlaps the D stream and the Z dependency costs one
 // barrier instead of a second launch.
 //
-// Grid barrier: a counter and a generation word in the workspace control
-// block (the counter is zero before first use; the last arriver resets it,
-// so it is zero again after every launch; the generation word only grows).  The grid never exceeds one
-// workgroup per CU, so every workgroup is resident; the wait is bounded
-// anyway: after `spin_limit` polls a workgroup sets the error word and goes
-// on, so the kernel always terminates.
+// Grid barrier: per-workgroup arrival flags, one collector, a generation
+// word (see grid_barrier).  The grid never exceeds one workgroup per CU, so
+// every workgroup is resident; the waits are bounded anyway: after
+// `spin_limit` polls a workgroup sets the error word and goes on, so the
+// kernel always terminates.
 #include "csc_chunks.hpp"
 #include "gemv_common.hpp"
 
@@ -46,40 +45,110 @@ struct LayerRow {
   int64_t nnz;
 };
 
-// Release: every wave waits for its own Z stores to complete (they reach the
-// XCD's L2; L1 is write-through), then one thread per workgroup performs the
-// agent-scope release (write back the L2 for other XCDs) with its arrival.
-// Acquire: the same thread's agent-scope acquire invalidates this CU's L1
-// and the XCD's L2 before any wave reads Z.  One fence pair per workgroup,
-// not per thread: agent-scope fences are cache-wide operations.
+// Grid barrier without a contended counter.  Control block (caller's
+// workspace, zero before first use): generation word at byte 64, error word
+// at byte 128, one arrival flag per workgroup from byte 1024.
+//   arrive   every wave waits for its own Z stores; one thread per workgroup
+//            reads the generation g, performs the agent-scope release (the
+//            XCD's L2 is written back for the other XCDs) and stores g+1 to
+//            its own flag -- a plain store, so arrivals never serialise.
+//   collect  workgroup 0's threads poll all flags in parallel; when every
+//            flag holds g+1 it publishes generation g+1.
+//   wait     one thread per other workgroup polls the generation word, then
+//            the agent-scope acquire invalidates stale Z lines in its caches.
+// Every poll loop is bounded by spin_limit; a workgroup that gives up sets
+// the error word and continues, so the kernel always terminates.
+constexpr int kCtrlGen = 16, kCtrlErr = 32, kCtrlFlags = 256;  // in 32-bit words
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ void grid_barrier(uint32_t* ctrl, uint32_t G, uint32_t spin_limit) {
-  uint32_t* count = ctrl;
-  uint32_t* gen = ctrl + 16;
-  uint32_t* err = ctrl + 32;
+  __shared__ uint32_t g_next;
+  uint32_t* gen = ctrl + kCtrlGen;
+  uint32_t* err = ctrl + kCtrlErr;
+  uint32_t* flags = ctrl + kCtrlFlags;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are done
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t old = __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == G - 1) {
-      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
+    const uint32_t g1 = ld_agent(gen) + 1u;
+    g_next = g1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    st_agent(flags + blockIdx.x, g1);
+  }
+  __syncthreads();
+  const uint32_t g1 = g_next;
+  if (blockIdx.x == 0) {
+    for (uint32_t i = threadIdx.x; i < G; i += blockDim.x) {
       uint32_t it = 0;
-      while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+      while (ld_agent(flags + i) != g1) {
         if (++it > spin_limit) {
-          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          st_agent(err, 1u);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    __atomic_thread_fence(__ATOMIC_ACQUIRE);  // agent-scope acquire (system in HIP => >= agent)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      st_agent(gen, g1);
+    }
+  } else if (threadIdx.x == 0) {
+    uint32_t it = 0;
+    while (ld_agent(gen) != g1) {
+      if (++it > spin_limit) {
+        st_agent(err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
   }
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
 }
 
-template <int DT, int VT, int RT, int A>
+// Launder a kernel-argument pointer through SGPRs so that a lane-dependent
+// choice among a few of them stays a register select (the compiler would
+// otherwise turn the select chain into a vector load from the argument
+// segment, which then waits behind every load already in flight).
+template <typename T>
+__device__ __forceinline__ T* sreg_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
+// sum += Z[idx] * v over the 8 entries of a chunk whose positions p..p+7 lie
+// in [s, e); the other entries are masked without a branch, so the 8 LDS
+// gathers of a chunk are issued back to back.
+template <int VT>
+__device__ __forceinline__ float gather_chunk(const float* zl, const IdxChunk& ic,
+                                              const ValChunk<VT>& vc, int p, int s, int e,
+                                              float sum) {
+  const uint32_t len = (uint32_t)(e - s);
+  const int base = p - s;
+  float z[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool ok = (uint32_t)(base + i) < len;
+    z[i] = zl[ok ? ic.get(i) : 0u];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool ok = (uint32_t)(base + i) < len;
+    const float prod = z[i] * vc.get(i);
+    sum += ok ? prod : 0.0f;
+  }
+  return sum;
+}
+
+template <int DT, int VT, int RT, int A, int NX>
 __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f) {
   using Cf = Cfg<DT, DFS_F16, RT>;
   constexpr int CE = Cf::CE, SEGC = Cf::SEGC, SEG = Cf::SEG;
@@ -92,72 +161,57 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   _Float16* xs = reinterpret_cast<_Float16*>(big);
   float* zs = reinterpret_cast<float*>(big);
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int g = lane & 15;
   const int G = gridDim.x;
   const int d_in = a.d_in, k = a.k, d_out = z.d_out, nl = z.n_layers;
   const int NC = nl * d_out;
   const int c0 = (int)((int64_t)blockIdx.x * NC / G);
   const int c1 = (int)((int64_t)(blockIdx.x + 1) * NC / G);
-  const int ncols = c1 - c0;
+  const int ncols = c1 - c0;  // <= kThreads (checked on the host)
   const int rounds = (ncols + 15) / 16;
   const int ld = (d_in + SEG - 1) / SEG * SEG;
 
-  // ---- 1. layer table, column ranges and X rows into LDS
-  if (threadIdx.x < kFusedMaxLayers) {
-    const int l = threadIdx.x;
-    lt[l] = LayerRow{z.colptr[l], z.rowidx[l], z.vals[l], z.vscales[l], z.vts[l], z.Y[l], z.nnz[l]};
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < ncols; i += kThreads) {
-    const int c = c0 + i, l = c / d_out, j = c - l * d_out;
-    const auto* cp = gptr(lt[l].colptr);
-    const int64_t nnz = lt[l].nnz;
-    const int s = (int)min<int64_t>(max(cp[j], 0), nnz);
-    const int e = (int)min<int64_t>(max(cp[j + 1], s), nnz);
-    cse[i] = make_int2(s, e);
-  }
-  stage_x<DFS_F16, RT, _Float16>(xs, a, 0, 0, ld, ld);
-  __syncthreads();
-
-  // ---- 2. first two rounds of C chunks in flight
-  const int slot = wave * 4 + (lane >> 4);
-  auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
-    const int ci = r * 16 + slot;
-    if (ci < ncols) {
-      const int2 se = cse[ci];
-      const LayerRow& L = lt[(c0 + ci) / d_out];
-      const uint16_t* rowidx = L.rowidx;
-      const void* vals = L.vals;
-      const uint8_t* vsc = L.vsc;
-      const int64_t nnz = L.nnz;
-      const int p0 = (se.x & ~7) + g * 8;
+  // ---- 1a. this thread's column range (raw colptr values, not used yet)
+  int s_raw = 0, e_raw = 0, c_nnz = 0;
+  if (tid < ncols) {
+    const int c = c0 + tid, l = c / d_out, j = c - l * d_out;
+    const int32_t* cp = sreg_ptr(z.colptr[0]);
+    int64_t nz = z.nnz[0];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int p = p0 + 128 * u;
-        if (p < se.y) {
-          ic[u].load(rowidx, p, nnz);
-          vc[u].load(vals, vsc, p, nnz);
-        }
+    for (int i = 1; i < kFusedMaxLayers; ++i)
+      if (l == i) {
+        cp = sreg_ptr(z.colptr[i]);
+        nz = z.nnz[i];
       }
+    s_raw = gptr(cp)[j];
+    e_raw = gptr(cp)[j + 1];
+    c_nnz = (int)nz;
+  }
+  // ---- 1b. X rows (all of d_in, zero padded to ld), kept in registers
+  const int x_items = RT * ld / 8, x_per_row = ld / 8;
+  u4 xr[NX];
+#pragma unroll
+  for (int jx = 0; jx < NX; ++jx) {
+    const int item = jx * kThreads + tid;
+    const int r = item / x_per_row;
+    const int ge = (item - r * x_per_row) * 8;
+    xr[jx] = u4{0u, 0u, 0u, 0u};
+    if (item < x_items && r < nl && ge < d_in) {
+      const _Float16* xrow = (const _Float16*)a.X[0];
+#pragma unroll
+      for (int i = 1; i < RT; ++i)
+        if (r == i) xrow = (const _Float16*)sreg_ptr(a.X[i]);
+      xr[jx] = ld16<u4>(xrow + ge);  // d_in % 8 == 0 on this path
     }
-  };
-  IdxChunk ia[kU], ib[kU];
-  ValChunk<VT> va[kU], vb[kU];
-  load_round(ia, va, 0);
-  load_round(ib, vb, 1);
-
-  // ---- 3. Z for this workgroup's atoms
+  }
+  // ---- 1c. this workgroup's atoms: every D load of the first segment
   const int atom0 = (blockIdx.x * kWaves + wave) * A;
-  float acc[A][RT];
-#pragma unroll
-  for (int i = 0; i < A; ++i)
-#pragma unroll
-    for (int r = 0; r < RT; ++r) acc[i][r] = 0.0f;
-  for (int seg = 0; seg < d_in; seg += SEG) {
-    u4 dreg[A][SEGC];
-    uint32_t sreg[A][SEGC];
+  u4 dreg[A][SEGC];
+  uint32_t sreg[A][SEGC];
+  auto load_d = [&](int seg) {
 #pragma unroll
     for (int i = 0; i < A; ++i) {
       const int atom = atom0 + i;
@@ -170,13 +224,68 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
           if constexpr (DT == DFS_NVFP4) {
             const int64_t el = (int64_t)atom * d_in + e0;
             dreg[i][c] = ld16<u4>(a.dcodes + el / 2);
-            sreg[i][c] = (uint32_t)a.dscales[el / 16] | ((uint32_t)a.dscales[el / 16 + 1] << 8);
+            sreg[i][c] = (uint32_t)gptr(a.dscales)[el / 16] |
+                         ((uint32_t)gptr(a.dscales)[el / 16 + 1] << 8);
           } else {
             dreg[i][c] = ld16<u4>((const _Float16*)a.D + (int64_t)atom * a.ldd + e0);
           }
         }
       }
     }
+  };
+  load_d(0);
+
+  // ---- 1d. commit the column ranges, the layer table and X to LDS (waits
+  // only for the older colptr and X loads; the D stream stays in flight)
+  if (tid < kFusedMaxLayers) {
+    const int l = tid;
+    lt[l] = LayerRow{z.colptr[l], z.rowidx[l], z.vals[l], z.vscales[l], z.vts[l], z.Y[l], z.nnz[l]};
+  }
+  if (tid < ncols) {
+    const int s0 = min(max(s_raw, 0), c_nnz);
+    cse[tid] = make_int2(s0, min(max(e_raw, s0), c_nnz));
+  }
+#pragma unroll
+  for (int jx = 0; jx < NX; ++jx) {
+    const int item = jx * kThreads + tid;
+    if (item < x_items) {
+      const int r = item / x_per_row;
+      *reinterpret_cast<u4*>(xs + r * ld + (item - r * x_per_row) * 8) = xr[jx];
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. first two rounds of C chunks in flight
+  const int slot = wave * 4 + (lane >> 4);
+  auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
+    const int ci = r * 16 + slot;
+    if (ci < ncols) {
+      const int2 se = cse[ci];
+      const LayerRow& L = lt[(c0 + ci) / d_out];
+      const int p0 = (se.x & ~7) + g * 8;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int p = p0 + 128 * u;
+        if (p < se.y) {
+          ic[u].load(L.rowidx, p, L.nnz);
+          vc[u].load(L.vals, L.vsc, p, L.nnz);
+        }
+      }
+    }
+  };
+  IdxChunk ia[kU], ib[kU];
+  ValChunk<VT> va[kU], vb[kU];
+  load_round(ia, va, 0);
+  load_round(ib, vb, 1);
+
+  // ---- 3. Z for this workgroup's atoms
+  float acc[A][RT];
+#pragma unroll
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[i][r] = 0.0f;
+  for (int seg = 0; seg < d_in; seg += SEG) {
+    if (seg > 0) load_d(seg);
     const _Float16* xseg = xs + seg;
 #pragma unroll
     for (int c = 0; c < SEGC; ++c) {
@@ -190,14 +299,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
     }
   }
   float dts = 1.0f;
-  if constexpr (DT == DFS_NVFP4) dts = *a.dts;
+  if constexpr (DT == DFS_NVFP4) dts = *gptr(a.dts);
 #pragma unroll
   for (int i = 0; i < A; ++i) {
     const int atom = atom0 + i;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const float v = wave_sum(acc[i][r]) * dts;
-      if (lane == r && atom < k && r < nl) f.zws[(int64_t)r * k + atom] = v;
+      if (lane == r && atom < k && r < nl) gptr_w(f.zws)[(int64_t)r * k + atom] = v;
     }
   }
 
@@ -212,12 +321,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
       u4 v[kUnr];
 #pragma unroll
       for (int j = 0; j < kUnr; ++j) {
-        const int i4 = base + j * kThreads + threadIdx.x;
+        const int i4 = base + j * kThreads + tid;
         if (i4 < n4) v[j] = ld16<u4>(f.zws + 4 * i4);
       }
 #pragma unroll
       for (int j = 0; j < kUnr; ++j) {
-        const int i4 = base + j * kThreads + threadIdx.x;
+        const int i4 = base + j * kThreads + tid;
         if (i4 < n4) *reinterpret_cast<u4*>(zs + 4 * i4) = v[j];
       }
     }
@@ -238,37 +347,23 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
     float sum = 0.0f;
     int p0 = (s & ~7) + g * 8;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int p = p0 + 128 * u;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = p + i;
-        if (q >= s && q < e) sum = __builtin_fmaf(zl[ic[u].get(i)], vc[u].get(i), sum);
-      }
-    }
+    for (int u = 0; u < kU; ++u) sum = gather_chunk<VT>(zl, ic[u], vc[u], p0 + 128 * u, s, e, sum);
     // columns longer than one batch continue with plain loads
     p0 += 128 * kU;
     if (p0 < e) {
-      const uint16_t* rowidx = lt[l].rowidx;
-      const void* vals = lt[l].vals;
-      const uint8_t* vsc = lt[l].vsc;
-      const int64_t nnz = lt[l].nnz;
+      const LayerRow& L = lt[l];
       while (p0 < e) {
         IdxChunk tc[kU];
         ValChunk<VT> tv[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u)
           if (p0 + 128 * u < e) {
-            tc[u].load(rowidx, p0 + 128 * u, nnz);
-            tv[u].load(vals, vsc, p0 + 128 * u, nnz);
+            tc[u].load(L.rowidx, p0 + 128 * u, L.nnz);
+            tv[u].load(L.vals, L.vsc, p0 + 128 * u, L.nnz);
           }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int q = p0 + 128 * u + i;
-            if (q < e) sum = __builtin_fmaf(zl[tc[u].get(i)], tv[u].get(i), sum);
-          }
+          sum = gather_chunk<VT>(zl, tc[u], tv[u], p0 + 128 * u, s, e, sum);
         p0 += 128 * kU;
       }
     }
@@ -308,33 +403,39 @@ int device_cus() {
 }
 
 struct Plan {
-  int G, A, RT;
+  int G, A, RT, NX;  // NX = 2 * RT (d_in <= 4096) or 4 * RT (d_in <= 8192)
   size_t col_bytes, smem;
 };
 
 bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   const int G = device_cus();
-  if (G <= 0) return false;
+  if (G <= 0 || G > kMaxBarrierGroups) return false;
   const int nl = zc.n_layers;
-  const int A = (xd.k + 4 * G - 1) / (4 * G);
-  if (A < 1 || A > 4) return false;
+  int A = (xd.k + 4 * G - 1) / (4 * G);
+  if (A > 3) return false;
+  A = A < 2 ? 2 : A;
   const int RT = nl <= 1 ? 1 : (nl <= 2 ? 2 : 4);
   const int seg = xd.ddt == DFS_NVFP4 ? kWave * 2 * 32 : kWave * 8 * 8;  // Cfg<.., F16, RT<=4>::SEG
   const size_t ld = (size_t)(xd.d_in + seg - 1) / seg * seg;
   const size_t xbytes = (size_t)RT * ld * 2;
   const size_t zbytes = (size_t)nl * xd.k * 4;
   const int max_cols = (nl * zc.d_out + G - 1) / G + 1;
+  if (max_cols > kThreads) return false;  // one column range per thread
+  const int x_items = (int)((size_t)RT * ld / 8);
+  const int NX = (x_items + kThreads - 1) / kThreads;
+  if (NX > 8 || (NX != 2 * RT && NX != 4 * RT)) return false;  // X held in registers
   p->G = G;
   p->A = A;
   p->RT = RT;
+  p->NX = NX;
   p->col_bytes = ((size_t)max_cols * 8 + 15) / 16 * 16;
   p->smem = kLayerTableBytes + p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
   return p->smem <= 128 * 1024;
 }
 
-template <int DT, int VT, int RT, int A>
-hipError_t launch4(FusedLaunch f, const Plan& p, hipStream_t s) {
-  auto kern = fused_decode_kernel<DT, VT, RT, A>;
+template <int DT, int VT, int RT, int A, int NX>
+hipError_t launch5(FusedLaunch f, const Plan& p, hipStream_t s) {
+  auto kern = fused_decode_kernel<DT, VT, RT, A, NX>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.smem);
   if (err != hipSuccess) return err;
@@ -347,14 +448,17 @@ hipError_t launch4(FusedLaunch f, const Plan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DT, int VT, int RT, int A>
+hipError_t launch4(FusedLaunch f, const Plan& p, hipStream_t s) {
+  if constexpr (RT <= 2) {
+    if (p.NX == 4 * RT) return launch5<DT, VT, RT, A, 4 * RT>(f, p, s);
+  }
+  return launch5<DT, VT, RT, A, 2 * RT>(f, p, s);
+}
+
 template <int DT, int VT, int RT>
 hipError_t launch3(FusedLaunch f, const Plan& p, hipStream_t s) {
-  switch (p.A) {
-    case 1: return launch4<DT, VT, RT, 1>(f, p, s);
-    case 2: return launch4<DT, VT, RT, 2>(f, p, s);
-    case 3: return launch4<DT, VT, RT, 3>(f, p, s);
-    default: return launch4<DT, VT, RT, 4>(f, p, s);
-  }
+  return p.A == 2 ? launch4<DT, VT, RT, 2>(f, p, s) : launch4<DT, VT, RT, 3>(f, p, s);
 }
 
 template <int DT, int VT>

@@ -92,21 +92,21 @@ __global__ __launch_bounds__(kThreads) void spmm_csc_kernel(ZcLaunch a) {
           vc[u].load(vals, vsc, p + 8 * u, nnz);
         }
     };
+    const uint32_t len = (uint32_t)(e - s);
     auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int p) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
+        // entries outside [s, e) are masked without a branch (atom 0, zero
+        // product) so that the LDS gathers of a chunk issue back to back
+        const int base = p + 8 * u - s;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int q = p + 8 * u + i;
-          if (q >= s && q < e) {
-            const int r = (int)ic[u].get(i);
-            const float v = vc[u].get(i);
-            const h4 z = *reinterpret_cast<const h4*>(zraw + zoff<TT>(r, sub));
-            acc[0] = __builtin_fmaf((float)z[0], v, acc[0]);
-            acc[1] = __builtin_fmaf((float)z[1], v, acc[1]);
-            acc[2] = __builtin_fmaf((float)z[2], v, acc[2]);
-            acc[3] = __builtin_fmaf((float)z[3], v, acc[3]);
-          }
+          const bool ok = (uint32_t)(base + i) < len;
+          const int r = ok ? (int)ic[u].get(i) : 0;
+          const float v = vc[u].get(i);
+          const h4 z = *reinterpret_cast<const h4*>(zraw + zoff<TT>(r, sub));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[t] += ok ? (float)z[t] * v : 0.0f;
         }
       }
     };

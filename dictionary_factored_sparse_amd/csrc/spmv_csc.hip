@@ -134,29 +134,28 @@ __global__ __launch_bounds__(kThreads) void spmv_csc_kernel(ZcLaunch a) {
     float acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+    const uint32_t len = (uint32_t)(e - s);
     while (p0 < e) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int p = p0 + 128 * u;
+        const int base = p0 + 128 * u - s;
+        // entries outside [s, e) are masked without a branch (index 0, zero
+        // product), so the LDS gathers of a chunk issue back to back
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int q = p + i;
-          if (q >= s && q < e) {
-            const float v = vc[u].get(i);
-            const float* zr = zs + ic[u].get(i) * TT;
-            if constexpr (TT % 4 == 0) {
+          const bool ok = (uint32_t)(base + i) < len;
+          const float v = ok ? vc[u].get(i) : 0.0f;
+          const float* zr = zs + (ok ? ic[u].get(i) : 0u) * TT;
+          if constexpr (TT % 4 == 0) {
 #pragma unroll
-              for (int t = 0; t < TT; t += 4) {
-                const f4 z4 = *reinterpret_cast<const f4*>(zr + t);
-                acc[t] = __builtin_fmaf(z4[0], v, acc[t]);
-                acc[t + 1] = __builtin_fmaf(z4[1], v, acc[t + 1]);
-                acc[t + 2] = __builtin_fmaf(z4[2], v, acc[t + 2]);
-                acc[t + 3] = __builtin_fmaf(z4[3], v, acc[t + 3]);
-              }
-            } else {
+            for (int t = 0; t < TT; t += 4) {
+              const f4 z4 = *reinterpret_cast<const f4*>(zr + t);
 #pragma unroll
-              for (int t = 0; t < TT; ++t) acc[t] = __builtin_fmaf(zr[t], v, acc[t]);
+              for (int q = 0; q < 4; ++q) acc[t + q] += ok ? z4[q] * v : 0.0f;
             }
+          } else {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[t] += ok ? zr[t] * v : 0.0f;
           }
         }
       }

@@ -153,15 +153,14 @@ dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream);
  * (dict_proj_forward: n_layers = 1).  D and C describe the shapes and dtypes
  * (C may point at any one layer's descriptor; only k/d_out/dtype are read).
  *
- * Forward workspace contract: its first 256 bytes are a control block that
+ * Forward workspace contract: its first 4096 bytes are a control block that
  * must be ZERO before the first forward call that uses the workspace (e.g.
- * hipMemset once after allocation).  Every call leaves the barrier counter
- * (the 32-bit word at byte 0) at zero again; the generation word (byte 64)
- * keeps counting and may hold any value.  Calls sharing one workspace must
- * not run concurrently.  After a call, the 32-bit word at byte offset 128 is
- * non-zero only if the one-launch decode path (T = 1, <= 4 layers) gave up
- * waiting at its grid barrier, in which case that call's outputs are
- * invalid. */
+ * hipMemset once after allocation); later calls keep it consistent (it holds
+ * a generation counter and per-workgroup arrival flags of the one-launch
+ * decode's grid barrier).  Calls sharing one workspace must not run
+ * concurrently.  After a call, the 32-bit word at byte offset 128 is non-zero
+ * only if the one-launch decode path (T = 1, <= 4 layers) gave up waiting at
+ * its grid barrier, in which case that call's outputs are invalid. */
 dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, const dfs_csc* C,
                                size_t* bytes);
 

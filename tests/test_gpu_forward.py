@@ -256,7 +256,6 @@ def _both_paths(g, nvfp4=False):
         finally:
             os.environ.pop("DFS_DECODE_PATH", None)
         assert B.workspace_error_word(ws) == 0
-        assert int(ws[0:4].view(torch.int32).item()) == 0, "barrier counter not reset"
     return out
 
 
