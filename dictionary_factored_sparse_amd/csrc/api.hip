@@ -325,7 +325,8 @@ dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, c
   DFS_TRY(check_dict(D));
   if (!C || C->k != D->k || C->d_out <= 0) return DFS_E_INVALID;
   const int64_t rows = (int64_t)n_layers * T;
-  *bytes = kCtrlBytes + round256((size_t)rows * D->k * 4) + xd_ws_bytes(rows, DFS_F16, D);
+  const size_t per = rows <= kGemvMaxRows ? 8 : 4;  // decode: (epoch, value) words
+  *bytes = kCtrlBytes + round256((size_t)rows * D->k * per) + xd_ws_bytes(rows, DFS_F16, D);
   return DFS_OK;
 }
 
@@ -384,7 +385,8 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
   const int64_t rows = (int64_t)n_layers * T;
   const bool mfma = mfma_path(rows, xdt, D);
   const int32_t zdt = mfma ? DFS_F16 : DFS_F32;
-  const size_t zbytes = round256((size_t)rows * D->k * esize(zdt));
+  // the one-launch decode hands Z over as 8-byte (epoch, value) words
+  const size_t zbytes = round256((size_t)rows * D->k * (mfma ? 2 : 8));
   const size_t need = kCtrlBytes + zbytes + xd_ws_bytes(rows, xdt, D);
   if (!ws || ws_bytes < need) return DFS_E_WORKSPACE;
   if (!aligned16(ws)) return DFS_E_ALIGN;

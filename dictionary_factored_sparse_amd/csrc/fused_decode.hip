@@ -6,21 +6,18 @@
 // group) and each C_l.  Run as two kernels, C_l's stream cannot start until
 // the Z kernel ends.  Here one persistent grid (one workgroup per CU) does
 // both:
-//   1. each workgroup stages X and the [start, end) of its output columns;
+//   1. each workgroup puts its slice of D_g's atoms in flight, then commits
+//      X and the [start, end) of its output columns to LDS;
 //   2. it issues the loads of its first two rounds of C chunks (they do not
-//      depend on Z) and of its slice of D_g's atoms;
-//   3. it computes its atoms' Z, writes them to the workspace and arrives at
-//      a grid barrier;
-//   4. after the barrier it stages all of Z into LDS and finishes its
-//      columns, later rounds of C double-buffered in registers.
+//      depend on Z);
+//   3. it computes its atoms' Z and publishes them as epoch-tagged words;
+//   4. it receives the Z rows of its layers (polling for the current epoch)
+//      into LDS and finishes its columns, later rounds of C double-buffered
+//      in registers.
 // So the C stream overlaps the D stream and the Z dependency costs one
-// barrier instead of a second launch.
-//
-// Grid barrier: per-workgroup arrival flags, one collector, a generation
-// word (see grid_barrier).  The grid never exceeds one workgroup per CU, so
-// every workgroup is resident; the waits are bounded anyway: after
-// `spin_limit` polls a workgroup sets the error word and goes on, so the
-// kernel always terminates.
+// round trip through memory instead of a second launch.  The grid never
+// exceeds one workgroup per CU, so every workgroup is resident; every wait
+// is bounded anyway (see receive_z), so the kernel always terminates.
 #include "csc_chunks.hpp"
 #include "gemv_common.hpp"
 
@@ -45,20 +42,18 @@ struct LayerRow {
   int64_t nnz;
 };
 
-// Grid barrier without a contended counter.  Control block (caller's
-// workspace, zero before first use): generation word at byte 64, error word
-// at byte 128, one arrival flag per workgroup from byte 1024.
-//   arrive   every wave waits for its own Z stores; one thread per workgroup
-//            reads the generation g, performs the agent-scope release (the
-//            XCD's L2 is written back for the other XCDs) and stores g+1 to
-//            its own flag -- a plain store, so arrivals never serialise.
-//   collect  workgroup 0's threads poll all flags in parallel; when every
-//            flag holds g+1 it publishes generation g+1.
-//   wait     one thread per other workgroup polls the generation word, then
-//            the agent-scope acquire invalidates stale Z lines in its caches.
-// Every poll loop is bounded by spin_limit; a workgroup that gives up sets
-// the error word and continues, so the kernel always terminates.
-constexpr int kCtrlGen = 16, kCtrlErr = 32, kCtrlFlags = 256;  // in 32-bit words
+// Hand-off of Z between workgroups without a grid barrier.  Each Z entry is
+// one 64-bit word (epoch << 32 | fp32 bits) written with a single agent-scope
+// atomic store, so a reader that sees the current epoch also sees the value;
+// readers poll exactly the entries they need with agent-scope loads (these
+// bypass the non-coherent caches), so no cache-wide fence is needed.
+// Control block (caller's workspace, zero before first use): error word at
+// byte 128; from byte 1024 one epoch word per workgroup.  Workgroup w reads
+// its word, uses epoch + 1 and stores it back; every launch advances every
+// word once, so all workgroups of a launch agree on the epoch.  Polls are
+// bounded by spin_limit: a workgroup that gives up sets the error word and
+// continues, so the kernel always terminates.
+constexpr int kCtrlErr = 32, kCtrlEpochs = 256;  // in 32-bit words
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -66,26 +61,36 @@ __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
 __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t ld_agent64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-__device__ void grid_barrier(uint32_t* ctrl, uint32_t G, uint32_t spin_limit) {
-  __shared__ uint32_t g_next;
-  uint32_t* gen = ctrl + kCtrlGen;
-  uint32_t* err = ctrl + kCtrlErr;
-  uint32_t* flags = ctrl + kCtrlFlags;
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are done
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t g1 = ld_agent(gen) + 1u;
-    g_next = g1;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    st_agent(flags + blockIdx.x, g1);
-  }
-  __syncthreads();
-  const uint32_t g1 = g_next;
-  if (blockIdx.x == 0) {
-    for (uint32_t i = threadIdx.x; i < G; i += blockDim.x) {
-      uint32_t it = 0;
-      while (ld_agent(flags + i) != g1) {
+// Copy the n tagged Z entries from zz into LDS zs as fp32 once each carries
+// `epoch`; 16 entries per thread are polled at a time.
+__device__ void receive_z(float* zs, const uint64_t* zz, int n, uint32_t epoch, uint32_t* err,
+                          uint32_t spin_limit) {
+  constexpr int kPer = 16;
+  for (int base = 0; base < n; base += kThreads * kPer) {
+    uint32_t pending = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (base + j * kThreads + (int)threadIdx.x < n) pending |= 1u << j;
+    uint32_t it = 0;
+    while (pending) {
+      uint64_t w[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (pending & (1u << j)) w[j] = ld_agent64(zz + base + j * kThreads + threadIdx.x);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if ((pending & (1u << j)) && (uint32_t)(w[j] >> 32) == epoch) {
+          zs[base + j * kThreads + threadIdx.x] = __uint_as_float((uint32_t)w[j]);
+          pending &= ~(1u << j);
+        }
+      if (pending) {
         if (++it > spin_limit) {
           st_agent(err, 1u);
           break;
@@ -93,23 +98,7 @@ __device__ void grid_barrier(uint32_t* ctrl, uint32_t G, uint32_t spin_limit) {
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
-      st_agent(gen, g1);
-    }
-  } else if (threadIdx.x == 0) {
-    uint32_t it = 0;
-    while (ld_agent(gen) != g1) {
-      if (++it > spin_limit) {
-        st_agent(err, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
   }
-  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  __syncthreads();
 }
 
 // Launder a kernel-argument pointer through SGPRs so that a lane-dependent
@@ -173,6 +162,15 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   const int ncols = c1 - c0;  // <= kThreads (checked on the host)
   const int rounds = (ncols + 15) / 16;
   const int ld = (d_in + SEG - 1) / SEG * SEG;
+
+  // ---- 0. this launch's epoch (see receive_z)
+  __shared__ uint32_t epoch_s;
+  if (tid == 0) {
+    uint32_t* ew = f.ctrl + kCtrlEpochs + blockIdx.x;
+    const uint32_t e = ld_agent(ew) + 1u;
+    st_agent(ew, e);
+    epoch_s = e;
+  }
 
   // ---- 1a. this thread's column range (raw colptr values, not used yet)
   int s_raw = 0, e_raw = 0, c_nnz = 0;
@@ -279,6 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   load_round(ib, vb, 1);
 
   // ---- 3. Z for this workgroup's atoms
+  const uint32_t epoch = epoch_s;  // written before the LDS commit barrier
   float acc[A][RT];
 #pragma unroll
   for (int i = 0; i < A; ++i)
@@ -300,40 +299,27 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   }
   float dts = 1.0f;
   if constexpr (DT == DFS_NVFP4) dts = *gptr(a.dts);
+  uint64_t* zz = reinterpret_cast<uint64_t*>(f.zws);
 #pragma unroll
   for (int i = 0; i < A; ++i) {
     const int atom = atom0 + i;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const float v = wave_sum(acc[i][r]) * dts;
-      if (lane == r && atom < k && r < nl) gptr_w(f.zws)[(int64_t)r * k + atom] = v;
+      if (lane == r && atom < k && r < nl)
+        st_agent64(zz + (int64_t)r * k + atom, ((uint64_t)epoch << 32) | __float_as_uint(v));
     }
   }
 
-  // ---- 4. every workgroup's Z is written
-  grid_barrier(f.ctrl, (uint32_t)G, f.spin_limit);
-
-  // ---- 5. all of Z (nl x k fp32) into LDS
+  // ---- 4. receive the Z rows of this workgroup's layers into LDS
   {
-    const int n4 = nl * k / 4;  // k % 4 == 0 on this path
-    constexpr int kUnr = 4;
-    for (int base = 0; base < n4; base += kThreads * kUnr) {
-      u4 v[kUnr];
-#pragma unroll
-      for (int j = 0; j < kUnr; ++j) {
-        const int i4 = base + j * kThreads + tid;
-        if (i4 < n4) v[j] = ld16<u4>(f.zws + 4 * i4);
-      }
-#pragma unroll
-      for (int j = 0; j < kUnr; ++j) {
-        const int i4 = base + j * kThreads + tid;
-        if (i4 < n4) *reinterpret_cast<u4*>(zs + 4 * i4) = v[j];
-      }
-    }
+    const int l_first = c0 / d_out, l_last = (c1 - 1) / d_out;
+    receive_z(zs + l_first * k, zz + (int64_t)l_first * k, (l_last - l_first + 1) * k, epoch,
+              f.ctrl + kCtrlErr, f.spin_limit);
   }
   __syncthreads();
 
-  // ---- 6. the columns, two rounds in flight
+  // ---- 5. the columns, two rounds in flight
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int r) {
     const int ci = r * 16 + slot;
     int s = 0, e = 0, l = 0;
