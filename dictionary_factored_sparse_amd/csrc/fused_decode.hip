@@ -28,6 +28,9 @@ using namespace gemv;
 
 constexpr int kU = 6;  // 8-entry C chunks per lane per batch
 constexpr int kLayerTableBytes = 256;
+constexpr int kFT = 512;          // threads per workgroup (2 waves per SIMD)
+constexpr int kFW = kFT / kWave;  // waves per workgroup
+constexpr int kSlots = kFW * 4;   // columns per round (4 per wave)
 
 // Per-layer pointers live in a small LDS table: looking one up for a
 // lane-dependent layer is an LDS read (LGKM counter), not a vector load
@@ -73,21 +76,21 @@ __device__ __forceinline__ void st_agent64(uint64_t* p, uint64_t v) {
 __device__ void receive_z(float* zs, const uint64_t* zz, int n, uint32_t epoch, uint32_t* err,
                           uint32_t spin_limit) {
   constexpr int kPer = 16;
-  for (int base = 0; base < n; base += kThreads * kPer) {
+  for (int base = 0; base < n; base += kFT * kPer) {
     uint32_t pending = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      if (base + j * kThreads + (int)threadIdx.x < n) pending |= 1u << j;
+      if (base + j * kFT + (int)threadIdx.x < n) pending |= 1u << j;
     uint32_t it = 0;
     while (pending) {
       uint64_t w[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (pending & (1u << j)) w[j] = ld_agent64(zz + base + j * kThreads + threadIdx.x);
+        if (pending & (1u << j)) w[j] = ld_agent64(zz + base + j * kFT + threadIdx.x);
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
         if ((pending & (1u << j)) && (uint32_t)(w[j] >> 32) == epoch) {
-          zs[base + j * kThreads + threadIdx.x] = __uint_as_float((uint32_t)w[j]);
+          zs[base + j * kFT + threadIdx.x] = __uint_as_float((uint32_t)w[j]);
           pending &= ~(1u << j);
         }
       if (pending) {
@@ -138,7 +141,7 @@ __device__ __forceinline__ float gather_chunk(const float* zl, const IdxChunk& i
 }
 
 template <int DT, int VT, int RT, int A, int NX>
-__global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f) {
+__global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
   using Cf = Cfg<DT, DFS_F16, RT>;
   constexpr int CE = Cf::CE, SEGC = Cf::SEGC, SEG = Cf::SEG;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -159,46 +162,44 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   const int NC = nl * d_out;
   const int c0 = (int)((int64_t)blockIdx.x * NC / G);
   const int c1 = (int)((int64_t)(blockIdx.x + 1) * NC / G);
-  const int ncols = c1 - c0;  // <= kThreads (checked on the host)
-  const int rounds = (ncols + 15) / 16;
+  const int ncols = c1 - c0;  // <= kFT (checked on the host)
+  const int rounds = (ncols + kSlots - 1) / kSlots;
   const int ld = (d_in + SEG - 1) / SEG * SEG;
 
-  // ---- 0. this launch's epoch (see receive_z)
-  __shared__ uint32_t epoch_s;
+  // Loads are issued oldest-first in the order they are needed: vector loads
+  // retire in order, so waiting for an early load must not have to wait for
+  // the weight stream queued behind it.
+  // ---- 0. layer table from the kernel arguments (scalar loads, LGKM counter)
   if (tid == 0) {
-    uint32_t* ew = f.ctrl + kCtrlEpochs + blockIdx.x;
-    const uint32_t e = ld_agent(ew) + 1u;
-    st_agent(ew, e);
-    epoch_s = e;
-  }
-
-  // ---- 1a. this thread's column range (raw colptr values, not used yet)
-  int s_raw = 0, e_raw = 0, c_nnz = 0;
-  if (tid < ncols) {
-    const int c = c0 + tid, l = c / d_out, j = c - l * d_out;
-    const int32_t* cp = sreg_ptr(z.colptr[0]);
-    int64_t nz = z.nnz[0];
 #pragma unroll
-    for (int i = 1; i < kFusedMaxLayers; ++i)
-      if (l == i) {
-        cp = sreg_ptr(z.colptr[i]);
-        nz = z.nnz[i];
-      }
-    s_raw = gptr(cp)[j];
-    e_raw = gptr(cp)[j + 1];
-    c_nnz = (int)nz;
+    for (int l = 0; l < kFusedMaxLayers; ++l)
+      lt[l] = LayerRow{z.colptr[l], z.rowidx[l], z.vals[l], z.vscales[l], z.vts[l], z.Y[l], z.nnz[l]};
   }
-  // ---- 1b. X rows (all of d_in, zero padded to ld), kept in registers
+  // this launch's epoch word (consumed only when Z is published)
+  const uint32_t epoch_old = ld_agent(f.ctrl + kCtrlEpochs + blockIdx.x);
+  // ---- 1a. this thread's column range (raw colptr values, used at commit)
+  const int cidx = tid < ncols ? tid : 0;
+  const int cl = (c0 + cidx) / d_out, cj = c0 + cidx - cl * d_out;
+  const int32_t* cp = sreg_ptr(z.colptr[0]);
+  int64_t cnz = z.nnz[0];
+#pragma unroll
+  for (int i = 1; i < kFusedMaxLayers; ++i)
+    if (cl == i) {
+      cp = sreg_ptr(z.colptr[i]);
+      cnz = z.nnz[i];
+    }
+  const int s_raw = gptr(cp)[cj], e_raw = gptr(cp)[cj + 1];
+  // ---- 1b. X rows (all of d_in, zero padded to ld), held in registers
   const int x_items = RT * ld / 8, x_per_row = ld / 8;
   u4 xr[NX];
 #pragma unroll
   for (int jx = 0; jx < NX; ++jx) {
-    const int item = jx * kThreads + tid;
+    const int item = jx * kFT + tid;
     const int r = item / x_per_row;
     const int ge = (item - r * x_per_row) * 8;
     xr[jx] = u4{0u, 0u, 0u, 0u};
     if (item < x_items && r < nl && ge < d_in) {
-      const _Float16* xrow = (const _Float16*)a.X[0];
+      const _Float16* xrow = (const _Float16*)sreg_ptr(a.X[0]);
 #pragma unroll
       for (int i = 1; i < RT; ++i)
         if (r == i) xrow = (const _Float16*)sreg_ptr(a.X[i]);
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
     }
   }
   // ---- 1c. this workgroup's atoms: every D load of the first segment
-  const int atom0 = (blockIdx.x * kWaves + wave) * A;
+  const int atom0 = (blockIdx.x * kFW + wave) * A;
   u4 dreg[A][SEGC];
   uint32_t sreg[A][SEGC];
   auto load_d = [&](int seg) {
@@ -233,19 +234,16 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   };
   load_d(0);
 
-  // ---- 1d. commit the column ranges, the layer table and X to LDS (waits
-  // only for the older colptr and X loads; the D stream stays in flight)
-  if (tid < kFusedMaxLayers) {
-    const int l = tid;
-    lt[l] = LayerRow{z.colptr[l], z.rowidx[l], z.vals[l], z.vscales[l], z.vts[l], z.Y[l], z.nnz[l]};
-  }
+  // ---- 1d. commit the column ranges and X to LDS (waits only for the older
+  // colptr and X loads; the D stream stays in flight)
   if (tid < ncols) {
-    const int s0 = min(max(s_raw, 0), c_nnz);
-    cse[tid] = make_int2(s0, min(max(e_raw, s0), c_nnz));
+    const int nz = (int)cnz;
+    const int s0 = min(max(s_raw, 0), nz);
+    cse[tid] = make_int2(s0, min(max(e_raw, s0), nz));
   }
 #pragma unroll
   for (int jx = 0; jx < NX; ++jx) {
-    const int item = jx * kThreads + tid;
+    const int item = jx * kFT + tid;
     if (item < x_items) {
       const int r = item / x_per_row;
       *reinterpret_cast<u4*>(xs + r * ld + (item - r * x_per_row) * 8) = xr[jx];
@@ -256,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   // ---- 2. first two rounds of C chunks in flight
   const int slot = wave * 4 + (lane >> 4);
   auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
-    const int ci = r * 16 + slot;
+    const int ci = r * kSlots + slot;
     if (ci < ncols) {
       const int2 se = cse[ci];
       const LayerRow& L = lt[(c0 + ci) / d_out];
@@ -276,8 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   load_round(ia, va, 0);
   load_round(ib, vb, 1);
 
-  // ---- 3. Z for this workgroup's atoms
-  const uint32_t epoch = epoch_s;  // written before the LDS commit barrier
+  // ---- 3. Z for this workgroup's atoms, published as epoch-tagged words
   float acc[A][RT];
 #pragma unroll
   for (int i = 0; i < A; ++i)
@@ -299,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
   }
   float dts = 1.0f;
   if constexpr (DT == DFS_NVFP4) dts = *gptr(a.dts);
+  const uint32_t epoch = epoch_old + 1u;
   uint64_t* zz = reinterpret_cast<uint64_t*>(f.zws);
 #pragma unroll
   for (int i = 0; i < A; ++i) {
@@ -318,10 +316,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_decode_kernel(FusedLaunch f
               f.ctrl + kCtrlErr, f.spin_limit);
   }
   __syncthreads();
+  // every wave has published and received: advance this workgroup's epoch
+  if (tid == 0) st_agent(f.ctrl + kCtrlEpochs + blockIdx.x, epoch);
 
   // ---- 5. the columns, two rounds in flight
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int r) {
-    const int ci = r * 16 + slot;
+    const int ci = r * kSlots + slot;
     int s = 0, e = 0, l = 0;
     if (ci < ncols) {
       const int2 se = cse[ci];
@@ -389,7 +389,7 @@ int device_cus() {
 }
 
 struct Plan {
-  int G, A, RT, NX;  // NX = 2 * RT (d_in <= 4096) or 4 * RT (d_in <= 8192)
+  int G, A, RT, NX;  // NX = RT (d_in <= 4096) or 2 * RT (d_in <= 8192)
   size_t col_bytes, smem;
 };
 
@@ -397,19 +397,21 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   const int G = device_cus();
   if (G <= 0 || G > kMaxBarrierGroups) return false;
   const int nl = zc.n_layers;
-  int A = (xd.k + 4 * G - 1) / (4 * G);
-  if (A > 3) return false;
-  A = A < 2 ? 2 : A;
+  int A = (xd.k + kFW * G - 1) / (kFW * G);  // atoms per wave
+  if (A > 2) return false;
+  A = A < 1 ? 1 : A;
   const int RT = nl <= 1 ? 1 : (nl <= 2 ? 2 : 4);
+  if (xd.ddt == DFS_NVFP4 && RT == 4 && A == 2) return false;  // would spill registers
   const int seg = xd.ddt == DFS_NVFP4 ? kWave * 2 * 32 : kWave * 8 * 8;  // Cfg<.., F16, RT<=4>::SEG
   const size_t ld = (size_t)(xd.d_in + seg - 1) / seg * seg;
   const size_t xbytes = (size_t)RT * ld * 2;
   const size_t zbytes = (size_t)nl * xd.k * 4;
   const int max_cols = (nl * zc.d_out + G - 1) / G + 1;
-  if (max_cols > kThreads) return false;  // one column range per thread
+  if (max_cols > kFT) return false;  // one column range per thread
   const int x_items = (int)((size_t)RT * ld / 8);
-  const int NX = (x_items + kThreads - 1) / kThreads;
-  if (NX > 8 || (NX != 2 * RT && NX != 4 * RT)) return false;  // X held in registers
+  const int NX = (x_items + kFT - 1) / kFT;
+  if (NX != RT && NX != 2 * RT) return false;  // X rows held in registers: ld <= 8192
+  if (NX > 4) return false;
   p->G = G;
   p->A = A;
   p->RT = RT;
@@ -426,25 +428,25 @@ hipError_t launch5(FusedLaunch f, const Plan& p, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.smem);
   if (err != hipSuccess) return err;
   int per_cu = 0;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, p.smem);
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFT, p.smem);
   if (err != hipSuccess) return err;
   if (per_cu < 1) return hipErrorInvalidConfiguration;  // grid must be co-resident
   f.col_bytes = (int)p.col_bytes;
-  hipLaunchKernelGGL(kern, dim3(p.G), dim3(kThreads), p.smem, s, f);
+  hipLaunchKernelGGL(kern, dim3(p.G), dim3(kFT), p.smem, s, f);
   return hipGetLastError();
 }
 
 template <int DT, int VT, int RT, int A>
 hipError_t launch4(FusedLaunch f, const Plan& p, hipStream_t s) {
   if constexpr (RT <= 2) {
-    if (p.NX == 4 * RT) return launch5<DT, VT, RT, A, 4 * RT>(f, p, s);
+    if (p.NX == 2 * RT) return launch5<DT, VT, RT, A, 2 * RT>(f, p, s);
   }
-  return launch5<DT, VT, RT, A, 2 * RT>(f, p, s);
+  return launch5<DT, VT, RT, A, RT>(f, p, s);
 }
 
 template <int DT, int VT, int RT>
 hipError_t launch3(FusedLaunch f, const Plan& p, hipStream_t s) {
-  return p.A == 2 ? launch4<DT, VT, RT, 2>(f, p, s) : launch4<DT, VT, RT, 3>(f, p, s);
+  return p.A == 1 ? launch4<DT, VT, RT, 1>(f, p, s) : launch4<DT, VT, RT, 2>(f, p, s);
 }
 
 template <int DT, int VT>
