@@ -177,6 +177,22 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
   }
   // this launch's epoch word (consumed only when Z is published)
   const uint32_t epoch_old = ld_agent(f.ctrl + kCtrlEpochs + blockIdx.x);
+  // ---- 1. the bounds of this lane's columns in rounds 0 and 1, loaded by
+  // the lane itself so that its C loads can go out right behind the D loads
+  const int slot = wave * 4 + (lane >> 4);
+  int rs_raw[2], re_raw[2], rl[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int ci = r * kSlots + slot < ncols ? r * kSlots + slot : 0;
+    const int l = (c0 + ci) / d_out, j = c0 + ci - l * d_out;
+    const int32_t* cpr = sreg_ptr(z.colptr[0]);
+#pragma unroll
+    for (int i = 1; i < kFusedMaxLayers; ++i)
+      if (l == i) cpr = sreg_ptr(z.colptr[i]);
+    rs_raw[r] = gptr(cpr)[j];
+    re_raw[r] = gptr(cpr)[j + 1];
+    rl[r] = l;
+  }
   // ---- 1a. this thread's column range (raw colptr values, used at commit)
   const int cidx = tid < ncols ? tid : 0;
   const int cl = (c0 + cidx) / d_out, cj = c0 + cidx - cl * d_out;
@@ -234,8 +250,51 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
   };
   load_d(0);
 
+  // ---- 2. rounds 0 and 1 of C chunks in flight behind the D loads (waits
+  // only for the lane's own colptr values, the oldest loads)
+  auto load_chunks = [&](IdxChunk* ic, ValChunk<VT>* vc, int s0, int e0, const uint16_t* rowidx,
+                         const void* vals, const uint8_t* vsc, int64_t nnz) {
+    const int p0 = (s0 & ~7) + g * 8;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int p = p0 + 128 * u;
+      if (p < e0) {
+        ic[u].load(rowidx, p, nnz);
+        vc[u].load(vals, vsc, p, nnz);
+      }
+    }
+  };
+  IdxChunk ia[kU], ib[kU];
+  ValChunk<VT> va[kU], vb[kU];
+  int rse[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int l = rl[r];
+    const uint16_t* rowidx = sreg_ptr(z.rowidx[0]);
+    const void* vals = sreg_ptr(z.vals[0]);
+    const uint8_t* vsc = sreg_ptr(z.vscales[0]);
+    int64_t nnz = z.nnz[0];
+#pragma unroll
+    for (int i = 1; i < kFusedMaxLayers; ++i)
+      if (l == i) {
+        rowidx = sreg_ptr(z.rowidx[i]);
+        vals = sreg_ptr(z.vals[i]);
+        vsc = sreg_ptr(z.vscales[i]);
+        nnz = z.nnz[i];
+      }
+    const bool live = r * kSlots + slot < ncols;
+    const int s0 = live ? (int)min<int64_t>(max(rs_raw[r], 0), nnz) : 0;
+    const int e0 = live ? (int)min<int64_t>(max(re_raw[r], s0), nnz) : 0;
+    rse[r][0] = s0;
+    rse[r][1] = e0;
+    if (r == 0)
+      load_chunks(ia, va, s0, e0, rowidx, vals, vsc, nnz);
+    else
+      load_chunks(ib, vb, s0, e0, rowidx, vals, vsc, nnz);
+  }
+
   // ---- 1d. commit the column ranges and X to LDS (waits only for the older
-  // colptr and X loads; the D stream stays in flight)
+  // colptr and X loads; the D and C streams stay in flight)
   if (tid < ncols) {
     const int nz = (int)cnz;
     const int s0 = min(max(s_raw, 0), nz);
@@ -251,28 +310,15 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
   }
   __syncthreads();
 
-  // ---- 2. first two rounds of C chunks in flight
-  const int slot = wave * 4 + (lane >> 4);
+  // later rounds: bounds from the LDS table
   auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
     const int ci = r * kSlots + slot;
     if (ci < ncols) {
       const int2 se = cse[ci];
       const LayerRow& L = lt[(c0 + ci) / d_out];
-      const int p0 = (se.x & ~7) + g * 8;
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int p = p0 + 128 * u;
-        if (p < se.y) {
-          ic[u].load(L.rowidx, p, L.nnz);
-          vc[u].load(L.vals, L.vsc, p, L.nnz);
-        }
-      }
+      load_chunks(ic, vc, se.x, se.y, L.rowidx, L.vals, L.vsc, L.nnz);
     }
   };
-  IdxChunk ia[kU], ib[kU];
-  ValChunk<VT> va[kU], vb[kU];
-  load_round(ia, va, 0);
-  load_round(ib, vb, 1);
 
   // ---- 3. Z for this workgroup's atoms, published as epoch-tagged words
   float acc[A][RT];
