@@ -45,6 +45,8 @@ def _parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -180,6 +182,15 @@ def main():
     _log(f"two-launch step: {us_two:.2f} us")
     dom = "fused_decode"
     assert B.workspace_error_word(ws) == 0, "grid barrier timed out"
+
+    # ---------------------------------------------------------------- counter calibration
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)  # a plain copy kernel: reads and writes exactly this many bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------------------------------------------------------- prefill (extra)
     extras = {}
