@@ -36,6 +36,38 @@ METRIC = "µs and HBM GB/s per factored projection (b=1 decode); TFLOP/s at pref
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 
+# HBM traffic of one launch of the dominant kernel, from two rocprofv3 --pmc passes over
+# `bench.py --steps 20 --warmup 2 --no-cpu --no-prefill --copy-calibration-mib 256`
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the kernel's dispatches).
+# Each counter is scaled by what it reads for the plain 256 MiB device copy in the same
+# run (FETCH_SIZE reads 131086 KiB for 262144 KiB fetched: x2.0; WRITE_SIZE reads 262144
+# KiB: x1.0).  The figure holds only for the kernel source it was taken on: the digest
+# of the sources below must match, otherwise traffic is reported as null.
+TRAFFIC_SOURCES = ("dictionary_factored_sparse_amd/csrc/fused_decode.hip",
+                   "dictionary_factored_sparse_amd/csrc/csc_chunks.hpp",
+                   "dictionary_factored_sparse_amd/csrc/gemv_common.hpp",
+                   "dictionary_factored_sparse_amd/csrc/dfs_internal.hpp",
+                   "include/dictfs.h")
+TRAFFIC_MEASURED = {"digest": "0c73788433ae22b559483f8a776d9f0ccc36a7a99f61caf5f72879886495224a",
+                    "fetch_kib": 18530.13, "write_kib": 152.0,
+                    "fetch_scale": 1.99978, "write_scale": 1.0}
+
+
+def _sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _traffic_bytes():
+    t = TRAFFIC_MEASURED
+    if _sources_digest() != t["digest"]:
+        return None
+    return int(round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])))
+
 
 def _parse():
     ap = argparse.ArgumentParser()
@@ -181,7 +213,7 @@ def main():
         _log(f"{n}: {v['us']:.2f} us/launch, {v['gbs']:.0f} GB/s")
     _log(f"two-launch step: {us_two:.2f} us")
     dom = "fused_decode"
-    assert B.workspace_error_word(ws) == 0, "grid barrier timed out"
+    assert B.workspace_error_word(ws) == 0, "Z hand-off wait timed out"
 
     # ---------------------------------------------------------------- counter calibration
     if args.copy_calibration_mib:
@@ -266,10 +298,11 @@ def main():
         "config": {"workload": "q_proj decode group: 2 layers, d_in=d_out=4096, k=2048, "
                                "C density 0.30 CSC uint16 f16, T=1 f16",
                    "bytes_per_step": step_bytes, "replicas": R, "timing": "hip graph replay",
-                   "path": "one-launch decode (Z = X D, grid barrier, Y_l = Z_l C_l)"},
+                   "path": "one-launch decode (Z = X D, epoch-tagged Z hand-off, Y_l = Z_l C_l)"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(d["gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": _traffic_bytes(),
+                     "traffic_unit": "bytes per launch",
                      "us_per_launch": round(d["us"], 3), "bytes_per_launch": d["bytes"]},
         "kernels": {n: {"us_per_launch": round(v["us"], 3), "GB/s": round(v["gbs"], 1)}
                     for n, v in kern.items()},
