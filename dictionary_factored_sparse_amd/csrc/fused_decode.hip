@@ -6,18 +6,17 @@
 // group) and each C_l.  Run as two kernels, C_l's stream cannot start until
 // the Z kernel ends.  Here one persistent grid (one workgroup per CU) does
 // both:
-//   1. each workgroup puts its slice of D_g's atoms in flight, then commits
-//      X and the [start, end) of its output columns to LDS;
-//   2. it issues the loads of its first two rounds of C chunks (they do not
-//      depend on Z);
-//   3. it computes its atoms' Z and publishes them as epoch-tagged words;
-//   4. it receives the Z rows of its layers (polling for the current epoch)
-//      into LDS and finishes its columns, later rounds of C double-buffered
-//      in registers.
-// So the C stream overlaps the D stream and the Z dependency costs one
-// round trip through memory instead of a second launch.  The grid never
-// exceeds one workgroup per CU, so every workgroup is resident; every wait
-// is bounded anyway (see receive_z), so the kernel always terminates.
+//   1. each workgroup puts its X rows and its slice of D_g's atoms in flight;
+//   2. it computes its atoms' Z and publishes them as epoch-tagged words;
+//   3. it issues the loads of its coefficient columns (they do not depend on
+//      Z), then receives the Z rows of its layers (polling for the current
+//      epoch) into LDS while those loads arrive;
+//   4. it finishes its columns, later rounds of C double-buffered in
+//      registers.
+// So the Z dependency costs one round trip through memory, hidden under the
+// C stream, instead of a second launch.  The grid never exceeds one
+// workgroup per CU, so every workgroup is resident; every wait is bounded
+// anyway (see receive_z), so the kernel always terminates.
 #include "csc_chunks.hpp"
 #include "gemv_common.hpp"
 
@@ -140,13 +139,35 @@ __device__ __forceinline__ float gather_chunk(const float* zl, const IdxChunk& i
   return sum;
 }
 
+// Kernel arguments, compact so that they fit a few scalar-cache lines: the
+// first line holds everything the first loads need.
+struct FusedArgs {
+  const void* D;  // f16 atoms, or NVFP4 codes
+  const uint8_t* dscales;
+  int64_t ldd;
+  int32_t d_in, k;
+  const void* X[kFusedMaxLayers];
+  const int32_t* colptr[kFusedMaxLayers];
+  const uint16_t* rowidx[kFusedMaxLayers];
+  const void* vals[kFusedMaxLayers];
+  const uint8_t* vscales[kFusedMaxLayers];
+  const float* vts[kFusedMaxLayers];
+  void* Y[kFusedMaxLayers];
+  int64_t nnz[kFusedMaxLayers];
+  const float* dts;
+  uint64_t* zz;    // n_layers x k epoch-tagged Z words
+  uint32_t* ctrl;  // control block
+  int32_t n_layers, d_out, ydt;
+  uint32_t spin_limit;
+  int32_t col_bytes;
+  int32_t G;  // workgroups in the grid
+};
+
 template <int DT, int VT, int RT, int A, int NX>
-__global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
+__global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   using Cf = Cfg<DT, DFS_F16, RT>;
   constexpr int CE = Cf::CE, SEGC = Cf::SEGC, SEG = Cf::SEG;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const XdLaunch& a = f.xd;
-  const ZcLaunch& z = f.zc;
   LayerRow* lt = reinterpret_cast<LayerRow*>(smem);            // [kFusedMaxLayers]
   int2* cse = reinterpret_cast<int2*>(smem + kLayerTableBytes);  // [ncols] column [start, end)
   char* big = smem + kLayerTableBytes + f.col_bytes;           // X rows, later all of Z
@@ -157,72 +178,71 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int g = lane & 15;
-  const int G = gridDim.x;
-  const int d_in = a.d_in, k = a.k, d_out = z.d_out, nl = z.n_layers;
-  const int NC = nl * d_out;
-  const int c0 = (int)((int64_t)blockIdx.x * NC / G);
-  const int c1 = (int)((int64_t)(blockIdx.x + 1) * NC / G);
+  // Every kernel argument needed before the first wait is fetched in one
+  // batch of scalar loads (one round trip instead of one per first use).
+  const int d_in = f.d_in, k = f.k, d_out = f.d_out, nl = f.n_layers;
+  asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
+               "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
+               "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G));
+  static_assert(SEG % (8 * kFT) == 0, "an X row is a whole number of 512-thread passes");
+  constexpr int NR = NX / RT;  // passes of the workgroup per X row
+  static_assert(NR * RT == NX, "X register count");
+  const int ld = (d_in + SEG - 1) / SEG * SEG;  // == NR * 8 * kFT
+
+  // Order of the loads.  Vector loads retire in order, so a wait for one
+  // load also waits for every older one.  Issued first are the small loads
+  // whose values are needed early (X, the epoch word, the column bounds),
+  // then this workgroup's atoms of D_g.  The coefficient columns are issued
+  // only once the workgroup's own atoms have arrived and Z is published:
+  // the memory system serves requests roughly in arrival order, so D_g is
+  // never queued behind C, Z is ready after about half of the stream, and
+  // the Z hand-off runs while the C half is arriving.  Loads are issued
+  // without branches (out-of-range addresses are clamped and the values
+  // masked), so the compiler can count exactly how many are in flight.
+  // ---- 1. X rows (all of d_in, zero padded to ld), held in registers
+  u4 xr[NX];
+#pragma unroll
+  for (int jx = 0; jx < NX; ++jx) {
+    const int r = jx / NR;
+    const int ge = ((jx % NR) * kFT + tid) * 8;
+    const _Float16* xrow = (const _Float16*)(r < nl ? sreg_ptr(f.X[r]) : sreg_ptr(f.X[0]));
+    const bool ok = r < nl && ge < d_in;
+    const u4 v = ld16<u4>(xrow + (ok ? ge : 0));  // d_in % 8 == 0 on this path
+    xr[jx] = ok ? v : u4{0u, 0u, 0u, 0u};
+  }
+  // ---- 2. this launch's epoch word and the bounds of this workgroup's columns
+  const uint32_t NC = (uint32_t)(nl * d_out);  // NC * (G + 1) < 2^32 (host check)
+  const int c0 = (int)(blockIdx.x * NC / (uint32_t)f.G);
+  const int c1 = (int)((blockIdx.x + 1) * NC / (uint32_t)f.G);
   const int ncols = c1 - c0;  // <= kFT (checked on the host)
   const int rounds = (ncols + kSlots - 1) / kSlots;
-  const int ld = (d_in + SEG - 1) / SEG * SEG;
-
-  // Loads are issued oldest-first in the order they are needed: vector loads
-  // retire in order, so waiting for an early load must not have to wait for
-  // the weight stream queued behind it.
-  // ---- 0. layer table from the kernel arguments (scalar loads, LGKM counter)
-  if (tid == 0) {
-#pragma unroll
-    for (int l = 0; l < kFusedMaxLayers; ++l)
-      lt[l] = LayerRow{z.colptr[l], z.rowidx[l], z.vals[l], z.vscales[l], z.vts[l], z.Y[l], z.nnz[l]};
-  }
-  // this launch's epoch word (consumed only when Z is published)
   const uint32_t epoch_old = ld_agent(f.ctrl + kCtrlEpochs + blockIdx.x);
-  // ---- 1. the bounds of this lane's columns in rounds 0 and 1, loaded by
-  // the lane itself so that its C loads can go out right behind the D loads
+  // this lane's columns in rounds 0 and 1 (16 lanes per column)
   const int slot = wave * 4 + (lane >> 4);
   int rs_raw[2], re_raw[2], rl[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int ci = r * kSlots + slot < ncols ? r * kSlots + slot : 0;
     const int l = (c0 + ci) / d_out, j = c0 + ci - l * d_out;
-    const int32_t* cpr = sreg_ptr(z.colptr[0]);
+    const int32_t* cpr = sreg_ptr(f.colptr[0]);
 #pragma unroll
     for (int i = 1; i < kFusedMaxLayers; ++i)
-      if (l == i) cpr = sreg_ptr(z.colptr[i]);
+      if (l == i) cpr = sreg_ptr(f.colptr[i]);
     rs_raw[r] = gptr(cpr)[j];
     re_raw[r] = gptr(cpr)[j + 1];
     rl[r] = l;
   }
-  // ---- 1a. this thread's column range (raw colptr values, used at commit)
+  // this thread's column (one per thread, for the LDS table of later rounds)
   const int cidx = tid < ncols ? tid : 0;
   const int cl = (c0 + cidx) / d_out, cj = c0 + cidx - cl * d_out;
-  const int32_t* cp = sreg_ptr(z.colptr[0]);
-  int64_t cnz = z.nnz[0];
+  const int32_t* cp = sreg_ptr(f.colptr[0]);
 #pragma unroll
   for (int i = 1; i < kFusedMaxLayers; ++i)
-    if (cl == i) {
-      cp = sreg_ptr(z.colptr[i]);
-      cnz = z.nnz[i];
-    }
+    if (cl == i) cp = sreg_ptr(f.colptr[i]);
   const int s_raw = gptr(cp)[cj], e_raw = gptr(cp)[cj + 1];
-  // ---- 1b. X rows (all of d_in, zero padded to ld), held in registers
-  const int x_items = RT * ld / 8, x_per_row = ld / 8;
-  u4 xr[NX];
-#pragma unroll
-  for (int jx = 0; jx < NX; ++jx) {
-    const int item = jx * kFT + tid;
-    const int r = item / x_per_row;
-    const int ge = (item - r * x_per_row) * 8;
-    xr[jx] = u4{0u, 0u, 0u, 0u};
-    if (item < x_items && r < nl && ge < d_in) {
-      const _Float16* xrow = (const _Float16*)sreg_ptr(a.X[0]);
-#pragma unroll
-      for (int i = 1; i < RT; ++i)
-        if (r == i) xrow = (const _Float16*)sreg_ptr(a.X[i]);
-      xr[jx] = ld16<u4>(xrow + ge);  // d_in % 8 == 0 on this path
-    }
-  }
-  // ---- 1c. this workgroup's atoms: every D load of the first segment
+
+  // ---- 3. this workgroup's atoms of D_g (an out-of-range chunk loads
+  // element 0 and is zeroed)
   const int atom0 = (blockIdx.x * kFW + wave) * A;
   u4 dreg[A][SEGC];
   uint32_t sreg[A][SEGC];
@@ -233,94 +253,35 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
 #pragma unroll
       for (int c = 0; c < SEGC; ++c) {
         const int e0 = seg + (c * kWave + lane) * CE;
-        dreg[i][c] = u4{0u, 0u, 0u, 0u};
-        sreg[i][c] = 0u;
-        if (atom < k && e0 < d_in) {
-          if constexpr (DT == DFS_NVFP4) {
-            const int64_t el = (int64_t)atom * d_in + e0;
-            dreg[i][c] = ld16<u4>(a.dcodes + el / 2);
-            sreg[i][c] = (uint32_t)gptr(a.dscales)[el / 16] |
-                         ((uint32_t)gptr(a.dscales)[el / 16 + 1] << 8);
-          } else {
-            dreg[i][c] = ld16<u4>((const _Float16*)a.D + (int64_t)atom * a.ldd + e0);
-          }
+        const bool ok = atom < k && e0 < d_in;
+        if constexpr (DT == DFS_NVFP4) {
+          const int64_t el = ok ? (int64_t)atom * d_in + e0 : 0;
+          const u4 v = ld16<u4>((const uint8_t*)f.D + el / 2);
+          const uint32_t s0 = gptr(f.dscales)[el / 16], s1 = gptr(f.dscales)[el / 16 + 1];
+          dreg[i][c] = ok ? v : u4{0u, 0u, 0u, 0u};
+          sreg[i][c] = ok ? (s0 | (s1 << 8)) : 0u;
+        } else {
+          const u4 v = ld16<u4>((const _Float16*)f.D + (ok ? (int64_t)atom * f.ldd + e0 : 0));
+          dreg[i][c] = ok ? v : u4{0u, 0u, 0u, 0u};
+          sreg[i][c] = 0u;
         }
       }
     }
   };
   load_d(0);
 
-  // ---- 2. rounds 0 and 1 of C chunks in flight behind the D loads (waits
-  // only for the lane's own colptr values, the oldest loads)
-  auto load_chunks = [&](IdxChunk* ic, ValChunk<VT>* vc, int s0, int e0, const uint16_t* rowidx,
-                         const void* vals, const uint8_t* vsc, int64_t nnz) {
-    const int p0 = (s0 & ~7) + g * 8;
+  // ---- 4. layer table (scalar loads) and X into LDS (waits for X only)
+  if (tid == 0) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int p = p0 + 128 * u;
-      if (p < e0) {
-        ic[u].load(rowidx, p, nnz);
-        vc[u].load(vals, vsc, p, nnz);
-      }
-    }
-  };
-  IdxChunk ia[kU], ib[kU];
-  ValChunk<VT> va[kU], vb[kU];
-  int rse[2][2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int l = rl[r];
-    const uint16_t* rowidx = sreg_ptr(z.rowidx[0]);
-    const void* vals = sreg_ptr(z.vals[0]);
-    const uint8_t* vsc = sreg_ptr(z.vscales[0]);
-    int64_t nnz = z.nnz[0];
-#pragma unroll
-    for (int i = 1; i < kFusedMaxLayers; ++i)
-      if (l == i) {
-        rowidx = sreg_ptr(z.rowidx[i]);
-        vals = sreg_ptr(z.vals[i]);
-        vsc = sreg_ptr(z.vscales[i]);
-        nnz = z.nnz[i];
-      }
-    const bool live = r * kSlots + slot < ncols;
-    const int s0 = live ? (int)min<int64_t>(max(rs_raw[r], 0), nnz) : 0;
-    const int e0 = live ? (int)min<int64_t>(max(re_raw[r], s0), nnz) : 0;
-    rse[r][0] = s0;
-    rse[r][1] = e0;
-    if (r == 0)
-      load_chunks(ia, va, s0, e0, rowidx, vals, vsc, nnz);
-    else
-      load_chunks(ib, vb, s0, e0, rowidx, vals, vsc, nnz);
-  }
-
-  // ---- 1d. commit the column ranges and X to LDS (waits only for the older
-  // colptr and X loads; the D and C streams stay in flight)
-  if (tid < ncols) {
-    const int nz = (int)cnz;
-    const int s0 = min(max(s_raw, 0), nz);
-    cse[tid] = make_int2(s0, min(max(e_raw, s0), nz));
+    for (int l = 0; l < kFusedMaxLayers; ++l)
+      lt[l] = LayerRow{f.colptr[l], f.rowidx[l], f.vals[l], f.vscales[l], f.vts[l], f.Y[l], f.nnz[l]};
   }
 #pragma unroll
-  for (int jx = 0; jx < NX; ++jx) {
-    const int item = jx * kFT + tid;
-    if (item < x_items) {
-      const int r = item / x_per_row;
-      *reinterpret_cast<u4*>(xs + r * ld + (item - r * x_per_row) * 8) = xr[jx];
-    }
-  }
+  for (int jx = 0; jx < NX; ++jx)
+    *reinterpret_cast<u4*>(xs + (jx / NR) * ld + ((jx % NR) * kFT + tid) * 8) = xr[jx];
   __syncthreads();
 
-  // later rounds: bounds from the LDS table
-  auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
-    const int ci = r * kSlots + slot;
-    if (ci < ncols) {
-      const int2 se = cse[ci];
-      const LayerRow& L = lt[(c0 + ci) / d_out];
-      load_chunks(ic, vc, se.x, se.y, L.rowidx, L.vals, L.vsc, L.nnz);
-    }
-  };
-
-  // ---- 3. Z for this workgroup's atoms, published as epoch-tagged words
+  // ---- 5. Z for this workgroup's atoms; 6. published as epoch-tagged words
   float acc[A][RT];
 #pragma unroll
   for (int i = 0; i < A; ++i)
@@ -341,9 +302,8 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
     }
   }
   float dts = 1.0f;
-  if constexpr (DT == DFS_NVFP4) dts = *gptr(a.dts);
+  if constexpr (DT == DFS_NVFP4) dts = *gptr(f.dts);
   const uint32_t epoch = epoch_old + 1u;
-  uint64_t* zz = reinterpret_cast<uint64_t*>(f.zws);
 #pragma unroll
   for (int i = 0; i < A; ++i) {
     const int atom = atom0 + i;
@@ -351,21 +311,74 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
     for (int r = 0; r < RT; ++r) {
       const float v = wave_sum(acc[i][r]) * dts;
       if (lane == r && atom < k && r < nl)
-        st_agent64(zz + (int64_t)r * k + atom, ((uint64_t)epoch << 32) | __float_as_uint(v));
+        st_agent64(f.zz + (int64_t)r * k + atom, ((uint64_t)epoch << 32) | __float_as_uint(v));
     }
   }
 
-  // ---- 4. receive the Z rows of this workgroup's layers into LDS
+  // ---- 7. the column ranges into LDS; rounds 0 and 1 of C in flight (their
+  // bounds are older than D, so nothing here waits)
+  if (tid < ncols) {
+    const int nz = (int)lt[cl].nnz;
+    const int s0 = min(max(s_raw, 0), nz);
+    cse[tid] = make_int2(s0, min(max(e_raw, s0), nz));
+  }
+  auto load_chunks = [&](IdxChunk* ic, ValChunk<VT>* vc, int s0, int e0, const uint16_t* rowidx,
+                         const void* vals, const uint8_t* vsc, int64_t nnz) {
+    const int p0 = (s0 & ~7) + g * 8;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int p = p0 + 128 * u;
+      if (p < e0) {
+        ic[u].load(rowidx, p, nnz);
+        vc[u].load(vals, vsc, p, nnz);
+      }
+    }
+  };
+  IdxChunk ia[kU], ib[kU];
+  ValChunk<VT> va[kU], vb[kU];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int l = rl[r];
+    const uint16_t* rowidx = sreg_ptr(f.rowidx[0]);
+    const void* vals = sreg_ptr(f.vals[0]);
+    const uint8_t* vsc = sreg_ptr(f.vscales[0]);
+    int64_t nnz = f.nnz[0];
+#pragma unroll
+    for (int i = 1; i < kFusedMaxLayers; ++i)
+      if (l == i) {
+        rowidx = sreg_ptr(f.rowidx[i]);
+        vals = sreg_ptr(f.vals[i]);
+        vsc = sreg_ptr(f.vscales[i]);
+        nnz = f.nnz[i];
+      }
+    const bool live = r * kSlots + slot < ncols;
+    const int s0 = live ? (int)min<int64_t>(max(rs_raw[r], 0), nnz) : 0;
+    const int e0 = live ? (int)min<int64_t>(max(re_raw[r], s0), nnz) : 0;
+    if (r == 0)
+      load_chunks(ia, va, s0, e0, rowidx, vals, vsc, nnz);
+    else
+      load_chunks(ib, vb, s0, e0, rowidx, vals, vsc, nnz);
+  }
+  auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
+    const int ci = r * kSlots + slot;
+    if (ci < ncols) {
+      const int2 se = cse[ci];
+      const LayerRow& L = lt[(c0 + ci) / d_out];
+      load_chunks(ic, vc, se.x, se.y, L.rowidx, L.vals, L.vsc, L.nnz);
+    }
+  };
+
+  // ---- 8. receive the Z rows of this workgroup's layers into LDS
   {
     const int l_first = c0 / d_out, l_last = (c1 - 1) / d_out;
-    receive_z(zs + l_first * k, zz + (int64_t)l_first * k, (l_last - l_first + 1) * k, epoch,
+    receive_z(zs + l_first * k, f.zz + (int64_t)l_first * k, (l_last - l_first + 1) * k, epoch,
               f.ctrl + kCtrlErr, f.spin_limit);
   }
   __syncthreads();
   // every wave has published and received: advance this workgroup's epoch
   if (tid == 0) st_agent(f.ctrl + kCtrlEpochs + blockIdx.x, epoch);
 
-  // ---- 5. the columns, two rounds in flight
+  // ---- 9. the columns, two rounds in flight
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int r) {
     const int ci = r * kSlots + slot;
     int s = 0, e = 0, l = 0;
@@ -405,7 +418,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedLaunch f) {
       if constexpr (VT == DFS_NVFP4) ts = *gptr(lt[l].vts);
       const int j = c0 + ci - l * d_out;
       void* y = lt[l].Y;
-      if (z.ydt == DFS_F16)
+      if (f.ydt == DFS_F16)
         gptr_w((_Float16*)y)[j] = (_Float16)(sum * ts);
       else
         gptr_w((float*)y)[j] = sum * ts;
@@ -454,6 +467,7 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   const size_t zbytes = (size_t)nl * xd.k * 4;
   const int max_cols = (nl * zc.d_out + G - 1) / G + 1;
   if (max_cols > kFT) return false;  // one column range per thread
+  if ((uint64_t)nl * (uint64_t)zc.d_out * (uint64_t)(G + 1) >= (1ull << 32)) return false;
   const int x_items = (int)((size_t)RT * ld / 8);
   const int NX = (x_items + kFT - 1) / kFT;
   if (NX != RT && NX != 2 * RT) return false;  // X rows held in registers: ld <= 8192
@@ -468,7 +482,7 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
 }
 
 template <int DT, int VT, int RT, int A, int NX>
-hipError_t launch5(FusedLaunch f, const Plan& p, hipStream_t s) {
+hipError_t launch5(FusedArgs f, const Plan& p, hipStream_t s) {
   auto kern = fused_decode_kernel<DT, VT, RT, A, NX>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.smem);
@@ -478,12 +492,13 @@ hipError_t launch5(FusedLaunch f, const Plan& p, hipStream_t s) {
   if (err != hipSuccess) return err;
   if (per_cu < 1) return hipErrorInvalidConfiguration;  // grid must be co-resident
   f.col_bytes = (int)p.col_bytes;
+  f.G = p.G;
   hipLaunchKernelGGL(kern, dim3(p.G), dim3(kFT), p.smem, s, f);
   return hipGetLastError();
 }
 
 template <int DT, int VT, int RT, int A>
-hipError_t launch4(FusedLaunch f, const Plan& p, hipStream_t s) {
+hipError_t launch4(FusedArgs f, const Plan& p, hipStream_t s) {
   if constexpr (RT <= 2) {
     if (p.NX == 2 * RT) return launch5<DT, VT, RT, A, 2 * RT>(f, p, s);
   }
@@ -491,12 +506,12 @@ hipError_t launch4(FusedLaunch f, const Plan& p, hipStream_t s) {
 }
 
 template <int DT, int VT, int RT>
-hipError_t launch3(FusedLaunch f, const Plan& p, hipStream_t s) {
+hipError_t launch3(FusedArgs f, const Plan& p, hipStream_t s) {
   return p.A == 1 ? launch4<DT, VT, RT, 1>(f, p, s) : launch4<DT, VT, RT, 2>(f, p, s);
 }
 
 template <int DT, int VT>
-hipError_t launch2(FusedLaunch f, const Plan& p, hipStream_t s) {
+hipError_t launch2(FusedArgs f, const Plan& p, hipStream_t s) {
   switch (p.RT) {
     case 1: return launch3<DT, VT, 1>(f, p, s);
     case 2: return launch3<DT, VT, 2>(f, p, s);
@@ -521,11 +536,28 @@ hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, float* zw
                                uint32_t* ctrl, hipStream_t s) {
   Plan p;
   if (!plan(xd, zc, &p)) return hipErrorInvalidValue;
-  FusedLaunch f;
-  f.xd = xd;
-  f.zc = zc;
-  f.zws = zws;
+  FusedArgs f = {};
+  f.D = xd.ddt == DFS_NVFP4 ? (const void*)xd.dcodes : xd.D;
+  f.dscales = xd.dscales;
+  f.ldd = xd.ldd;
+  f.d_in = xd.d_in;
+  f.k = xd.k;
+  for (int l = 0; l < zc.n_layers; ++l) {
+    f.X[l] = xd.X[l];
+    f.colptr[l] = zc.colptr[l];
+    f.rowidx[l] = zc.rowidx[l];
+    f.vals[l] = zc.vals[l];
+    f.vscales[l] = zc.vscales[l];
+    f.vts[l] = zc.vts[l];
+    f.Y[l] = zc.Y[l];
+    f.nnz[l] = zc.nnz[l];
+  }
+  f.dts = xd.dts;
+  f.zz = reinterpret_cast<uint64_t*>(zws);
   f.ctrl = ctrl;
+  f.n_layers = zc.n_layers;
+  f.d_out = zc.d_out;
+  f.ydt = zc.ydt;
   f.spin_limit = 1u << 22;
   f.col_bytes = 0;
   if (xd.ddt == DFS_NVFP4)
