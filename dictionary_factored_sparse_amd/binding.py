@@ -27,7 +27,7 @@ STATUS = {0: "DFS_OK", 1: "DFS_E_INVALID", 2: "DFS_E_UNSUPPORTED", 3: "DFS_E_RAN
 SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspace_size",
            "nvfp4_pack", "nvfp4_unpack", "dict_workspace_size", "dict_proj_forward",
            "dict_group_forward", "dict_xd_forward", "dict_xd_workspace_size", "dict_zc_forward",
-           "dfs_status_str", "dfs_last_hip_error", "dfs_version")
+           "dfs_status_str", "dfs_last_hip_error", "dfs_version", "dict_csc_capacity")
 
 
 class NV(C.Structure):
@@ -92,6 +92,8 @@ def lib():
         L.dfs_status_str.restype = C.c_char_p
         L.dfs_last_hip_error.restype = C.c_int32
         L.dfs_version.restype = C.c_int32
+        L.dict_csc_capacity.argtypes = [C.c_int64]
+        L.dict_csc_capacity.restype = C.c_int64
         _lib = L
     return _lib
 
@@ -178,9 +180,9 @@ class DeviceCSC:
                    self.rowidx.data_ptr(), self.vals.data_ptr(), NV())
 
 
-def _pad16(n: int, esz: int) -> int:
-    per = 16 // esz
-    return max((n + per - 1) // per * per, per)
+def dict_csc_capacity(nnz: int) -> int:
+    """Entries rowidx/vals must be allocated for (whole 8-entry chunks)."""
+    return int(lib().dict_csc_capacity(int(nnz)))
 
 
 # ----------------------------------------------------------------- packing
@@ -202,8 +204,9 @@ def dict_pack_csc(Cd: torch.Tensor, stream=None) -> DeviceCSC:
                                                 colptr.data_ptr(), None, None, 0, C.byref(nnz),
                                                 ws.data_ptr(), ws_n.value, st))
     n = nnz.value
-    rowidx = torch.zeros(_pad16(n, 2), dtype=torch.int16, device=dev)
-    vals = torch.zeros(_pad16(n, Cd.element_size()), dtype=Cd.dtype, device=dev)
+    cap = dict_csc_capacity(n)
+    rowidx = torch.zeros(cap, dtype=torch.int16, device=dev)
+    vals = torch.zeros(cap, dtype=Cd.dtype, device=dev)
     _check("dict_pack_csc", lib().dict_pack_csc(Cd.data_ptr(), _dt(Cd), k, d_out, Cd.stride(0),
                                                 colptr.data_ptr(), rowidx.data_ptr(),
                                                 vals.data_ptr(), rowidx.numel(), C.byref(nnz),

@@ -235,7 +235,12 @@ const char* dfs_status_str(dfs_status st) {
 
 int32_t dfs_last_hip_error(void) { return g_last_hip; }
 
-int32_t dfs_version(void) { return 100; }
+int32_t dfs_version(void) { return 200; }
+
+int64_t dict_csc_capacity(int64_t nnz) {
+  if (nnz < 8) return 8;
+  return (nnz + 7) / 8 * 8;
+}
 
 // ------------------------------------------------------------------ packing
 
@@ -265,7 +270,7 @@ dfs_status dict_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out,
   *nnz_host = total;
   if (total >= kMaxNnz) return DFS_E_RANGE;
   if (!rowidx) return DFS_OK;
-  if (total > capacity) return DFS_E_RANGE;
+  if (capacity < dict_csc_capacity(total)) return DFS_E_RANGE;
   DFS_HIP(launch_pack_csc_scatter(C, dtype, k, d_out, ldc, rowidx, vals, ws, s));
   return DFS_OK;
 }

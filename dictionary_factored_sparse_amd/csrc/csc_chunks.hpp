@@ -3,25 +3,28 @@
 // The coefficient kernels read C_l as aligned groups of 8 consecutive stored
 // entries: 16 bytes of uint16 row indices plus the matching values (16 bytes
 // of f16, 32 bytes of f32, or 4 bytes of E2M1 codes and the one E4M3 block
-// scale that covers them: 8 divides the 16-entry NVFP4 block).  A chunk that
-// would run past the end of the arrays is read entry by entry.
+// scale that covers them: 8 divides the 16-entry NVFP4 block).  The arrays
+// are allocated for a whole number of chunks (dict_csc_capacity), so every
+// chunk is one unconditional load; entries past nnz are masked by the caller.
+// `p` is always a multiple of 8 below the capacity.
 #pragma once
 
 #include "dfs_internal.hpp"
 
 namespace dfs {
 
+// Start of the chunk that holds entry e - 1 (the last entry of a column that
+// ends at e; 0 when e == 0).  A lane whose chunk lies past its column loads
+// this one instead (in bounds, fully masked, and already fetched by a
+// neighbouring lane), so every lane issues the same loads.
+__device__ __forceinline__ int64_t last_chunk(int64_t e) {
+  return e > 0 ? (e - 1) & ~(int64_t)7 : 0;
+}
+
 struct IdxChunk {
   u4 w;
-  __device__ __forceinline__ void load(const uint16_t* rowidx, int64_t p, int64_t nnz) {
-    if (p + 8 <= nnz) {
-      w = ld16<u4>(rowidx + p);
-    } else {
-      uint32_t t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int i = 0; i < 8; ++i)
-        if (p + i < nnz) t[i] = gptr(rowidx)[p + i];
-      w = u4{t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16)};
-    }
+  __device__ __forceinline__ void load(const uint16_t* rowidx, int64_t p) {
+    w = ld16<u4>(rowidx + p);
   }
   __device__ __forceinline__ uint32_t get(int i) const {
     return (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
@@ -34,16 +37,8 @@ struct ValChunk;
 template <>
 struct ValChunk<DFS_F16> {
   u4 w;
-  __device__ __forceinline__ void load(const void* vals, const uint8_t*, int64_t p, int64_t nnz) {
-    const uint16_t* v = (const uint16_t*)vals;
-    if (p + 8 <= nnz) {
-      w = ld16<u4>(v + p);
-    } else {
-      uint32_t t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int i = 0; i < 8; ++i)
-        if (p + i < nnz) t[i] = gptr(v)[p + i];
-      w = u4{t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16)};
-    }
+  __device__ __forceinline__ void load(const void* vals, const uint8_t*, int64_t p) {
+    w = ld16<u4>((const uint16_t*)vals + p);
   }
   __device__ __forceinline__ float get(int i) const {
     const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
@@ -54,18 +49,10 @@ struct ValChunk<DFS_F16> {
 template <>
 struct ValChunk<DFS_F32> {
   u4 w0, w1;
-  __device__ __forceinline__ void load(const void* vals, const uint8_t*, int64_t p, int64_t nnz) {
+  __device__ __forceinline__ void load(const void* vals, const uint8_t*, int64_t p) {
     const uint32_t* v = (const uint32_t*)vals;
-    if (p + 8 <= nnz) {
-      w0 = ld16<u4>(v + p);
-      w1 = ld16<u4>(v + p + 4);
-    } else {
-      uint32_t t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int i = 0; i < 8; ++i)
-        if (p + i < nnz) t[i] = gptr(v)[p + i];
-      w0 = u4{t[0], t[1], t[2], t[3]};
-      w1 = u4{t[4], t[5], t[6], t[7]};
-    }
+    w0 = ld16<u4>(v + p);
+    w1 = ld16<u4>(v + p + 4);
   }
   __device__ __forceinline__ float get(int i) const {
     return __uint_as_float(i < 4 ? w0[i] : w1[i - 4]);
@@ -79,16 +66,8 @@ template <>
 struct ValChunk<DFS_NVFP4> {
   uint32_t word;
   float s;
-  __device__ __forceinline__ void load(const void* vals, const uint8_t* scales, int64_t p,
-                                       int64_t nnz) {
-    const uint8_t* codes = (const uint8_t*)vals;
-    if (p + 8 <= nnz) {
-      word = *gptr(reinterpret_cast<const uint32_t*>(codes + p / 2));
-    } else {
-      word = 0;
-      for (int i = 0; i < 8; i += 2)
-        if (p + i < nnz) word |= (uint32_t)gptr(codes)[(p + i) / 2] << (4 * i);
-    }
+  __device__ __forceinline__ void load(const void* vals, const uint8_t* scales, int64_t p) {
+    word = *gptr(reinterpret_cast<const uint32_t*>((const uint8_t*)vals + p / 2));
     s = e4m3_to_f32(gptr(scales)[p / 16]);
   }
   // i is a compile-time constant after unrolling, so the switch folds away.

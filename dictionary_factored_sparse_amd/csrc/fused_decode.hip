@@ -322,16 +322,17 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     const int s0 = min(max(s_raw, 0), nz);
     cse[tid] = make_int2(s0, min(max(e_raw, s0), nz));
   }
+  // every lane issues the same loads: past its column it reloads the
+  // column's last chunk (masked when consumed)
   auto load_chunks = [&](IdxChunk* ic, ValChunk<VT>* vc, int s0, int e0, const uint16_t* rowidx,
-                         const void* vals, const uint8_t* vsc, int64_t nnz) {
+                         const void* vals, const uint8_t* vsc) {
     const int p0 = (s0 & ~7) + g * 8;
+    const int64_t lastc = last_chunk(e0);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int p = p0 + 128 * u;
-      if (p < e0) {
-        ic[u].load(rowidx, p, nnz);
-        vc[u].load(vals, vsc, p, nnz);
-      }
+      const int64_t p = min<int64_t>(p0 + 128 * u, lastc);
+      ic[u].load(rowidx, p);
+      vc[u].load(vals, vsc, p);
     }
   };
   IdxChunk ia[kU], ib[kU];
@@ -355,16 +356,16 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     const int s0 = live ? (int)min<int64_t>(max(rs_raw[r], 0), nnz) : 0;
     const int e0 = live ? (int)min<int64_t>(max(re_raw[r], s0), nnz) : 0;
     if (r == 0)
-      load_chunks(ia, va, s0, e0, rowidx, vals, vsc, nnz);
-    else
-      load_chunks(ib, vb, s0, e0, rowidx, vals, vsc, nnz);
+      load_chunks(ia, va, s0, e0, rowidx, vals, vsc);
+    else if (rounds > 1)
+      load_chunks(ib, vb, s0, e0, rowidx, vals, vsc);
   }
   auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
     const int ci = r * kSlots + slot;
     if (ci < ncols) {
       const int2 se = cse[ci];
       const LayerRow& L = lt[(c0 + ci) / d_out];
-      load_chunks(ic, vc, se.x, se.y, L.rowidx, L.vals, L.vsc, L.nnz);
+      load_chunks(ic, vc, se.x, se.y, L.rowidx, L.vals, L.vsc);
     }
   };
 
@@ -400,12 +401,13 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
       while (p0 < e) {
         IdxChunk tc[kU];
         ValChunk<VT> tv[kU];
+        const int64_t lastc = last_chunk(e);
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-          if (p0 + 128 * u < e) {
-            tc[u].load(L.rowidx, p0 + 128 * u, L.nnz);
-            tv[u].load(L.vals, L.vsc, p0 + 128 * u, L.nnz);
-          }
+        for (int u = 0; u < kU; ++u) {
+          const int64_t pc = min<int64_t>(p0 + 128 * u, lastc);
+          tc[u].load(L.rowidx, pc);
+          tv[u].load(L.vals, L.vsc, pc);
+        }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
           sum = gather_chunk<VT>(zl, tc[u], tv[u], p0 + 128 * u, s, e, sum);

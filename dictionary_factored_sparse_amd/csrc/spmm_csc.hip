@@ -5,136 +5,190 @@
 // VALU: the coefficients are unstructured, so the work is a gather-FMA over
 // each column's stored entries, not a dense contraction.
 //
-// Mapping: a workgroup owns a tile of TT tokens and a block of CB output
-// columns.  It stages the tile's Z (TT x k) into LDS once as f16 [k][TT],
-// with the 4-token quads of each atom row XOR-swizzled by the atom index so
-// that staging writes spread over the banks.  A lane owns 4 consecutive
-// tokens; TT/4 lanes share one column and read the same 8-entry C chunks
-// (broadcast loads), so a wave works on 64/(TT/4) columns at once.  Per stored
-// entry a lane does one 8-byte LDS read and four fp32 FMAs.  The next batch of
-// C chunks is loaded before the current one is consumed.
-// grid = (ceil(d_out / CB), ceil(T / TT), n_layers).
+// Mapping: a workgroup owns a tile of TT tokens and a block of output
+// columns, LPC lanes per column, each lane NT = TT / LPC of the tokens (at
+// most 16, which bounds the registers).  It stages the tile's Z into LDS
+// once as f16 [k + 1][TT] (row k is zero: masked entries point there).  For
+// every stored entry (r, v) of its column a lane reads its NT tokens of Z
+// row r (NT * 2 contiguous bytes) and does NT fused multiply-adds, f16 times
+// f32 into f32 (v_fma_mix), so a C entry fetched once serves the whole tile.
+// Chunks of 8 entries are loaded kU at a time, double-buffered, every lane
+// issuing the same loads (past its column it reloads the column's last
+// chunk, masked), so the compiler can wait for exactly the batch it needs.
+// Costs per MAC: one VALU op and 2 bytes of LDS.
+// grid = (ceil(d_out / (kThreads / LPC)), ceil(T / TT), n_layers).
 #include "csc_chunks.hpp"
 
 namespace dfs {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kCB = 256;  // columns per workgroup
-constexpr int kU = 4;     // 8-entry chunks per batch
+constexpr int kThreads = 512;
+// 8-entry chunks per batch (NVFP4 decodes on use and needs the registers)
+template <int VT>
+constexpr int kUnroll = VT == DFS_NVFP4 ? 2 : 4;
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
-// Byte offset of token quad `tq` of atom `a` in the [k][TT] f16 tile.
-template <int TT>
-__device__ __forceinline__ int zoff(int a, int tq) {
-  constexpr int NQ = TT / 4;
-  return a * (TT * 2) + ((tq ^ ((a >> 2) & (NQ - 1))) * 8);
+// NT f16 tokens of one Z row, read from LDS in 16-byte pieces (8 bytes for
+// NT = 4); `row` points at the lane's first token of the row.
+template <int NT>
+struct ZRow {
+  h8 v[NT / 8];
+  __device__ __forceinline__ void read(const _Float16* row) {
+    const h8* p = reinterpret_cast<const h8*>(row);
+#pragma unroll
+    for (int j = 0; j < NT / 8; ++j) v[j] = p[j];
+  }
+  __device__ __forceinline__ float get(int t) const { return (float)v[t / 8][t % 8]; }
+};
+template <>
+struct ZRow<4> {
+  h4 v;
+  __device__ __forceinline__ void read(const _Float16* row) {
+    v = *reinterpret_cast<const h4*>(row);
+  }
+  __device__ __forceinline__ float get(int t) const { return (float)v[t]; }
+};
+
+// Stage Z rows [row0, row0 + rows) (tokens) into the f16 tile [k + 1][TT].
+// Thread (token t, atom group) converts 8 atoms of token t per step: one
+// 16-byte load (32 for f32 Z) when k % 8 == 0, elementwise otherwise.
+template <int ZT, int TT>
+__device__ __forceinline__ void stage_z(_Float16* zt, const void* Z, int64_t row0, int rows,
+                                        int k) {
+  constexpr int kGroups = kThreads / TT;
+  const int t = threadIdx.x % TT;
+  const bool live = t < rows;
+  const int64_t zrow = (row0 + (live ? t : 0)) * k;
+  if (k % 8 == 0) {
+    for (int a0 = (threadIdx.x / TT) * 8; a0 < k; a0 += kGroups * 8) {
+      float v[8];
+      if constexpr (ZT == DFS_F32) {
+        const u4 w0 = ld16<u4>((const float*)Z + zrow + a0);
+        const u4 w1 = ld16<u4>((const float*)Z + zrow + a0 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = __uint_as_float(w0[i]);
+          v[4 + i] = __uint_as_float(w1[i]);
+        }
+      } else {
+        const h8 h = __builtin_bit_cast(h8, ld16<u4>((const _Float16*)Z + zrow + a0));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zt[(a0 + i) * TT + t] = live ? (_Float16)v[i] : (_Float16)0.0f;
+    }
+  } else {
+    for (int a0 = (threadIdx.x / TT) * 8; a0 < k; a0 += kGroups * 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (a0 + i < k) {
+          const float v = ZT == DFS_F32 ? ((const float*)Z)[zrow + a0 + i]
+                                        : (float)((const _Float16*)Z)[zrow + a0 + i];
+          zt[(a0 + i) * TT + t] = live ? (_Float16)v : (_Float16)0.0f;
+        }
+      }
+    }
+  }
+  for (int i = threadIdx.x; i < TT; i += kThreads) zt[k * TT + i] = (_Float16)0.0f;
 }
+
+template <int TT>
+struct Split {
+  static constexpr int LPC = TT > 16 ? TT / 16 : 1;  // lanes per column
+  static constexpr int NT = TT / LPC;                // tokens per lane
+  static constexpr int CPB = kThreads / LPC;         // columns per workgroup
+};
 
 template <int VT, int ZT, int TT>
 __global__ __launch_bounds__(kThreads) void spmm_csc_kernel(ZcLaunch a) {
-  constexpr int LPC = TT / 4;        // lanes per column
-  constexpr int CPW = kWave / LPC;   // columns per wave at once
+  constexpr int LPC = Split<TT>::LPC, NT = Split<TT>::NT, CPB = Split<TT>::CPB;
+  constexpr int kU = kUnroll<VT>;
   extern __shared__ __attribute__((aligned(16))) char zraw[];
+  _Float16* zt = reinterpret_cast<_Float16*>(zraw);
 
   const int layer = blockIdx.z;
   const int t0 = blockIdx.y * TT;
   const int k = a.k;
   const int rows = a.T - t0 < TT ? a.T - t0 : TT;
-  const int64_t zrow0 = (int64_t)layer * a.T + t0;
-
-  // ---- stage Z tile: thread (atom a, quad tq) gathers 4 tokens
-  for (int idx = threadIdx.x; idx < k * LPC; idx += kThreads) {
-    const int at = idx % k, tq = idx / k;
-    h4 q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = tq * 4 + i;
-      float v = 0.0f;
-      if (t < rows) {
-        const int64_t gi = (zrow0 + t) * k + at;
-        v = ZT == DFS_F32 ? ((const float*)a.Z)[gi] : (float)((const _Float16*)a.Z)[gi];
-      }
-      q[i] = (_Float16)v;
-    }
-    *reinterpret_cast<h4*>(zraw + zoff<TT>(at, tq)) = q;
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int cg = lane / LPC, sub = lane % LPC;
+  const int sub = threadIdx.x % LPC;  // this lane's tokens: sub * NT ...
+  const int col = blockIdx.x * CPB + threadIdx.x / LPC;
+  const bool col_ok = col < a.d_out;
   const int64_t nnz = a.nnz[layer];
+  int s = 0, e = 0;
+  if (col_ok) {  // clamped to [0, nnz] like the SpMV
+    s = (int)min<int64_t>(max(a.colptr[layer][col], 0), nnz);
+    e = (int)min<int64_t>(max(a.colptr[layer][col + 1], s), nnz);
+  }
   const uint16_t* rowidx = a.rowidx[layer];
   const void* vals = a.vals[layer];
   const uint8_t* vsc = a.vscales[layer];
-  float ts = 1.0f;
-  if constexpr (VT == DFS_NVFP4) ts = *a.vts[layer];
-  const int cend = min(a.d_out, (blockIdx.x + 1) * kCB);
+  const int64_t lastc = last_chunk(e);
 
-  for (int cbase = blockIdx.x * kCB; cbase < cend; cbase += kWaves * CPW) {
-    const int col = cbase + wave * CPW + cg;
-    int s = 0, e = 0;
-    if (col < cend) {  // clamped to [0, nnz] like the SpMV
-      s = (int)min<int64_t>(max(a.colptr[layer][col], 0), nnz);
-      e = (int)min<int64_t>(max(a.colptr[layer][col + 1], s), nnz);
+  IdxChunk ia[kU], ib[kU];
+  ValChunk<VT> va[kU], vb[kU];
+  auto load = [&](IdxChunk* ic, ValChunk<VT>* vc, int p) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t pc = min<int64_t>(p + 8 * u, lastc);
+      ic[u].load(rowidx, pc);
+      vc[u].load(vals, vsc, pc);
     }
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    IdxChunk ia[kU], ib[kU];
-    ValChunk<VT> va[kU], vb[kU];
-    auto load = [&](IdxChunk* ic, ValChunk<VT>* vc, int p) {
+  };
+  // the first batch does not depend on Z: in flight while the tile is staged
+  int p = s & ~7;
+  load(ia, va, p);
+  stage_z<ZT, TT>(zt, a.Z, (int64_t)layer * a.T + t0, rows, k);
+  __syncthreads();
+
+  float acc[NT];
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (p + 8 * u < e) {
-          ic[u].load(rowidx, p + 8 * u, nnz);
-          vc[u].load(vals, vsc, p + 8 * u, nnz);
-        }
-    };
-    const uint32_t len = (uint32_t)(e - s);
-    auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int p) {
+  for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+  const _Float16* zl = zt + sub * NT;
+  const uint32_t len = (uint32_t)(e - s);
+  auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int pb) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        // entries outside [s, e) are masked without a branch (atom 0, zero
-        // product) so that the LDS gathers of a chunk issue back to back
-        const int base = p + 8 * u - s;
+    for (int u = 0; u < kU; ++u) {
+      const int base = pb + 8 * u - s;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bool ok = (uint32_t)(base + i) < len;
-          const int r = ok ? (int)ic[u].get(i) : 0;
-          const float v = vc[u].get(i);
-          const h4 z = *reinterpret_cast<const h4*>(zraw + zoff<TT>(r, sub));
+      for (int i = 0; i < 8; ++i) {
+        // entries outside [s, e) read the zero row with a zero value
+        const bool ok = (uint32_t)(base + i) < len;
+        const uint32_t r = ok ? ic[u].get(i) : (uint32_t)k;
+        const float v = ok ? vc[u].get(i) : 0.0f;
+        ZRow<NT> z;
+        z.read(zl + r * TT);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[t] += ok ? (float)z[t] * v : 0.0f;
-        }
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(z.get(t), v, acc[t]);
       }
-    };
-    // two register buffers with static names, alternating: the loads of the
-    // next batch are in flight while the current one is consumed
-    int p = s & ~7;
-    load(ia, va, p);
-    while (p < e) {
-      load(ib, vb, p + 8 * kU);
-      consume(ia, va, p);
-      p += 8 * kU;
-      if (p >= e) break;
-      load(ia, va, p + 8 * kU);
-      consume(ib, vb, p);
-      p += 8 * kU;
     }
-    if (col < cend) {
+  };
+  // two register buffers with static names, alternating: the next batch is
+  // in flight while the current one is consumed
+  while (p < e) {
+    load(ib, vb, p + 8 * kU);
+    consume(ia, va, p);
+    p += 8 * kU;
+    if (p >= e) break;
+    load(ia, va, p + 8 * kU);
+    consume(ib, vb, p);
+    p += 8 * kU;
+  }
+
+  if (col_ok) {
+    float ts = 1.0f;
+    if constexpr (VT == DFS_NVFP4) ts = *a.vts[layer];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = sub * 4 + i;
-        if (t < rows) {
-          const int64_t o = (int64_t)(t0 + t) * a.ldy + col;
-          const float out = acc[i] * ts;
-          if (a.ydt == DFS_F16)
-            ((_Float16*)a.Y[layer])[o] = (_Float16)out;
-          else
-            ((float*)a.Y[layer])[o] = out;
-        }
+    for (int i = 0; i < NT; ++i) {
+      const int t = sub * NT + i;
+      if (t < rows) {
+        const int64_t o = (int64_t)(t0 + t) * a.ldy + col;
+        const float out = acc[i] * ts;
+        if (a.ydt == DFS_F16)
+          ((_Float16*)a.Y[layer])[o] = (_Float16)out;
+        else
+          ((float*)a.Y[layer])[o] = out;
       }
     }
   }
@@ -142,14 +196,15 @@ __global__ __launch_bounds__(kThreads) void spmm_csc_kernel(ZcLaunch a) {
 
 template <int VT, int ZT, int TT>
 hipError_t launch3(const ZcLaunch& a, hipStream_t s) {
-  const size_t smem = (size_t)a.k * TT * 2;
+  const size_t smem = (size_t)(a.k + 1) * TT * 2;
   auto kern = spmm_csc_kernel<VT, ZT, TT>;
   if (smem > 64 * 1024) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess) return err;
   }
-  dim3 grid((a.d_out + kCB - 1) / kCB, (a.T + TT - 1) / TT, a.n_layers);
+  constexpr int CPB = Split<TT>::CPB;
+  dim3 grid((a.d_out + CPB - 1) / CPB, (a.T + TT - 1) / TT, a.n_layers);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
   return hipGetLastError();
 }
@@ -175,10 +230,11 @@ hipError_t launch1(const ZcLaunch& a, hipStream_t s) {
 
 }  // namespace
 
-// Largest token tile (32, 16, 8 or 4) whose f16 Z tile fits in 128 KiB.
+// Largest token tile (32, 16, 8 or 4) whose f16 Z tile [k + 1][TT] fits in
+// 144 KiB of LDS (k <= 16384 always fits at TT = 4).
 int spmm_token_tile(int k) {
   int tt = 32;
-  while (tt > 4 && (size_t)k * tt * 2 > 128 * 1024) tt /= 2;
+  while (tt > 4 && (size_t)(k + 1) * tt * 2 > 144 * 1024) tt /= 2;
   return tt;
 }
 

@@ -9,9 +9,10 @@
 //
 // Mapping: a workgroup is 4 waves; each wave serves 4 columns at once, one
 // per 16-lane DPP row.  Lane g of a row reads the 8-entry chunks g, g+16, ...
-// of its column (128 entries per step), U steps in flight per batch.  The
-// first batch is issued before Z is staged into LDS (C does not depend on
-// Z).  The Z tile is [k][TT] fp32 (TT tokens per pass); the partial sums are
+// of its column (128 entries per step), U steps in flight per batch, every
+// lane issuing the same loads (past its column it reloads the last chunk of
+// the arrays, masked).  The first batch is issued before Z is staged into
+// LDS (C does not depend on Z).  The Z tile is [k][TT] fp32 (TT tokens per pass); the partial sums are
 // reduced over the 16 lanes of the row with DPP, in a fixed order.
 // grid = (ceil(d_out / 16), n_layers); one launch covers a whole group.
 #include "csc_chunks.hpp"
@@ -24,10 +25,11 @@ constexpr int kColsPerBlock = 16;  // 4 waves x 4 DPP rows
 
 // 8-entry chunks in flight per lane per batch: with 16 lanes per column a
 // batch covers 128 * U entries, enough for a whole column at the densities of
-// the decode workloads (mean 410-615 stored entries per column).
-template <int VT>
+// the decode workloads (mean 410-615 stored entries per column).  Wide token
+// tiles keep fewer chunks so that the accumulators and Z reads fit.
+template <int VT, int TT>
 struct Unroll {
-  static constexpr int U = VT == DFS_F32 ? 3 : 6;
+  static constexpr int U = TT >= 16 ? 1 : TT >= 8 ? 2 : TT >= 4 ? 4 : (VT == DFS_F32 ? 3 : 6);
 };
 
 // Z rows [row0, row0 + rows) -> LDS [k][TT] fp32 (zero rows past `rows`).
@@ -92,7 +94,7 @@ __device__ __forceinline__ void stage_z(float* zs, const void* Z, int64_t row0, 
 
 template <int VT, int ZT, int TT>
 __global__ __launch_bounds__(kThreads) void spmv_csc_kernel(ZcLaunch a) {
-  constexpr int U = Unroll<VT>::U;
+  constexpr int U = Unroll<VT, TT>::U;
   extern __shared__ __attribute__((aligned(16))) float zs[];  // [k][TT]
 
   const int layer = blockIdx.y;
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void spmv_csc_kernel(ZcLaunch a) {
   const void* vals = a.vals[layer];
   const uint8_t* vsc = a.vscales[layer];
   const int first = (s & ~7) + g * 8;
+  const int64_t lastc = last_chunk(e);
   float ts = 1.0f;
   if constexpr (VT == DFS_NVFP4) ts = *a.vts[layer];
 
@@ -120,11 +123,9 @@ __global__ __launch_bounds__(kThreads) void spmv_csc_kernel(ZcLaunch a) {
     int p0 = first;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int p = p0 + 128 * u;
-      if (p < e) {
-        ic[u].load(rowidx, p, nnz);
-        vc[u].load(vals, vsc, p, nnz);
-      }
+      const int64_t p = min<int64_t>(p0 + 128 * u, lastc);
+      ic[u].load(rowidx, p);
+      vc[u].load(vals, vsc, p);
     }
     if (t0 > 0) __syncthreads();
     const int rows = a.T - t0 < TT ? a.T - t0 : TT;
@@ -163,11 +164,9 @@ __global__ __launch_bounds__(kThreads) void spmv_csc_kernel(ZcLaunch a) {
       if (p0 < e) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int p = p0 + 128 * u;
-          if (p < e) {
-            ic[u].load(rowidx, p, nnz);
-            vc[u].load(vals, vsc, p, nnz);
-          }
+          const int64_t p = min<int64_t>(p0 + 128 * u, lastc);
+          ic[u].load(rowidx, p);
+          vc[u].load(vals, vsc, p);
         }
       }
     }

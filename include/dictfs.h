@@ -91,7 +91,12 @@ typedef struct {
  *   rowidx[nnz] uint16 atom indices, strictly increasing within a column;
  *   values in CSC order: `vals` (F16/F32) or `nv` (NVFP4, blocks of 16 run
  *   over the flat CSC value array and may straddle column boundaries).
- * k <= 65536 (16-bit indices), nnz < 2^31. */
+ * k <= 65536 (16-bit indices), nnz < 2^31.
+ * Padding: the forward kernels read rowidx and the values in aligned chunks
+ * of 8 entries, so rowidx and vals must be allocated for
+ * dict_csc_capacity(nnz) entries (NVFP4 codes: half that many bytes; block
+ * scales: ceil(nnz / 16) bytes).  Entries past nnz are never used and may
+ * hold anything.  The caller owns all arrays. */
 typedef struct {
   int32_t k;
   int32_t d_out;
@@ -108,6 +113,11 @@ typedef struct {
 /* Packing                                                                */
 /* ---------------------------------------------------------------------- */
 
+/* Entries that rowidx and vals must be allocated for when a CSC with nnz
+ * stored entries is passed to a forward call: nnz rounded up to a multiple
+ * of 8, at least 8 (negative nnz gives 8). */
+int64_t dict_csc_capacity(int64_t nnz);
+
 /* Workspace bytes dict_pack_csc needs for a k x d_out matrix. */
 dfs_status dict_pack_csc_workspace_size(int32_t k, int32_t d_out, size_t* bytes);
 
@@ -119,8 +129,9 @@ dfs_status dict_pack_csc_workspace_size(int32_t k, int32_t d_out, size_t* bytes)
  * ("DictLLM: Shared Dictionaries for Post-Training Compression", Algorithm 2:
  * export of dictionary, codes, scales and support, zeros preserved).
  *   rowidx == NULL and vals == NULL: fill colptr[d_out+1] and *nnz_host only.
- *   otherwise: fill colptr, rowidx, vals; capacity (elements of rowidx/vals)
- *   < nnz gives DFS_E_RANGE with colptr written and rowidx/vals untouched.
+ *   otherwise: fill colptr, rowidx[0..nnz), vals[0..nnz); capacity (elements
+ *   of rowidx/vals) < dict_csc_capacity(nnz) gives DFS_E_RANGE with colptr
+ *   written and rowidx/vals untouched.
  * Synchronises `stream` to return *nnz_host (host pointer, required). */
 dfs_status dict_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out, int64_t ldc,
                          int32_t* colptr, uint16_t* rowidx, void* vals, int64_t capacity,

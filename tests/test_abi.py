@@ -23,7 +23,8 @@ P = 0x10000  # 16-byte aligned placeholder address, never dereferenced
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"^\s*(?:dfs_status|const char\*|int32_t)\s+(\w+)\s*\(", src, re.M))
+    return set(re.findall(r"^\s*(?:dfs_status|const char\*|int32_t|int64_t)\s+(\w+)\s*\(", src,
+                          re.M))
 
 
 def test_header_declares_the_north_star_calls():
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert fns == set(B.SYMBOLS)
     for name in fns:
         assert hasattr(L, name), name
-    assert L.dfs_version() == 100
+    assert L.dfs_version() == 200
     assert L.dfs_status_str(0) == b"ok"
     assert L.dfs_status_str(6) == b"HIP runtime error"
 
@@ -164,3 +165,10 @@ def test_workspace_sizes():
     assert L.dict_xd_workspace_size(1, 2048, C.byref(Dn), C.byref(n)) == OK
     assert n.value >= 4096 * 2048 * 2      # f16 expansion for the MFMA path
     assert L.dict_xd_workspace_size(1, 1, C.byref(Dn), C.byref(n)) == OK and n.value == 0
+
+
+def test_csc_capacity_is_whole_chunks():
+    L = B.lib()
+    for nnz, cap in ((-1, 8), (0, 8), (1, 8), (7, 8), (8, 8), (9, 16), (2516386, 2516392),
+                     ((1 << 31) - 1, 1 << 31)):
+        assert L.dict_csc_capacity(nnz) == cap, nnz
