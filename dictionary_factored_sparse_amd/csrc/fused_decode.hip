@@ -57,6 +57,7 @@ struct LayerRow {
 // continues, so the kernel always terminates.
 constexpr int kCtrlErr = 32, kCtrlEpochs = 256;  // in 32-bit words
 
+
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -241,28 +242,27 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     if (cl == i) cp = sreg_ptr(f.colptr[i]);
   const int s_raw = gptr(cp)[cj], e_raw = gptr(cp)[cj + 1];
 
-  // ---- 3. this workgroup's atoms of D_g (an out-of-range chunk loads
-  // element 0 and is zeroed)
+  // ---- 3. this workgroup's atoms of D_g.  Out-of-range reads are clamped,
+  // not masked: an atom past k reads atom k - 1 (its Z is never published),
+  // a chunk past d_in reads the atom's last chunk and meets the zero padding
+  // of X, so it adds 0 (or propagates a non-finite value of that same atom).
   const int atom0 = (blockIdx.x * kFW + wave) * A;
   u4 dreg[A][SEGC];
   uint32_t sreg[A][SEGC];
   auto load_d = [&](int seg) {
 #pragma unroll
     for (int i = 0; i < A; ++i) {
-      const int atom = atom0 + i;
+      const int atom = min(atom0 + i, k - 1);
 #pragma unroll
       for (int c = 0; c < SEGC; ++c) {
-        const int e0 = seg + (c * kWave + lane) * CE;
-        const bool ok = atom < k && e0 < d_in;
+        const int e0 = min(seg + (c * kWave + lane) * CE, d_in - CE);
         if constexpr (DT == DFS_NVFP4) {
-          const int64_t el = ok ? (int64_t)atom * d_in + e0 : 0;
-          const u4 v = ld16<u4>((const uint8_t*)f.D + el / 2);
-          const uint32_t s0 = gptr(f.dscales)[el / 16], s1 = gptr(f.dscales)[el / 16 + 1];
-          dreg[i][c] = ok ? v : u4{0u, 0u, 0u, 0u};
-          sreg[i][c] = ok ? (s0 | (s1 << 8)) : 0u;
+          const int64_t el = (int64_t)atom * d_in + e0;
+          dreg[i][c] = ld16<u4>((const uint8_t*)f.D + el / 2);
+          sreg[i][c] = (uint32_t)gptr(f.dscales)[el / 16] |
+                       ((uint32_t)gptr(f.dscales)[el / 16 + 1] << 8);
         } else {
-          const u4 v = ld16<u4>((const _Float16*)f.D + (ok ? (int64_t)atom * f.ldd + e0 : 0));
-          dreg[i][c] = ok ? v : u4{0u, 0u, 0u, 0u};
+          dreg[i][c] = ld16<u4>((const _Float16*)f.D + (int64_t)atom * f.ldd + e0);
           sreg[i][c] = 0u;
         }
       }
@@ -322,17 +322,20 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     const int s0 = min(max(s_raw, 0), nz);
     cse[tid] = make_int2(s0, min(max(e_raw, s0), nz));
   }
-  // every lane issues the same loads: past its column it reloads the
-  // column's last chunk (masked when consumed)
+  // A lane loads only the chunks inside its column: here nothing waits for
+  // an exact count of these loads (the Z polls issued after them wait for
+  // all of them), and skipping the lanes past the column's end saves their
+  // share of the memory pipeline.
   auto load_chunks = [&](IdxChunk* ic, ValChunk<VT>* vc, int s0, int e0, const uint16_t* rowidx,
                          const void* vals, const uint8_t* vsc) {
     const int p0 = (s0 & ~7) + g * 8;
-    const int64_t lastc = last_chunk(e0);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t p = min<int64_t>(p0 + 128 * u, lastc);
-      ic[u].load(rowidx, p);
-      vc[u].load(vals, vsc, p);
+      const int p = p0 + 128 * u;
+      if (p < e0) {
+        ic[u].load(rowidx, p);
+        vc[u].load(vals, vsc, p);
+      }
     }
   };
   IdxChunk ia[kU], ib[kU];
@@ -401,13 +404,12 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
       while (p0 < e) {
         IdxChunk tc[kU];
         ValChunk<VT> tv[kU];
-        const int64_t lastc = last_chunk(e);
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int64_t pc = min<int64_t>(p0 + 128 * u, lastc);
-          tc[u].load(L.rowidx, pc);
-          tv[u].load(L.vals, L.vsc, pc);
-        }
+        for (int u = 0; u < kU; ++u)
+          if (p0 + 128 * u < e) {
+            tc[u].load(L.rowidx, p0 + 128 * u);
+            tv[u].load(L.vals, L.vsc, p0 + 128 * u);
+          }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
           sum = gather_chunk<VT>(zl, tc[u], tv[u], p0 + 128 * u, s, e, sum);
