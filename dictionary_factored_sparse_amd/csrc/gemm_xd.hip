@@ -11,112 +11,231 @@
 // atom-major (each of the N = k atoms has its K elements contiguous), f16
 // operands, fp32 accumulation in v_mfma_f32_32x32x16_f16.
 //
-// Tiling: 128 x 128 output tile per workgroup of 4 waves (2 x 2), each wave
-// 64 x 64 = 2 x 2 MFMA blocks; K advances 64 at a time through two LDS
-// buffers (rows padded by 16 bytes so the 16-byte fragment reads of 16
-// consecutive rows fall in distinct banks).  The next K tile is fetched into
-// registers while the current one is multiplied.
+// Tiling: a 256 x 128 output tile per workgroup of 4 waves (2 x 2), each
+// wave 128 x 64 = 4 x 2 MFMA blocks of 32 x 32, so that one 16-wide slice of
+// K costs a wave 6 fragment reads from LDS for 8 MFMAs.  K advances 64 at a
+// time through three LDS stages filled straight from global memory
+// (global_load_lds_dwordx4: each wave instruction writes 1 KiB = 8 tile rows
+// of 128 bytes), so two K tiles are in flight while one is multiplied and
+// no registers stage the operands.  Rows are unpadded; the eight 16-byte
+// chunks of a row are stored in an XOR-swizzled slot order (see swz) that
+// keeps the fragment reads free of bank conflicts.  Rows past M or N
+// read a valid row and are never stored; a K tail (K % 64 != 0, K % 8 == 0)
+// is zeroed in LDS after its loads land.  One workgroup per CU; tiles are
+// numbered so that the workgroups that share an XCD (dispatch is
+// round-robin over the 8 XCDs) cover a compact 4 x 8 block of tiles and so
+// share A and B panels in their L2.
 #include "dfs_internal.hpp"
 
 namespace dfs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;               // padded row length (halfs)
-constexpr int kChunks = BM * BK / 8;      // 16-byte chunks per operand tile
-constexpr int kPerThread = kChunks / kThreads;
+constexpr int kWavesG = kThreads / kWave;
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int kRowBytes = BK * 2;                        // 128
+constexpr int kStages = 3;
+constexpr int kStageBytes = (BM + BN) * kRowBytes;       // 48 KiB
+constexpr int kAInst = BM * kRowBytes / 1024 / kWavesG;  // 1 KiB loads per wave per stage (A)
+constexpr int kBInst = BN * kRowBytes / 1024 / kWavesG;  // (B)
+constexpr int kLoadsPerStage = kAInst + kBInst;          // 12
+constexpr int MI = 4, NJ = 2;                            // 32 x 32 blocks per wave
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;
+constexpr size_t kSmemBytes = (size_t)kStages * kStageBytes;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): wait until at most n vector memory ops are pending
+// (and every LDS op has completed).
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Workgroup barrier without the release/acquire fences of __syncthreads:
+// those would wait for every vector memory op, i.e. for the K tiles still
+// in flight.  The waits the pipeline needs are issued explicitly before it
+// (the compiler does not track the LDS writes of global_load_lds), and the
+// memory clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Tile (mb, nb) of workgroup `bid`: workgroups bid = x, x + 8, x + 16, ...
+// run on XCD x, so consecutive positions of the tile order go to one XCD,
+// and the order walks groups of kGroupM m-tiles column by column.
+__device__ __forceinline__ void tile_of(int bid, int G, int MB, int NB, int* mb, int* nb) {
+  int t = bid;
+  if (G % kXcds == 0) t = (bid % kXcds) * (G / kXcds) + bid / kXcds;
+  const int per_group = kGroupM * NB;
+  const int g = t / per_group;
+  const int first = g * kGroupM;
+  const int gm = MB - first < kGroupM ? MB - first : kGroupM;
+  const int r = t - g * per_group;
+  *mb = first + r % gm;
+  *nb = r / gm;
+}
+
+// Slot of K chunk c of tile row r is c ^ swz(r).  A fragment read serves
+// 32 consecutive rows at one chunk; with swz(r) = (r >> 1) & 7 the rows that
+// share a bank window (every 2nd row in 8, every 4th row in 16) land in
+// distinct slots, so the reads are conflict-free whether the LDS serves 8 or
+// 16 lanes of a 16-byte read per clock.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef const __attribute__((address_space(1))) void* glob_ptr;
 
 template <int ZT>
-__global__ __launch_bounds__(kThreads) void gemm_xd_kernel(XdLaunch a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * LDK];
+__global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int M = a.n_layers * a.T, N = a.k, K = a.d_in;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int MB = (M + BM - 1) / BM, NB = (N + BN - 1) / BN;
+  int mb, nb;
+  tile_of(blockIdx.x, gridDim.x, MB, NB, &mb, &nb);
+  const int m0 = mb * BM, n0 = nb * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * (MI * 32), wn = (wave & 1) * (NJ * 32);
 
-  // Row pointers of the chunks this thread loads (fixed across K tiles).
-  const _Float16* arow[kPerThread];
-  const _Float16* brow[kPerThread];
-  int kc[kPerThread];
+  // Each load instruction fills 8 tile rows; lane j writes row rr = 8 * q +
+  // j / 8 (q = instruction index in the tile), LDS slot j % 8, and so reads
+  // the global chunk (j % 8) ^ swz(rr) of that row.
+  const _Float16* arow[kAInst];
+  const _Float16* brow[kBInst];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int c = tid + i * kThreads;
-    const int r = c / (BK / 8);
-    kc[i] = (c % (BK / 8)) * 8;
-    const int m = m0 + r;
-    arow[i] = nullptr;
-    if (m < M) {
-      const int l = m / a.T, t = m - l * a.T;
-      arow[i] = (const _Float16*)a.X[l] + (int64_t)t * a.ldx;
-    }
-    const int n = n0 + r;
-    brow[i] = n < N ? (const _Float16*)a.D + (int64_t)n * a.ldd : nullptr;
+  for (int i = 0; i < kAInst; ++i) {
+    const int m = min(m0 + 8 * (wave * kAInst + i) + (lane >> 3), M - 1);
+    const int l = m / a.T, t = m - l * a.T;
+    arow[i] = (const _Float16*)a.X[l] + (int64_t)t * a.ldx;
   }
-
-  u4 ra[kPerThread], rb[kPerThread];
-  auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int kk = k0 + kc[i];
-      ra[i] = (arow[i] && kk < K) ? ld16<u4>(arow[i] + kk) : u4{0u, 0u, 0u, 0u};
-      rb[i] = (brow[i] && kk < K) ? ld16<u4>(brow[i] + kk) : u4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < kBInst; ++i) {
+    const int n = min(n0 + 8 * (wave * kBInst + i) + (lane >> 3), N - 1);
+    brow[i] = (const _Float16*)a.D + (int64_t)n * a.ldd;
+  }
+  const int nk = (K + BK - 1) / BK;
+  // Loads of K tile kt into LDS stage kt % 3.  A chunk past K (only in a
+  // short last tile; K % 8 == 0 on this path) reads the row's last chunk and
+  // is zeroed once it has landed.
+  // K offset (elements) of this lane's chunk in load instruction q
+  auto chunk_of = [&](int q) { return ((lane & 7) ^ swz(8 * q + (lane >> 3))) * 8; };
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kAInst; ++i) {
+      const int q = wave * kAInst + i;
+      const int kk = min(kt * BK + chunk_of(q), K - 8);
+      __builtin_amdgcn_global_load_lds((glob_ptr)(arow[i] + kk), (lds_ptr)(st + q * 1024), 16, 0,
+                                       0);
+    }
+#pragma unroll
+    for (int i = 0; i < kBInst; ++i) {
+      const int q = wave * kBInst + i;
+      const int kk = min(kt * BK + chunk_of(q), K - 8);
+      __builtin_amdgcn_global_load_lds((glob_ptr)(brow[i] + kk),
+                                       (lds_ptr)(st + BM * kRowBytes + q * 1024), 16, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
+  auto zero_tail = [&](int kt) {
+    char* st = smem + (kt % kStages) * kStageBytes;
+    const u4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / (BK / 8);
-      *reinterpret_cast<u4*>(&As[buf][r * LDK + kc[i]]) = ra[i];
-      *reinterpret_cast<u4*>(&Bs[buf][r * LDK + kc[i]]) = rb[i];
+    for (int i = 0; i < kAInst; ++i) {
+      const int q = wave * kAInst + i;
+      if (kt * BK + chunk_of(q) >= K) *reinterpret_cast<u4*>(st + q * 1024 + lane * 16) = z;
+    }
+#pragma unroll
+    for (int i = 0; i < kBInst; ++i) {
+      const int q = wave * kBInst + i;
+      if (kt * BK + chunk_of(q) >= K)
+        *reinterpret_cast<u4*>(st + BM * kRowBytes + q * 1024 + lane * 16) = z;
     }
   };
 
-  f16v acc[2][2];
+  f16v acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  const int fr = lane & 31, fc = lane >> 5;
+  // Fragments of 16-wide K slice ks (lane: row fr of each 32-row block, K
+  // chunk 2 * ks + fc), read into one of two register sets so that the
+  // reads of slice ks + 1 overlap the MFMAs of slice ks.
+  auto frags = [&](const char* as, const char* bs, int ks, h8* fa, h8* fb) {
+    const int c = 2 * ks + fc;
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      h8 fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const h8*>(&As[cur][(wm + 32 * i + fr) * LDK + ks + fk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const h8*>(&Bs[cur][(wn + 32 * j + fr) * LDK + ks + fk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm + 32 * i + fr;
+      fa[i] = *reinterpret_cast<const h8*>(as + r * kRowBytes + ((c ^ swz(r)) * 16));
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = wn + 32 * j + fr;
+      fb[j] = *reinterpret_cast<const h8*>(bs + r * kRowBytes + ((c ^ swz(r)) * 16));
+    }
+  };
+  auto mma = [&](const h8* fa, const h8* fb) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  auto compute = [&](int buf) {
+    const char* as = smem + buf * kStageBytes;
+    const char* bs = as + BM * kRowBytes;
+    h8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
+    frags(as, bs, 0, fa0, fb0);
+    frags(as, bs, 1, fa1, fb1);
+    mma(fa0, fb0);
+    frags(as, bs, 2, fa0, fb0);
+    mma(fa1, fb1);
+    frags(as, bs, 3, fa1, fb1);
+    mma(fa0, fb0);
+    mma(fa1, fb1);
+    // Issue order for the scheduler: the reads of slices 0 and 1, then the
+    // MFMAs of slices 0 and 1 each paired with one read of slices 2 and 3,
+    // then the remaining MFMAs (masks: 0x100 LDS read, 0x008 MFMA).
+    constexpr int kReads = MI + NJ;  // fragment reads per slice
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReads, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int r = 0; r < kReads; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - kReads, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * NJ, 0);
+  };
+
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt have landed (stage kt + 1 may still be
+    // in flight); the barrier makes every wave's loads visible and frees
+    // the buffer of stage kt - 1 for stage kt + 2
+    if (kt + 1 < nk) {
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kLoadsPerStage));
+    } else {
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+      if (K % BK != 0) {
+        zero_tail(kt);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+      }
+    }
+    lds_barrier();
+    if (kt + 2 < nk) issue(kt + 2);
+    compute(kt % kStages);
   }
 
   // Accumulator layout of a 32 x 32 block: lane l holds column l % 32 and
   // rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int n = n0 + wn + 32 * j + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -149,16 +268,23 @@ __global__ __launch_bounds__(256) void nvfp4_to_f16_kernel(const uint8_t* codes,
   *reinterpret_cast<h8*>(out + i8) = o;
 }
 
+template <int ZT>
+hipError_t launch_z(const XdLaunch& a, hipStream_t s) {
+  auto kern = gemm_xd_kernel<ZT>;
+  hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kSmemBytes);
+  if (err != hipSuccess) return err;
+  const int M = a.n_layers * a.T;
+  const unsigned G = (unsigned)(((M + BM - 1) / BM) * ((a.k + BN - 1) / BN));
+  hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), kSmemBytes, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_xd_mfma(const XdLaunch& a, hipStream_t s) {
-  const int M = a.n_layers * a.T;
-  dim3 grid((a.k + BN - 1) / BN, (M + BM - 1) / BM);
-  if (a.zdt == DFS_F32)
-    hipLaunchKernelGGL(gemm_xd_kernel<DFS_F32>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(gemm_xd_kernel<DFS_F16>, grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return a.zdt == DFS_F32 ? launch_z<DFS_F32>(a, s) : launch_z<DFS_F16>(a, s);
 }
 
 // n must be a multiple of 8 (the caller checks d_in % 32 == 0).
