@@ -48,7 +48,7 @@ TRAFFIC_SOURCES = ("dictionary_factored_sparse_amd/csrc/fused_decode.hip",
                    "dictionary_factored_sparse_amd/csrc/gemv_common.hpp",
                    "dictionary_factored_sparse_amd/csrc/dfs_internal.hpp",
                    "include/dictfs.h")
-TRAFFIC_MEASURED = {"digest": "6d7cb0a258a82250e9bbd3d44d1d0ec23806055ef6143583404268b348dfbef1",
+TRAFFIC_MEASURED = {"digest": "2e98f688458283e07193ed90742086b2088b273808ef7f19fa3fd94b9f6917f0",
                     "fetch_kib": 18404.90, "write_kib": 152.0,
                     "fetch_scale": 1.99978, "write_scale": 1.0}
 
@@ -76,6 +76,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the MLP, NVFP4-stack and packer measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -260,6 +262,124 @@ def main():
             "group_forward_ms": round(res["group_forward"], 4),
         }
         _log(f"prefill: {extras['prefill_T2048_group2']}")
+
+    # ---------------------------------------------------------------- other decode workloads
+    # The MLP group of four layers (one dictionary per projection type) at
+    # b = 1 and b = 16, and the NVFP4 stack as projection time per token:
+    # every projection type's group timed once (all 16 groups of a type
+    # have the same shape and density), summed over the 16 groups.
+    def clone_nv(q):
+        return B.DeviceNVFP4(q.codes.clone(), q.scales.clone(), q.ts.clone(), q.n)
+
+    def clone_dict(d):
+        if d.nv is not None:
+            return B.DeviceDict(d.d_in, d.k, nv=clone_nv(d.nv))
+        return B.DeviceDict(d.d_in, d.k, data=d.data.clone())
+
+    def clone_csc(c):
+        if c.nv is not None:
+            return B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
+                               nv=clone_nv(c.nv))
+        return B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
+                           vals=c.vals.clone())
+
+    def time_group(gx, Ts, nvfp4):
+        """us per group forward at each T in Ts (inputs rotated over replicas
+        totalling > 1.2 GB), and algorithmic bytes per forward."""
+        Dd = B.to_device_dict(gx.D, dev, nvfp4=nvfp4)
+        Cd = [B.to_device_csc(c, dev, nvfp4=nvfp4) for c in gx.Cs]
+        nz = [c.nnz for c in Cd]
+        wdt = cdt = "nvfp4" if nvfp4 else "f16"
+        out = {}
+        for T in Ts:
+            nb = L.group_bytes(d_in=gx.d_in, d_out=gx.d_out, k=gx.k, T=T, nnzs=nz, wdtype=wdt,
+                               cdtype=cdt, xdtype="f16", ydtype="f16")
+            nrep = max(2, math.ceil(1.2e9 / nb))
+            rp = [(Dd, Cd)] + [(clone_dict(Dd), [clone_csc(c) for c in Cd]) for _ in range(nrep - 1)]
+            Xg = [torch.from_numpy(np.ascontiguousarray(X[:T])).to(dev) for X in gx.Xs]
+            Yg = [torch.empty(T, gx.d_out, dtype=torch.float16, device=dev) for _ in Xg]
+            wsg = B.workspace(len(Xg), T, Dd, Cd[0], dev)
+            nstep = 100 if T == 1 else 20
+            gr = capture(lambda i: B.dict_group_forward(Xg, rp[i % nrep][0], rp[i % nrep][1],
+                                                        Ys=Yg, ws=wsg), nstep)
+            gr.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            gr.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            assert B.workspace_error_word(wsg) == 0, "Z hand-off wait timed out"
+            us = ev0.elapsed_time(ev1) / nstep * 1e3
+            out[T] = (us, nb)
+            del rp, gr
+            torch.cuda.empty_cache()
+        return out
+
+    if not args.no_extras:
+        t1 = time.time()
+        mlp = {}
+        for ptype in ("gate", "down"):
+            gx = synth.make_group("mlp", ptype=ptype, T=16)
+            for T, (us, nb) in time_group(gx, (1, 16), False).items():
+                mlp[f"{ptype}_b{T}"] = {"us": round(us, 2), "MB": round(nb / 1e6, 2),
+                                        "GB/s": round(nb / us / 1e3, 1),
+                                        "frac_of_8TBs": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+            del gx
+        extras["mlp_group4_k3072_density0.20"] = mlp
+        _log(f"mlp groups: {mlp}")
+        stack, per_tok_us, per_tok_b = {}, 0.0, 0
+        for ptype, count in (("q", 4), ("gate", 2), ("down", 1)):
+            gx = synth.make_group("stack_nvfp4", ptype=ptype)
+            us, nb = time_group(gx, (1,), True)[1]
+            stack[ptype] = {"us_per_group": round(us, 2), "MB": round(nb / 1e6, 2),
+                            "GB/s": round(nb / us / 1e3, 1), "groups_per_token": 16 * count}
+            per_tok_us += 16 * count * us
+            per_tok_b += 16 * count * nb
+            del gx
+        stack["per_token_us"] = round(per_tok_us, 1)
+        stack["per_token_GB"] = round(per_tok_b / 1e9, 3)
+        stack["per_token_GB/s"] = round(per_tok_b / per_tok_us / 1e3, 1)
+        extras["stack_nvfp4_32_layers_per_token"] = stack
+        _log(f"nvfp4 stack: {stack}")
+
+        # packers (offline steps, timed for information): dense -> CSC of one
+        # q_proj C (2048 x 4096 f16), NVFP4 pack and unpack of one D_g
+        Cdense = torch.from_numpy(g.Cs[0]).to(dev)
+        B.dict_pack_csc(Cdense)
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        for _ in range(5):
+            B.dict_pack_csc(Cdense)
+        torch.cuda.synchronize()
+        pack_us = (time.perf_counter() - tp) / 5 * 1e6
+        xf = torch.from_numpy(g.D.astype(np.float32)).to(dev).reshape(-1)
+        q = B.nvfp4_pack(xf)
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        for _ in range(5):
+            q = B.nvfp4_pack(xf)
+        torch.cuda.synchronize()
+        nvp_us = (time.perf_counter() - tp) / 5 * 1e6
+        B.nvfp4_unpack(q)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(20):
+            B.nvfp4_unpack(q)
+        ev1.record()
+        torch.cuda.synchronize()
+        nvu_us = ev0.elapsed_time(ev1) / 20 * 1e3
+        n_el = xf.numel()
+        extras["packers"] = {
+            "dict_pack_csc_us": round(pack_us, 1),
+            "dict_pack_csc_entries_per_s": round(Cdense.numel() / pack_us * 1e6 / 1e9, 2),
+            "dict_pack_csc_note": "2048 x 4096 f16 dense -> CSC, count and fill calls with "
+                                  "their host synchronisations, wall clock",
+            "nvfp4_pack_us": round(nvp_us, 1),
+            "nvfp4_pack_GB/s_in": round(n_el * 4 / nvp_us / 1e3, 1),
+            "nvfp4_unpack_us": round(nvu_us, 1),
+            "nvfp4_unpack_GB/s_out": round(n_el * 4 / nvu_us / 1e3, 1),
+            "nvfp4_elements": n_el}
+        _log(f"packers: {extras['packers']} ({time.time() - t1:.0f} s of extras)")
 
     # ---------------------------------------------------------------- CPU baseline
     cpu = None

@@ -257,7 +257,7 @@ def workspace(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC, device) -> to
 
 def workspace_error_word(ws: torch.Tensor) -> int:
     """Word 32 of the control block: non-zero if a one-launch decode timed
-    out at its grid barrier (results of that call are invalid)."""
+    out waiting for a Z word (results of that call are invalid)."""
     return int(ws[128:132].view(torch.int32).item())
 
 

@@ -207,7 +207,7 @@ bool fused_allowed() {
   return !(v && std::strcmp(v, "two") == 0);
 }
 
-constexpr size_t kCtrlBytes = kCtrlBlockBytes;  // grid-barrier words at the start of the workspace
+constexpr size_t kCtrlBytes = kCtrlBlockBytes;  // control block at the start of the workspace
 
 }  // namespace
 

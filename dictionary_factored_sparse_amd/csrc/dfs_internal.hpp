@@ -129,7 +129,7 @@ constexpr int kGemvMaxRows = 16;
 // One-launch decode of a group (T == 1, up to 4 layers).
 constexpr int kFusedMaxLayers = 4;
 constexpr int kCtrlBlockBytes = 4096;   // forward workspace control block
-constexpr int kMaxBarrierGroups = 768;  // per-workgroup epoch words from byte 1024
+constexpr int kMaxFusedGroups = 768;  // per-workgroup epoch words from byte 1024
 bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc);
 hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, float* zws,
                                uint32_t* ctrl, hipStream_t s);

@@ -458,7 +458,7 @@ struct Plan {
 
 bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   const int G = device_cus();
-  if (G <= 0 || G > kMaxBarrierGroups) return false;
+  if (G <= 0 || G > kMaxFusedGroups) return false;
   const int nl = zc.n_layers;
   int A = (xd.k + kFW * G - 1) / (kFW * G);  // atoms per wave
   if (A > 2) return false;

@@ -167,11 +167,12 @@ dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream);
  * Forward workspace contract: its first 4096 bytes are a control block that
  * must be ZERO before the first forward call that uses the workspace (e.g.
  * hipMemset once after allocation); later calls keep it consistent (it holds
- * a generation counter and per-workgroup arrival flags of the one-launch
- * decode's grid barrier).  Calls sharing one workspace must not run
- * concurrently.  After a call, the 32-bit word at byte offset 128 is non-zero
- * only if the one-launch decode path (T = 1, <= 4 layers) gave up waiting at
- * its grid barrier, in which case that call's outputs are invalid. */
+ * the per-workgroup epoch words of the one-launch decode, whose workgroups
+ * hand Z to each other as epoch-tagged words instead of meeting at a grid
+ * barrier).  Calls sharing one workspace must not run concurrently.  After a
+ * call, the 32-bit word at byte offset 128 is non-zero only if the one-launch
+ * decode path (T = 1, <= 4 layers) gave up waiting for a Z word (a bounded
+ * wait), in which case that call's outputs are invalid. */
 dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, const dfs_csc* C,
                                size_t* bytes);
 
@@ -189,8 +190,8 @@ dfs_status dict_proj_forward(const void* X, int32_t xdt, int32_t T, int64_t ldx,
  * contracted against D_g in one pass, so D_g is read from memory once per
  * group rather than once per layer; then one launch applies every C_l.
  * Decode (T = 1, <= 4 layers, f16 X, f16/NVFP4 D and C) runs both halves in
- * a single launch with a grid barrier between them (environment variable
- * DFS_DECODE_PATH=two selects the two-launch path instead).
+ * a single launch, Z handed between workgroups through the workspace
+ * (environment variable DFS_DECODE_PATH=two selects the two-launch path).
  *   X, Y: host arrays of n_layers device pointers; C: host array of n_layers
  *   descriptors sharing k and d_out.  1 <= n_layers <= 16 (the largest
  *   group the pages study). */
