@@ -32,17 +32,25 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesG = kThreads / kWave;
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int kRowBytes = BK * 2;                        // 128
+constexpr int BK = 64;
+constexpr int kRowBytes = BK * 2;  // 128
 constexpr int kStages = 3;
-constexpr int kStageBytes = (BM + BN) * kRowBytes;       // 48 KiB
-constexpr int kAInst = BM * kRowBytes / 1024 / kWavesG;  // 1 KiB loads per wave per stage (A)
-constexpr int kBInst = BN * kRowBytes / 1024 / kWavesG;  // (B)
-constexpr int kLoadsPerStage = kAInst + kBInst;          // 12
-constexpr int MI = 4, NJ = 2;                            // 32 x 32 blocks per wave
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
-constexpr size_t kSmemBytes = (size_t)kStages * kStageBytes;
+
+// Workgroup tile BM x BN: 2 x 2 waves of (BM / 2) x (BN / 2), i.e. MI x NJ
+// MFMA blocks of 32 x 32 per wave.  256 x 128 for large M; 64 x 64 when M
+// (the stacked rows) is at most 128, where the large tile would leave most
+// CUs idle (a 4-layer group at b = 16 has M = 64).
+template <int BM, int BN>
+struct Tile {
+  static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+  static constexpr int kAInst = BM * kRowBytes / 1024 / kWavesG;  // 1 KiB loads per wave (A)
+  static constexpr int kBInst = BN * kRowBytes / 1024 / kWavesG;  // (B)
+  static constexpr int kLoadsPerStage = kAInst + kBInst;
+  static constexpr int MI = BM / 64, NJ = BN / 64;
+  static constexpr size_t kSmemBytes = (size_t)kStages * kStageBytes;
+};
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8): wait until at most n vector memory ops are pending
@@ -81,8 +89,11 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef const __attribute__((address_space(1))) void* glob_ptr;
 
-template <int ZT>
+template <int ZT, int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a) {
+  using TC = Tile<BM, BN>;
+  constexpr int kStageBytes = TC::kStageBytes, kAInst = TC::kAInst, kBInst = TC::kBInst;
+  constexpr int kLoadsPerStage = TC::kLoadsPerStage, MI = TC::MI, NJ = TC::NJ;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int M = a.n_layers * a.T, N = a.k, K = a.d_in;
@@ -197,16 +208,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a) {
     // MFMAs of slices 0 and 1 each paired with one read of slices 2 and 3,
     // then the remaining MFMAs (masks: 0x100 LDS read, 0x008 MFMA).
     constexpr int kReads = MI + NJ;  // fragment reads per slice
+    constexpr int kPair = 2 * kReads < 2 * MI * NJ ? 2 * kReads : 2 * MI * NJ;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReads, 0);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-      for (int r = 0; r < kReads; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - kReads, 0);
+    for (int r = 0; r < kPair; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if constexpr (2 * MI * NJ > kPair)
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * NJ - kPair, 0);
+    if constexpr (2 * kReads > kPair)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReads - kPair, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * NJ, 0);
   };
 
@@ -268,17 +280,23 @@ __global__ __launch_bounds__(256) void nvfp4_to_f16_kernel(const uint8_t* codes,
   *reinterpret_cast<h8*>(out + i8) = o;
 }
 
-template <int ZT>
-hipError_t launch_z(const XdLaunch& a, hipStream_t s) {
-  auto kern = gemm_xd_kernel<ZT>;
+template <int ZT, int BM, int BN>
+hipError_t launch_tile(const XdLaunch& a, hipStream_t s) {
+  auto kern = gemm_xd_kernel<ZT, BM, BN>;
+  constexpr size_t smem = Tile<BM, BN>::kSmemBytes;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kSmemBytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
   const int M = a.n_layers * a.T;
   const unsigned G = (unsigned)(((M + BM - 1) / BM) * ((a.k + BN - 1) / BN));
-  hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), kSmemBytes, s, a);
+  hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), smem, s, a);
   return hipGetLastError();
+}
+
+template <int ZT>
+hipError_t launch_z(const XdLaunch& a, hipStream_t s) {
+  if (a.n_layers * a.T <= 128) return launch_tile<ZT, 64, 64>(a, s);
+  return launch_tile<ZT, 256, 128>(a, s);
 }
 
 }  // namespace

@@ -7,29 +7,103 @@
 // the column's row indices and values from HBM with coalesced 16-byte loads
 // and gathers the matching Z entries from LDS.
 //
-// Mapping: a workgroup is 4 waves; each wave serves 4 columns at once, one
-// per 16-lane DPP row.  Lane g of a row reads the 8-entry chunks g, g+16, ...
+// Mapping: a workgroup is 4 waves (8 with the f16 tile); each wave serves
+// 4 columns at once, one per 16-lane DPP row.  Lane g of a row reads the 8-entry chunks g, g+16, ...
 // of its column (128 entries per step), U steps in flight per batch, every
-// lane issuing the same loads (past its column it reloads the last chunk of
-// the arrays, masked).  The first batch is issued before Z is staged into
-// LDS (C does not depend on Z).  The Z tile is [k][TT] fp32 (TT tokens per pass); the partial sums are
-// reduced over the 16 lanes of the row with DPP, in a fixed order.
-// grid = (ceil(d_out / 16), n_layers); one launch covers a whole group.
+// lane issuing the same loads (past its column it reloads the column's last
+// chunk, masked).  The first batch is issued before Z is staged into
+// LDS (C does not depend on Z).  The Z tile is [k][TT] fp32 (TT tokens per
+// pass), or f16 [k + 1][TT] when fp32 would not fit (see spmv_token_tile),
+// so that up to 16 tokens take one pass over C; the partial sums are
+// reduced over the 16 lanes of the row with DPP, in a fixed order.  A
+// workgroup serves a run of 16-column groups (about 512 workgroups per
+// launch), so one staging of Z serves many columns.
+// grid = (ceil(groups / groups per workgroup), n_layers).
 #include "csc_chunks.hpp"
 
 namespace dfs {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kColsPerBlock = 16;  // 4 waves x 4 DPP rows
+constexpr int kThreads = 256;      // fp32 Z tile (small T)
+constexpr int kThreadsH = 512;     // f16 Z tile: one large tile per CU, 2 waves per SIMD share it
+
+template <bool ZH>
+constexpr int threads_of() { return ZH ? kThreadsH : kThreads; }
 
 // 8-entry chunks in flight per lane per batch: with 16 lanes per column a
 // batch covers 128 * U entries, enough for a whole column at the densities of
 // the decode workloads (mean 410-615 stored entries per column).  Wide token
 // tiles keep fewer chunks so that the accumulators and Z reads fit.
-template <int VT, int TT>
+template <int VT, int TT, bool ZH>
 struct Unroll {
-  static constexpr int U = TT >= 16 ? 1 : TT >= 8 ? 2 : TT >= 4 ? 4 : (VT == DFS_F32 ? 3 : 6);
+  static constexpr int U = ZH ? (TT >= 16 ? 2 : TT >= 8 ? 3 : (VT == DFS_F32 ? 3 : 4))
+                              : TT >= 16 ? 1 : TT >= 8 ? 2 : TT >= 4 ? 4 : (VT == DFS_F32 ? 3 : 6);
+};
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+// Z rows [row0, row0 + rows) -> LDS [k + 1][TT] f16, row k zero (masked
+// entries read it).  Used when the fp32 tile would not fit: the token tile
+// then still covers the whole call (T <= 16) in one pass over C.  Thread
+// (token t, atom group) converts 8 atoms of token t per step.
+template <int ZT, int TT, int NTH>
+__device__ __forceinline__ void stage_zh(_Float16* zh, const void* Z, int64_t row0, int rows,
+                                         int k) {
+  constexpr int kGroups = NTH / TT;
+  const int t = threadIdx.x % TT;
+  const bool live = t < rows;
+  const int64_t zrow = (row0 + (live ? t : 0)) * k;
+  if (k % 8 == 0) {  // 16-byte loads of 8 atoms (32 bytes for fp32 Z)
+    for (int a0 = (threadIdx.x / TT) * 8; a0 < k; a0 += kGroups * 8) {
+      float v[8];
+      if constexpr (ZT == DFS_F32) {
+        const u4 w0 = ld16<u4>((const float*)Z + zrow + a0);
+        const u4 w1 = ld16<u4>((const float*)Z + zrow + a0 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = __uint_as_float(w0[i]);
+          v[4 + i] = __uint_as_float(w1[i]);
+        }
+      } else {
+        const h8 h = __builtin_bit_cast(h8, ld16<u4>((const _Float16*)Z + zrow + a0));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zh[(a0 + i) * TT + t] = live ? (_Float16)v[i] : (_Float16)0.0f;
+    }
+  } else {
+    for (int a0 = (threadIdx.x / TT) * 8; a0 < k; a0 += kGroups * 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (a0 + i < k) {
+          const float v = ZT == DFS_F32 ? ((const float*)Z)[zrow + a0 + i]
+                                        : (float)((const _Float16*)Z)[zrow + a0 + i];
+          zh[(a0 + i) * TT + t] = live ? (_Float16)v : (_Float16)0.0f;
+        }
+      }
+    }
+  }
+  for (int i = threadIdx.x; i < TT; i += NTH) zh[k * TT + i] = (_Float16)0.0f;
+}
+
+// TT f16 tokens of one staged Z row (16-byte pieces; 8 bytes for TT = 4).
+template <int TT>
+struct ZRowH {
+  h8 v[TT / 8];
+  __device__ __forceinline__ void read(const _Float16* row) {
+#pragma unroll
+    for (int j = 0; j < TT / 8; ++j) v[j] = reinterpret_cast<const h8*>(row)[j];
+  }
+  __device__ __forceinline__ float get(int t) const { return (float)v[t / 8][t % 8]; }
+};
+template <>
+struct ZRowH<4> {
+  h4 v;
+  __device__ __forceinline__ void read(const _Float16* row) {
+    v = *reinterpret_cast<const h4*>(row);
+  }
+  __device__ __forceinline__ float get(int t) const { return (float)v[t]; }
 };
 
 // Z rows [row0, row0 + rows) -> LDS [k][TT] fp32 (zero rows past `rows`).
@@ -92,130 +166,172 @@ __device__ __forceinline__ void stage_z(float* zs, const void* Z, int64_t row0, 
   }
 }
 
-template <int VT, int ZT, int TT>
-__global__ __launch_bounds__(kThreads) void spmv_csc_kernel(ZcLaunch a) {
-  constexpr int U = Unroll<VT, TT>::U;
-  extern __shared__ __attribute__((aligned(16))) float zs[];  // [k][TT]
+template <int VT, int ZT, int TT, bool ZH>
+__global__ __launch_bounds__(threads_of<ZH>()) void spmv_csc_kernel(ZcLaunch a,
+                                                                     int groups_per_block) {
+  constexpr int NTH = threads_of<ZH>();
+  constexpr int CPG = NTH / 16;  // columns per group: 4 per wave, one per DPP row
+  constexpr int U = Unroll<VT, TT, ZH>::U;
+  extern __shared__ __attribute__((aligned(16))) float zs[];  // [k][TT] fp32, or f16 (ZH)
+  _Float16* zh = reinterpret_cast<_Float16*>(zs);
 
   const int layer = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int g = lane & 15;
-  const int col = blockIdx.x * kColsPerBlock + wave * 4 + (lane >> 4);
-  const bool col_ok = col < a.d_out;
+  // this workgroup's column groups (16 columns each): one staging of Z
+  // serves all of them
+  const int ngroups = (a.d_out + CPG - 1) / CPG;
+  const int gb = blockIdx.x * groups_per_block;
+  const int gend = min(gb + groups_per_block, ngroups);
   const int64_t nnz = a.nnz[layer];
-  int s = 0, e = 0;
-  if (col_ok) {  // clamp to [0, nnz] so a malformed colptr cannot index out of bounds
-    s = (int)min<int64_t>(max(a.colptr[layer][col], 0), nnz);
-    e = (int)min<int64_t>(max(a.colptr[layer][col + 1], s), nnz);
-  }
   const uint16_t* rowidx = a.rowidx[layer];
   const void* vals = a.vals[layer];
   const uint8_t* vsc = a.vscales[layer];
-  const int first = (s & ~7) + g * 8;
-  const int64_t lastc = last_chunk(e);
   float ts = 1.0f;
   if constexpr (VT == DFS_NVFP4) ts = *a.vts[layer];
 
-  for (int t0 = 0; t0 < a.T; t0 += TT) {
-    IdxChunk ic[U];
-    ValChunk<VT> vc[U];
-    int p0 = first;
+  struct Col {
+    int col, s, e, first;
+    int64_t lastc;
+  };
+  auto col_of = [&](int cg) {
+    Col c;
+    c.col = cg * CPG + wave * 4 + (lane >> 4);
+    c.s = c.e = 0;
+    if (c.col < a.d_out) {  // clamp to [0, nnz]: a malformed colptr cannot index out of bounds
+      c.s = (int)min<int64_t>(max(a.colptr[layer][c.col], 0), nnz);
+      c.e = (int)min<int64_t>(max(a.colptr[layer][c.col + 1], c.s), nnz);
+    }
+    c.first = (c.s & ~7) + g * 8;
+    c.lastc = last_chunk(c.e);
+    return c;
+  };
+  IdxChunk ic[U];
+  ValChunk<VT> vc[U];
+  auto load_batch = [&](const Col& c, int p0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t p = min<int64_t>(p0 + 128 * u, lastc);
+      const int64_t p = min<int64_t>(p0 + 128 * u, c.lastc);
       ic[u].load(rowidx, p);
       vc[u].load(vals, vsc, p);
     }
+  };
+
+  for (int t0 = 0; t0 < a.T; t0 += TT) {
+    Col c = col_of(gb);
+    load_batch(c, c.first);  // does not depend on Z: in flight while Z is staged
     if (t0 > 0) __syncthreads();
     const int rows = a.T - t0 < TT ? a.T - t0 : TT;
-    stage_z<ZT, TT>(zs, a.Z, (int64_t)layer * a.T + t0, rows, a.k);
+    if constexpr (ZH)
+      stage_zh<ZT, TT, NTH>(zh, a.Z, (int64_t)layer * a.T + t0, rows, a.k);
+    else
+      stage_z<ZT, TT>(zs, a.Z, (int64_t)layer * a.T + t0, rows, a.k);
     __syncthreads();
 
-    float acc[TT];
+    for (int cg = gb; cg < gend; ++cg) {
+      float acc[TT];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
-    const uint32_t len = (uint32_t)(e - s);
-    while (p0 < e) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int base = p0 + 128 * u - s;
-        // entries outside [s, e) are masked without a branch (index 0, zero
-        // product), so the LDS gathers of a chunk issue back to back
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bool ok = (uint32_t)(base + i) < len;
-          const float v = ok ? vc[u].get(i) : 0.0f;
-          const float* zr = zs + (ok ? ic[u].get(i) : 0u) * TT;
-          if constexpr (TT % 4 == 0) {
-#pragma unroll
-            for (int t = 0; t < TT; t += 4) {
-              const f4 z4 = *reinterpret_cast<const f4*>(zr + t);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) acc[t + q] += ok ? z4[q] * v : 0.0f;
-            }
-          } else {
-#pragma unroll
-            for (int t = 0; t < TT; ++t) acc[t] += ok ? zr[t] * v : 0.0f;
-          }
-        }
-      }
-      p0 += 128 * U;
-      if (p0 < e) {
+      for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+      const uint32_t len = (uint32_t)(c.e - c.s);
+      int p0 = c.first;
+      while (p0 < c.e) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t p = min<int64_t>(p0 + 128 * u, lastc);
-          ic[u].load(rowidx, p);
-          vc[u].load(vals, vsc, p);
-        }
-      }
-    }
-
-    float out = 0.0f;
+          const int base = p0 + 128 * u - c.s;
+          // entries outside [s, e) are masked without a branch, so the LDS
+          // gathers of a chunk issue back to back
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      const float r = row16_sum(acc[t]);
-      if (g == t) out = r;
-    }
-    if (col_ok && g < rows) {
-      const int64_t o = (int64_t)(t0 + g) * a.ldy + col;
-      out *= ts;
-      if (a.ydt == DFS_F16)
-        ((_Float16*)a.Y[layer])[o] = (_Float16)out;
-      else
-        ((float*)a.Y[layer])[o] = out;
+          for (int i = 0; i < 8; ++i) {
+            const bool ok = (uint32_t)(base + i) < len;
+            const float v = ok ? vc[u].get(i) : 0.0f;
+            if constexpr (ZH) {
+              // masked entries read the zero row with a zero value
+              ZRowH<TT> z;
+              z.read(zh + (ok ? ic[u].get(i) : (uint32_t)a.k) * TT);
+#pragma unroll
+              for (int t = 0; t < TT; ++t) acc[t] = __builtin_fmaf(z.get(t), v, acc[t]);
+            } else {
+              // masked entries read row 0 and add a zero product
+              const float* zr = zs + (ok ? ic[u].get(i) : 0u) * TT;
+              if constexpr (TT % 4 == 0) {
+#pragma unroll
+                for (int t = 0; t < TT; t += 4) {
+                  const f4 z4 = *reinterpret_cast<const f4*>(zr + t);
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) acc[t + q] += ok ? z4[q] * v : 0.0f;
+                }
+              } else {
+#pragma unroll
+                for (int t = 0; t < TT; ++t) acc[t] += ok ? zr[t] * v : 0.0f;
+              }
+            }
+          }
+        }
+        p0 += 128 * U;
+        if (p0 < c.e) load_batch(c, p0);
+      }
+      // the next group's first batch goes out before this group's reduction
+      Col n = c;
+      if (cg + 1 < gend) {
+        n = col_of(cg + 1);
+        load_batch(n, n.first);
+      }
+      float out = 0.0f;
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const float r = row16_sum(acc[t]);
+        if (g == t) out = r;
+      }
+      if (c.col < a.d_out && g < rows) {
+        const int64_t o = (int64_t)(t0 + g) * a.ldy + c.col;
+        out *= ts;
+        if (a.ydt == DFS_F16)
+          ((_Float16*)a.Y[layer])[o] = (_Float16)out;
+        else
+          ((float*)a.Y[layer])[o] = out;
+      }
+      c = n;
     }
   }
 }
 
-template <int VT, int ZT, int TT>
+template <int VT, int ZT, int TT, bool ZH>
 hipError_t launch3(const ZcLaunch& a, hipStream_t s) {
-  const size_t smem = (size_t)a.k * TT * sizeof(float);
-  auto kern = spmv_csc_kernel<VT, ZT, TT>;
+  const size_t smem = ZH ? (size_t)(a.k + 1) * TT * 2 : (size_t)a.k * TT * sizeof(float);
+  auto kern = spmv_csc_kernel<VT, ZT, TT, ZH>;
   if (smem > 64 * 1024) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess) return err;
   }
-  dim3 grid((a.d_out + kColsPerBlock - 1) / kColsPerBlock, a.n_layers);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
+  // enough workgroups to fill the chip twice over, each staging Z once for
+  // as many 16-column groups as that leaves it
+  constexpr int NTH = threads_of<ZH>();
+  const int ngroups = (a.d_out + NTH / 16 - 1) / (NTH / 16);
+  const int target = ZH ? 256 : 512;
+  const int per = (ngroups * a.n_layers + target - 1) / target;
+  const int gpb = per < 1 ? 1 : per;
+  dim3 grid((ngroups + gpb - 1) / gpb, a.n_layers);
+  hipLaunchKernelGGL(kern, grid, dim3(NTH), smem, s, a, gpb);
   return hipGetLastError();
 }
 
 template <int VT, int ZT>
 hipError_t launch2(const ZcLaunch& a, hipStream_t s) {
-  const int tt = spmv_token_tile(a.T, a.k);
+  bool half = false;
+  const int tt = spmv_token_tile(a.T, a.k, &half);
   switch (tt) {
     case 1:
-      return launch3<VT, ZT, 1>(a, s);
+      return launch3<VT, ZT, 1, false>(a, s);
     case 2:
-      return launch3<VT, ZT, 2>(a, s);
+      return launch3<VT, ZT, 2, false>(a, s);
     case 4:
-      return launch3<VT, ZT, 4>(a, s);
+      return half ? launch3<VT, ZT, 4, true>(a, s) : launch3<VT, ZT, 4, false>(a, s);
     case 8:
-      return launch3<VT, ZT, 8>(a, s);
+      return half ? launch3<VT, ZT, 8, true>(a, s) : launch3<VT, ZT, 8, false>(a, s);
     default:
-      return launch3<VT, ZT, 16>(a, s);
+      return half ? launch3<VT, ZT, 16, true>(a, s) : launch3<VT, ZT, 16, false>(a, s);
   }
 }
 
@@ -226,10 +342,24 @@ hipError_t launch1(const ZcLaunch& a, hipStream_t s) {
 
 }  // namespace
 
-int spmv_token_tile(int T, int k) {
+// Token tile of the SpMV: the smallest power of two covering T (at most 16),
+// staged as fp32 when that fits in 64 KiB of LDS, else as f16 (with a zero
+// row) when that fits in 144 KiB, else a smaller tile (fp32 at TT = 1 holds
+// any k <= 16384).
+int spmv_token_tile(int T, int k, bool* half) {
   int tt = 1;
-  while (tt < T && tt < 16 && (size_t)k * (tt * 2) * sizeof(float) <= 64 * 1024) tt *= 2;
-  return tt;
+  while (tt < T && tt < 16) tt *= 2;
+  for (;;) {
+    if ((size_t)k * tt * sizeof(float) <= 64 * 1024 || tt == 1) {
+      *half = false;
+      return tt;
+    }
+    if (tt >= 4 && (size_t)(k + 1) * tt * 2 <= 144 * 1024) {
+      *half = true;
+      return tt;
+    }
+    tt /= 2;
+  }
 }
 
 hipError_t launch_spmv_csc(const ZcLaunch& a, hipStream_t s) {
