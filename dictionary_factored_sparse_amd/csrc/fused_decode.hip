@@ -474,8 +474,10 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   if ((uint64_t)nl * (uint64_t)zc.d_out * (uint64_t)(G + 1) >= (1ull << 32)) return false;
   const int x_items = (int)((size_t)RT * ld / 8);
   const int NX = (x_items + kFT - 1) / kFT;
-  if (NX != RT && NX != 2 * RT) return false;  // X rows held in registers: ld <= 8192
-  if (NX > 4) return false;
+  // X rows pass through registers: 1, 2 or 3 passes of the workgroup per
+  // row (ld <= 12288), at most 12 16-byte registers per thread
+  if (NX != RT && NX != 2 * RT && NX != 3 * RT) return false;
+  if (NX > 12) return false;
   p->G = G;
   p->A = A;
   p->RT = RT;
@@ -503,9 +505,8 @@ hipError_t launch5(FusedArgs f, const Plan& p, hipStream_t s) {
 
 template <int DT, int VT, int RT, int A>
 hipError_t launch4(FusedArgs f, const Plan& p, hipStream_t s) {
-  if constexpr (RT <= 2) {
-    if (p.NX == 2 * RT) return launch5<DT, VT, RT, A, 2 * RT>(f, p, s);
-  }
+  if (p.NX == 3 * RT) return launch5<DT, VT, RT, A, 3 * RT>(f, p, s);
+  if (p.NX == 2 * RT) return launch5<DT, VT, RT, A, 2 * RT>(f, p, s);
   return launch5<DT, VT, RT, A, RT>(f, p, s);
 }
 
