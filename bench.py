@@ -283,25 +283,38 @@ def main():
         return B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
                            vals=c.vals.clone())
 
-    def time_group(gx, Ts, nvfp4):
+    def time_group(gx, Ts, nvfp4, cnvfp4=None, sequential=False):
         """us per group forward at each T in Ts (inputs rotated over replicas
-        totalling > 1.2 GB), and algorithmic bytes per forward."""
+        totalling > 1.2 GB), and algorithmic bytes per forward.  cnvfp4 sets
+        the coefficients' storage apart from the dictionary's; sequential
+        runs each layer alone (dict_proj_forward, D read once per layer)."""
+        cnvfp4 = nvfp4 if cnvfp4 is None else cnvfp4
         Dd = B.to_device_dict(gx.D, dev, nvfp4=nvfp4)
-        Cd = [B.to_device_csc(c, dev, nvfp4=nvfp4) for c in gx.Cs]
+        Cd = [B.to_device_csc(c, dev, nvfp4=cnvfp4) for c in gx.Cs]
         nz = [c.nnz for c in Cd]
-        wdt = cdt = "nvfp4" if nvfp4 else "f16"
+        wdt = "nvfp4" if nvfp4 else "f16"
+        cdt = "nvfp4" if cnvfp4 else "f16"
         out = {}
         for T in Ts:
             nb = L.group_bytes(d_in=gx.d_in, d_out=gx.d_out, k=gx.k, T=T, nnzs=nz, wdtype=wdt,
                                cdtype=cdt, xdtype="f16", ydtype="f16")
+            if sequential:  # D once per layer
+                nb += (len(nz) - 1) * L.dict_bytes(gx.d_in, gx.k, wdt)
             nrep = max(2, math.ceil(1.2e9 / nb))
             rp = [(Dd, Cd)] + [(clone_dict(Dd), [clone_csc(c) for c in Cd]) for _ in range(nrep - 1)]
             Xg = [torch.from_numpy(np.ascontiguousarray(X[:T])).to(dev) for X in gx.Xs]
             Yg = [torch.empty(T, gx.d_out, dtype=torch.float16, device=dev) for _ in Xg]
             wsg = B.workspace(len(Xg), T, Dd, Cd[0], dev)
             nstep = 100 if T == 1 else 20
-            gr = capture(lambda i: B.dict_group_forward(Xg, rp[i % nrep][0], rp[i % nrep][1],
-                                                        Ys=Yg, ws=wsg), nstep)
+            if sequential:
+                def fwd(i):
+                    for l in range(len(Xg)):
+                        B.dict_proj_forward(Xg[l], rp[i % nrep][0], rp[i % nrep][1][l], Y=Yg[l],
+                                            ws=wsg)
+            else:
+                def fwd(i):
+                    B.dict_group_forward(Xg, rp[i % nrep][0], rp[i % nrep][1], Ys=Yg, ws=wsg)
+            gr = capture(fwd, nstep)
             gr.replay()
             torch.cuda.synchronize()
             ev0.record()
@@ -327,19 +340,32 @@ def main():
             del gx
         extras["mlp_group4_k3072_density0.20"] = mlp
         _log(f"mlp groups: {mlp}")
-        stack, per_tok_us, per_tok_b = {}, 0.0, 0
+        stack, per_tok_us, per_tok_b, seq_us, seq_b = {}, 0.0, 0, 0.0, 0
         for ptype, count in (("q", 4), ("gate", 2), ("down", 1)):
             gx = synth.make_group("stack_nvfp4", ptype=ptype)
             us, nb = time_group(gx, (1,), True)[1]
+            sus, snb = time_group(gx, (1,), True, sequential=True)[1]
             stack[ptype] = {"us_per_group": round(us, 2), "MB": round(nb / 1e6, 2),
-                            "GB/s": round(nb / us / 1e3, 1), "groups_per_token": 16 * count}
+                            "GB/s": round(nb / us / 1e3, 1), "groups_per_token": 16 * count,
+                            "sequential_us_per_2_projections": round(sus, 2)}
             per_tok_us += 16 * count * us
             per_tok_b += 16 * count * nb
+            seq_us += 16 * count * sus
+            seq_b += 16 * count * snb
             del gx
         stack["per_token_us"] = round(per_tok_us, 1)
         stack["per_token_GB"] = round(per_tok_b / 1e9, 3)
         stack["per_token_GB/s"] = round(per_tok_b / per_tok_us / 1e3, 1)
+        stack["sequential_per_token_us"] = round(seq_us, 1)
+        stack["sequential_per_token_GB"] = round(seq_b / 1e9, 3)
+        stack["sequential_note"] = ("each projection alone through dict_proj_forward, D read "
+                                    "once per layer, inputs rotated so that no cache serves them")
         extras["stack_nvfp4_32_layers_per_token"] = stack
+        # mixed factors on the q_proj decode group: NVFP4 dictionary, f16 coefficients
+        us, nb = time_group(g, (1,), True, cnvfp4=False)[1]
+        extras["qproj_group_nvfp4_D_f16_C"] = {"us": round(us, 2), "MB": round(nb / 1e6, 2),
+                                               "GB/s": round(nb / us / 1e3, 1),
+                                               "frac_of_8TBs": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
         _log(f"nvfp4 stack: {stack}")
 
         # packers (offline steps, timed for information): dense -> CSC of one

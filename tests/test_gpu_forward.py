@@ -254,9 +254,9 @@ def test_graph_replays_match_eager():
             assert torch.equal(y, r), f"replay {i}"
 
 
-def _both_paths(g, nvfp4=False):
+def _both_paths(g, nvfp4=False, dfmt=None, cfmt=None):
     import os
-    D, Cs, Xs = device_group(g, nvfp4=nvfp4)
+    D, Cs, Xs = device_group(g, nvfp4=nvfp4, dfmt=dfmt, cfmt=cfmt)
     ws = B.workspace(g.n_layers, g.T, D, Cs[0], DEV)
     out = {}
     for path in ("fused", "two"):
@@ -283,6 +283,25 @@ def test_one_launch_decode_matches_two_launch_and_oracle(wl, ptype, nvfp4, n):
     for l, ref in enumerate(refs):
         assert_close(out["fused"][l], ref, f"fused layer {l}")
         assert_close(out["two"][l], ref, f"two-launch layer {l}")
+
+
+@pytest.mark.parametrize("dfmt,cfmt", [("nvfp4", "plain"), ("plain", "nvfp4")])
+def test_mixed_precision_factors(dfmt, cfmt):
+    # one factor NVFP4, the other f16: the pages' mixed variants (NVFP4 D with
+    # FP16 C); both decode paths and the MFMA prefill path
+    say(f"case: mixed factors D {dfmt}, C {cfmt}")
+    g = synth.make_group("qproj", d_in=1024, d_out=768, k=512, T=1, n_layers=2)
+    out = _both_paths(g, dfmt=dfmt, cfmt=cfmt)
+    refs = oracle_group(g, dfmt=dfmt, cfmt=cfmt)
+    for l, ref in enumerate(refs):
+        assert_close(out["fused"][l], ref, f"fused layer {l}")
+        assert_close(out["two"][l], ref, f"two-launch layer {l}")
+    gp = synth.make_group("qproj", d_in=1024, d_out=768, k=512, T=40, n_layers=2)
+    D, Cs, Xs = device_group(gp, dfmt=dfmt, cfmt=cfmt)
+    Ys = B.dict_group_forward(Xs, D, Cs)
+    torch.cuda.synchronize()
+    for l, ref in enumerate(oracle_group(gp, dfmt=dfmt, cfmt=cfmt)):
+        assert_close(Ys[l], ref, f"prefill layer {l}")
 
 
 def test_one_launch_decode_repeated_launches_identical():
