@@ -40,6 +40,29 @@ def nvfp4_bits_per_value() -> float:
     return 4.0 + 8.0 / 16.0
 
 
+VALUE_BITS = {"f16": 16.0, "fp8": 8.0, "int8": 8.0}
+
+
+def value_bits(fmt: str) -> float:
+    """Bits per retained value under the values-only accounting of the
+    pages (outer scales, indices and padding left out)."""
+    return nvfp4_bits_per_value() if fmt == "nvfp4" else VALUE_BITS[fmt]
+
+
+def mixed_gain(dict_share: float, dfmt: str, cfmt: str) -> float:
+    """Storage gain over an all-FP16 factorised model whose retained values
+    are a fraction ``dict_share`` in D and the rest in C (tables page,
+    Table 4: the gain of each factor-format pair)."""
+    bits = dict_share * value_bits(dfmt) + (1.0 - dict_share) * value_bits(cfmt)
+    return 16.0 / bits
+
+
+def dict_share_from_gain(gain: float, dfmt: str, cfmt: str) -> float:
+    """Inverse of ``mixed_gain`` in ``dict_share``."""
+    bd, bc = value_bits(dfmt), value_bits(cfmt)
+    return (16.0 / gain - bc) / (bd - bc)
+
+
 def macs_factored(n: int, k: int, d_in: int, d_out: int, p: float) -> float:
     """Per group and token: n*k*(d_in + (1-p)*d_out) multiply-adds."""
     return n * k * (d_in + (1.0 - p) * d_out)
@@ -66,10 +89,13 @@ def dict_bytes(d_in: int, k: int, dtype: str) -> int:
 
 
 def csc_bytes(d_out: int, nnz: int, dtype: str) -> int:
-    """colptr int32[d_out+1] + uint16 row indices + values."""
+    """colptr int32[d_out+1] + uint16 row indices + values (8-bit codes:
+    one byte per entry plus one fp32 scale per column)."""
     base = 4 * (d_out + 1) + 2 * nnz
     if dtype == "nvfp4":
         return base + nvfp4_bytes(nnz)
+    if dtype in ("fp8", "int8"):
+        return base + nnz + 4 * d_out
     return base + int(nnz * ELEM_BYTES[dtype])
 
 

@@ -16,6 +16,11 @@ Pages (cited by title and section):
   scale per 16 values (Review, "From retained values to measured decoding")
   and one fp32 tensor scale.  The scale recipe is a reading; parity unpinned
   against the pages, pinned against format definitions and bounds.
+* ``quantize8_csc`` -- 8-bit coefficient codes, FP8 (E4M3) or INT8, for the
+  mixed-precision rows of Table 4 on the tables page ("DictLLM: Post-training
+  Compression of Large Language Model with Dictionary Kernels").  Reading:
+  one fp32 scale per column of C, amax / 448 or amax / 127, nearest code with
+  ties to even (the pages leave the scaling open).
 """
 from __future__ import annotations
 
@@ -28,12 +33,12 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-DT_F32, DT_F16, DT_NVFP4 = 0, 1, 2   # element-type codes of oracle.c
+DT_F32, DT_F16, DT_NVFP4, DT_FP8, DT_INT8 = 0, 1, 2, 3, 4   # element types of oracle.c
 
 
 class _Tensor(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("data", C.c_void_p), ("codes", C.c_void_p),
-                ("scales", C.c_void_p), ("ts", C.c_float)]
+                ("scales", C.c_void_p), ("ts", C.c_float), ("col_scale", C.c_void_p)]
 
 
 _lib = None
@@ -65,6 +70,11 @@ def lib():
         L.orc_nvfp4_unpack.restype = None
         L.orc_nvfp4_unpack.argtypes = [C.c_void_p, C.c_void_p, C.c_float, C.c_int64,
                                        C.c_void_p]
+        L.orc_int8_nearest.restype = C.c_int
+        L.orc_int8_nearest.argtypes = [C.c_float]
+        L.orc_quant8_csc.restype = C.c_int
+        L.orc_quant8_csc.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
+                                     C.c_void_p, C.c_void_p]
         L.orc_pack_csc.restype = C.c_int64
         L.orc_pack_csc.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int64,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64]
@@ -103,6 +113,10 @@ def e2m1_nearest(v: float) -> int:
     return lib().orc_e2m1_nearest(float(np.float32(v)))
 
 
+def int8_nearest(v: float) -> int:
+    return lib().orc_int8_nearest(float(np.float32(v)))
+
+
 def nvfp4_tensor_scale(amax: float) -> float:
     return lib().orc_nvfp4_tensor_scale(float(np.float32(amax)))
 
@@ -132,6 +146,19 @@ def nvfp4_unpack(q: NVFP4) -> np.ndarray:
     y = np.empty(q.n, np.float32)
     lib().orc_nvfp4_unpack(_ptr(q.codes), _ptr(q.scales), q.ts, q.n, _ptr(y))
     return y
+
+
+@dataclass
+class Codes8:
+    """8-bit coefficient values in CSC order with one fp32 scale per column:
+    entry p of column j decodes to value(codes[p]) * col_scale[j]."""
+    kind: str               # "fp8" (E4M3) or "int8"
+    codes: np.ndarray       # uint8[nnz]
+    col_scale: np.ndarray   # float32[d_out]
+
+    @property
+    def dtype_code(self) -> int:
+        return DT_FP8 if self.kind == "fp8" else DT_INT8
 
 
 # ---------------------------------------------------------------- CSC
@@ -176,6 +203,25 @@ def pack_csc(Cd: np.ndarray) -> CSC:
     return CSC(k, d_out, colptr, rowidx[:nnz], vals[:nnz])
 
 
+def quantize8_csc(c: CSC, kind: str) -> CSC:
+    """Quantise a CSC's float16/float32 values to 8-bit codes, ``kind``
+    "fp8" (E4M3) or "int8", one scale per column; support unchanged."""
+    if kind not in ("fp8", "int8"):
+        raise ValueError(kind)
+    vals = np.ascontiguousarray(c.vals)
+    colptr = np.ascontiguousarray(c.colptr, np.int32)
+    codes = np.zeros(max(c.nnz, 1), np.uint8)
+    scale = np.zeros(max(c.d_out, 1), np.float32)
+    q = Codes8(kind, codes, scale)
+    if vals.size == 0:
+        vals = np.zeros(1, np.float32)
+    rc = lib().orc_quant8_csc(_ptr(vals), _dtype_code(vals), _ptr(colptr), c.d_out,
+                              q.dtype_code, _ptr(codes), _ptr(scale))
+    if rc != 0:
+        raise ValueError("quantize8_csc: values hold NaN or Inf")
+    return CSC(c.k, c.d_out, c.colptr, c.rowidx, Codes8(kind, codes[:c.nnz], scale[:c.d_out]))
+
+
 def csc_to_nvfp4(c: CSC) -> CSC:
     """Quantise a CSC's values (in CSC order) to NVFP4; support unchanged."""
     return CSC(c.k, c.d_out, c.colptr, c.rowidx,
@@ -187,10 +233,14 @@ def csc_to_nvfp4(c: CSC) -> CSC:
 def _tensor(t, keep: list) -> _Tensor:
     if isinstance(t, NVFP4):
         keep.extend([t.codes, t.scales])
-        return _Tensor(DT_NVFP4, None, _ptr(t.codes), _ptr(t.scales), t.ts)
+        return _Tensor(DT_NVFP4, None, _ptr(t.codes), _ptr(t.scales), t.ts, None)
+    if isinstance(t, Codes8):
+        codes = t.codes if t.codes.size else np.zeros(1, np.uint8)
+        keep.extend([codes, t.col_scale])
+        return _Tensor(t.dtype_code, _ptr(codes), None, None, 0.0, _ptr(t.col_scale))
     a = np.ascontiguousarray(t)
     keep.append(a)
-    return _Tensor(_dtype_code(a), _ptr(a), None, None, 0.0)
+    return _Tensor(_dtype_code(a), _ptr(a), None, None, 0.0, None)
 
 
 def forward(X: np.ndarray, D, d_in: int, c: CSC) -> np.ndarray:

@@ -27,6 +27,13 @@
  *              scale.  The scale recipe below is a reading, not printed on
  *              the pages (parity unpinned against the pages; pinned against
  *              format definitions, brute force and error bounds).
+ *   codes8     8-bit coefficient values, FP8 (E4M3) or INT8, for the mixed
+ *              precision rows of [Tables] Table 4 (NVFP4 dictionary with FP8
+ *              or INT8 coefficients; also [Review] "From retained values to
+ *              measured decoding", mixed precision).  The pages do not say
+ *              how those codes are scaled; the reading taken here is one
+ *              fp32 scale per column of C, symmetric, amax / 448 (E4M3) or
+ *              amax / 127 (INT8), nearest code with ties to even.
  *
  * Every floating-point step that decides an integer code is done in fp32,
  * each operation correctly rounded (compile with -ffp-contract=off, no
@@ -40,14 +47,17 @@
 #define ORC_F32 0
 #define ORC_F16 1
 #define ORC_NVFP4 2
+#define ORC_FP8 3
+#define ORC_INT8 4
 
 /* A read-only view of a stored tensor (flat element index). */
 typedef struct {
-  int32_t dtype;        /* ORC_F32, ORC_F16 or ORC_NVFP4 */
-  const void* data;     /* f32 / f16 elements (unused for NVFP4) */
+  int32_t dtype;        /* ORC_F32, ORC_F16, ORC_NVFP4, ORC_FP8 or ORC_INT8 */
+  const void* data;     /* f32 / f16 elements; FP8 / INT8: one code byte each */
   const uint8_t* codes; /* NVFP4: two 4-bit codes per byte, element 2i low */
   const uint8_t* scales;/* NVFP4: one E4M3 code per 16 elements */
   float ts;             /* NVFP4: fp32 tensor scale */
+  const float* col_scale; /* FP8 / INT8 coefficients: fp32 scale per column */
 } orc_tensor;
 
 /* IEEE 754 binary16, decoded from its definition: sign, 5-bit exponent with
@@ -165,6 +175,12 @@ int orc_nvfp4_pack(const float* x, int64_t n, uint8_t* codes, uint8_t* scales,
   return 0;
 }
 
+/* Exact value of an F32 or F16 element (the quantiser's inputs). */
+static double elem_plain(const orc_tensor* t, int64_t i) {
+  return t->dtype == ORC_F32 ? (double)((const float*)t->data)[i]
+                             : orc_half_value(((const uint16_t*)t->data)[i]);
+}
+
 static int nibble(const uint8_t* codes, int64_t i) {
   return (i & 1) ? (codes[i / 2] >> 4) & 15 : codes[i / 2] & 15;
 }
@@ -178,13 +194,80 @@ void orc_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, float ts,
                    orc_e4m3_value(scales[i / 16]) * (double)ts);
 }
 
-/* Exact float64 value of stored element i. */
+/* Nearest integer in [-127, 127] to v, ties to the even integer, values
+ * beyond the ends take the end.  Brute force over the 255 candidates; every
+ * difference is exact in float64. */
+int orc_int8_nearest(float v) {
+  int best = 0;
+  double bestd = INFINITY;
+  for (int c = -127; c <= 127; ++c) {
+    double d = fabs((double)v - (double)c);
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* Value of the stored code of element i, without any scale: E4M3 or a
+ * two's-complement byte.  The column scale is applied by the caller. */
+static double code8_value(const orc_tensor* t, int64_t i) {
+  uint8_t b = ((const uint8_t*)t->data)[i];
+  return t->dtype == ORC_FP8 ? orc_e4m3_value(b) : (double)(int8_t)b;
+}
+
+/* Quantise the stored values of a CSC (vals[colptr[d_out]], F32 or F16, in
+ * CSC order) to 8-bit codes with one scale per column.  Every step that
+ * decides a code is one correctly rounded fp32 operation:
+ *   amax_j = max |v| over column j;  s_j = amax_j / qmax, or 1 if that is 0
+ *   (qmax = 448 for E4M3, the largest finite value; 127 for INT8);
+ *   q = v / s_j;
+ *   E4M3: code = (sign bit of v) << 7 | nearest magnitude code of |q|;
+ *   INT8: code = nearest integer to q in [-127, 127], as a byte.
+ * Decoded value of entry p in column j: value(code_p) * s_j.
+ * Returns 0, or -1 (nothing written) if a value is NaN or infinite or kind
+ * is neither ORC_FP8 nor ORC_INT8. */
+int orc_quant8_csc(const void* vals, int32_t dtype, const int32_t* colptr, int32_t d_out,
+                   int32_t kind, uint8_t* codes, float* col_scale) {
+  if (kind != ORC_FP8 && kind != ORC_INT8) return -1;
+  orc_tensor t = {dtype, vals, NULL, NULL, 0.0f, NULL};
+  int64_t nnz = colptr[d_out];
+  for (int64_t p = 0; p < nnz; ++p)
+    if (!isfinite(elem_plain(&t, p))) return -1;
+  const float qmax = kind == ORC_FP8 ? 448.0f : 127.0f;
+  for (int32_t j = 0; j < d_out; ++j) {
+    float amax = 0.0f;
+    for (int64_t p = colptr[j]; p < colptr[j + 1]; ++p) {
+      float a = fabsf((float)elem_plain(&t, p));
+      if (a > amax) amax = a;
+    }
+    float s = amax / qmax;
+    if (s == 0.0f) s = 1.0f;
+    col_scale[j] = s;
+    for (int64_t p = colptr[j]; p < colptr[j + 1]; ++p) {
+      float v = (float)elem_plain(&t, p); /* exact: v is an f32 or f16 value */
+      float q = v / s;
+      if (kind == ORC_FP8)
+        codes[p] = (uint8_t)(orc_e4m3_nearest(fabsf(q)) | (signbit(v) ? 0x80 : 0));
+      else
+        codes[p] = (uint8_t)(int8_t)orc_int8_nearest(q);
+    }
+  }
+  return 0;
+}
+
+/* Exact float64 value of stored element i (8-bit codes: without their
+ * column scale). */
 static double elem(const orc_tensor* t, int64_t i) {
   switch (t->dtype) {
     case ORC_F32:
       return (double)((const float*)t->data)[i];
     case ORC_F16:
       return orc_half_value(((const uint16_t*)t->data)[i]);
+    case ORC_FP8:
+    case ORC_INT8:
+      return code8_value(t, i);
     default:
       return orc_e2m1_value(nibble(t->codes, i)) *
              orc_e4m3_value(t->scales[i / 16]) * (double)t->ts;
@@ -200,7 +283,7 @@ static double elem(const orc_tensor* t, int64_t i) {
 int64_t orc_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out,
                      int64_t ldc, int32_t* colptr, uint16_t* rowidx, void* vals,
                      int64_t capacity) {
-  orc_tensor t = {dtype, C, NULL, NULL, 0.0f};
+  orc_tensor t = {dtype, C, NULL, NULL, 0.0f, NULL};
   int64_t nnz = 0;
   colptr[0] = 0;
   for (int32_t j = 0; j < d_out; ++j) {
@@ -228,7 +311,8 @@ int64_t orc_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out,
  *   Z[t,a] = sum_{i=0..d_in-1} X[t,i] * D[i,a]        (i ascending)
  *   Y[t,j] = sum_{p=colptr[j]..colptr[j+1]-1} Z[t,rowidx[p]] * C_p  (p asc.)
  * X: T x d_in row-major (leading dim ldx).  D: d_in x k stored atom by atom
- * (element (i,a) at flat index a*ldd + i).  C: k x d_out in CSC.
+ * (element (i,a) at flat index a*ldd + i).  C: k x d_out in CSC; with 8-bit
+ * codes C_p = value(code_p) * col_scale[j], exact in float64.
  * Y: T x d_out row-major float64, leading dimension d_out.
  * Returns 0, or -1 on allocation failure. */
 int orc_forward(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_in,
@@ -267,8 +351,11 @@ int orc_forward(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_in,
   for (int32_t j = 0; j < d_out; ++j)
     for (int32_t t = 0; t < T; ++t) {
       double sum = 0.0;
-      for (int32_t p = colptr[j]; p < colptr[j + 1]; ++p)
-        sum += Z[(size_t)t * k + rowidx[p]] * elem(C, p);
+      for (int32_t p = colptr[j]; p < colptr[j + 1]; ++p) {
+        double c = elem(C, p);
+        if (C->col_scale) c *= (double)C->col_scale[j];
+        sum += Z[(size_t)t * k + rowidx[p]] * c;
+      }
       Y[(size_t)t * d_out + j] = sum;
     }
 

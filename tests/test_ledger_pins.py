@@ -83,3 +83,37 @@ def test_group_bytes_of_the_qproj_decode_group():
     b = L.group_bytes(d_in=4096, d_out=4096, k=2048, T=1, nnzs=[nnz, nnz], wdtype="f16",
                       cdtype="f16", xdtype="f16", ydtype="f16")
     assert abs(b / 1e6 - 36.98) < 0.05
+
+
+def test_table4_mixed_precision_gains(golden):
+    """Table 4's gains follow from values-only accounting: NVFP4 4.5 bits,
+    FP8 and INT8 8 bits, FP16 16 bits.  The NVFP4/FP16 row fixes the
+    dictionary's share of the retained values (about 0.53); the 8-bit rows
+    must then come out at 2.60 for every share that rounds to that row's
+    1.61, and the two 8-bit formats must tie."""
+    rows = {(d, c): (float(g), int(dec)) for d, c, g, dec in golden("table4_gains.txt")}
+    g16, dec = rows[("nvfp4", "f16")]
+    lo = L.dict_share_from_gain(g16 - 0.5 * 10 ** -dec, "nvfp4", "f16")
+    hi = L.dict_share_from_gain(g16 + 0.5 * 10 ** -dec, "nvfp4", "f16")
+    mid = L.dict_share_from_gain(g16, "nvfp4", "f16")
+    assert 0.5 < lo < mid < hi < 0.55
+    for cf in ("fp8", "int8"):
+        want, d8 = rows[("nvfp4", cf)]
+        assert round(L.mixed_gain(mid, "nvfp4", cf), d8) == want
+        g_lo, g_hi = sorted(L.mixed_gain(f, "nvfp4", cf) for f in (lo, hi))
+        assert g_lo - 0.5 * 10 ** -d8 <= want <= g_hi + 0.5 * 10 ** -d8
+    assert L.mixed_gain(mid, "nvfp4", "nvfp4") == 16 / 4.5
+    assert round(L.mixed_gain(mid, "nvfp4", "nvfp4"), 2) == rows[("nvfp4", "nvfp4")][0]
+    assert L.mixed_gain(mid, "f16", "f16") == rows[("f16", "f16")][0]
+    # a wrong bit count for the 8-bit codes (e.g. counting a 16-bit index or
+    # a per-16 scale as for NVFP4) misses the table
+    assert round(16 / (mid * 4.5 + (1 - mid) * 8.5), 2) != rows[("nvfp4", "fp8")][0]
+
+
+def test_csc_bytes_of_8bit_codes():
+    k, d_out = 2048, 4096
+    nnz = int(0.3 * k * d_out)
+    b16 = L.csc_bytes(d_out, nnz, "f16")
+    for f in ("fp8", "int8"):
+        b8 = L.csc_bytes(d_out, nnz, f)
+        assert b16 - b8 == nnz - 4 * d_out
