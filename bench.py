@@ -280,20 +280,24 @@ def main():
         if c.nv is not None:
             return B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
                                nv=clone_nv(c.nv))
+        if c.codes8 is not None:
+            return B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
+                               codes8=c.codes8.clone(), col_scale=c.col_scale.clone(),
+                               code_kind=c.code_kind)
         return B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
                            vals=c.vals.clone())
 
-    def time_group(gx, Ts, nvfp4, cnvfp4=None, sequential=False):
+    def time_group(gx, Ts, nvfp4, cfmt=None, sequential=False):
         """us per group forward at each T in Ts (inputs rotated over replicas
-        totalling > 1.2 GB), and algorithmic bytes per forward.  cnvfp4 sets
-        the coefficients' storage apart from the dictionary's; sequential
-        runs each layer alone (dict_proj_forward, D read once per layer)."""
-        cnvfp4 = nvfp4 if cnvfp4 is None else cnvfp4
+        totalling > 1.2 GB), and algorithmic bytes per forward.  cfmt sets
+        the coefficients' storage ("f16", "nvfp4", "fp8", "int8") apart from
+        the dictionary's; sequential runs each layer alone
+        (dict_proj_forward, D read once per layer)."""
+        cdt = cfmt or ("nvfp4" if nvfp4 else "f16")
         Dd = B.to_device_dict(gx.D, dev, nvfp4=nvfp4)
-        Cd = [B.to_device_csc(c, dev, nvfp4=cnvfp4) for c in gx.Cs]
+        Cd = [B.to_device_csc(c, dev, fmt=None if cdt == "f16" else cdt) for c in gx.Cs]
         nz = [c.nnz for c in Cd]
         wdt = "nvfp4" if nvfp4 else "f16"
-        cdt = "nvfp4" if cnvfp4 else "f16"
         out = {}
         for T in Ts:
             nb = L.group_bytes(d_in=gx.d_in, d_out=gx.d_out, k=gx.k, T=T, nnzs=nz, wdtype=wdt,
@@ -361,12 +365,18 @@ def main():
         stack["sequential_note"] = ("each projection alone through dict_proj_forward, D read "
                                     "once per layer, inputs rotated so that no cache serves them")
         extras["stack_nvfp4_32_layers_per_token"] = stack
-        # mixed factors on the q_proj decode group: NVFP4 dictionary, f16 coefficients
-        us, nb = time_group(g, (1,), True, cnvfp4=False)[1]
-        extras["qproj_group_nvfp4_D_f16_C"] = {"us": round(us, 2), "MB": round(nb / 1e6, 2),
-                                               "GB/s": round(nb / us / 1e3, 1),
-                                               "frac_of_8TBs": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
         _log(f"nvfp4 stack: {stack}")
+        # the factor-format pairs of the tables page's Table 4 on the q_proj
+        # decode group (one launch each): bytes moved and time per group
+        t4 = {}
+        for dfmt, cfmt in (("f16", "f16"), ("nvfp4", "f16"), ("nvfp4", "fp8"), ("nvfp4", "int8"),
+                           ("nvfp4", "nvfp4")):
+            us, nb = time_group(g, (1,), dfmt == "nvfp4", cfmt=cfmt)[1]
+            t4[f"D_{dfmt}_C_{cfmt}"] = {"us": round(us, 2), "MB": round(nb / 1e6, 2),
+                                         "GB/s": round(nb / us / 1e3, 1),
+                                         "frac_of_8TBs": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+        extras["table4_formats_qproj_decode_group"] = t4
+        _log(f"table 4 formats: {t4}")
 
         # packers (offline steps, timed for information): dense -> CSC of one
         # q_proj C (2048 x 4096 f16), NVFP4 pack and unpack of one D_g
@@ -395,6 +405,16 @@ def main():
         torch.cuda.synchronize()
         nvu_us = ev0.elapsed_time(ev1) / 20 * 1e3
         n_el = xf.numel()
+        c16 = B.dict_pack_csc(Cdense)
+        q8 = {}
+        for kind in ("fp8", "int8"):
+            B.csc_quantize8(c16, kind)
+            torch.cuda.synchronize()
+            tp = time.perf_counter()
+            for _ in range(5):
+                B.csc_quantize8(c16, kind)
+            torch.cuda.synchronize()
+            q8[kind] = (time.perf_counter() - tp) / 5 * 1e6
         extras["packers"] = {
             "dict_pack_csc_us": round(pack_us, 1),
             "dict_pack_csc_entries_per_s": round(Cdense.numel() / pack_us * 1e6 / 1e9, 2),
@@ -404,7 +424,11 @@ def main():
             "nvfp4_pack_GB/s_in": round(n_el * 4 / nvp_us / 1e3, 1),
             "nvfp4_unpack_us": round(nvu_us, 1),
             "nvfp4_unpack_GB/s_out": round(n_el * 4 / nvu_us / 1e3, 1),
-            "nvfp4_elements": n_el}
+            "nvfp4_elements": n_el,
+            "csc_quantize8_fp8_us": round(q8["fp8"], 1),
+            "csc_quantize8_int8_us": round(q8["int8"], 1),
+            "csc_quantize8_note": f"{c16.nnz} f16 values of one q_proj C, two passes and a "
+                                  "host synchronisation, wall clock"}
         _log(f"packers: {extras['packers']} ({time.time() - t1:.0f} s of extras)")
 
     # ---------------------------------------------------------------- CPU baseline

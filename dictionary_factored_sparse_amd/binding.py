@@ -19,7 +19,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdictfs.so")
 
-DFS_F32, DFS_F16, DFS_NVFP4 = 0, 1, 2
+DFS_F32, DFS_F16, DFS_NVFP4, DFS_FP8, DFS_INT8 = 0, 1, 2, 3, 4
+CODE8 = {"fp8": DFS_FP8, "int8": DFS_INT8}
 STATUS = {0: "DFS_OK", 1: "DFS_E_INVALID", 2: "DFS_E_UNSUPPORTED", 3: "DFS_E_RANGE",
           4: "DFS_E_ALIGN", 5: "DFS_E_WORKSPACE", 6: "DFS_E_HIP"}
 
@@ -27,7 +28,8 @@ STATUS = {0: "DFS_OK", 1: "DFS_E_INVALID", 2: "DFS_E_UNSUPPORTED", 3: "DFS_E_RAN
 SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspace_size",
            "nvfp4_pack", "nvfp4_unpack", "dict_workspace_size", "dict_proj_forward",
            "dict_group_forward", "dict_xd_forward", "dict_xd_workspace_size", "dict_zc_forward",
-           "dfs_status_str", "dfs_last_hip_error", "dfs_version", "dict_csc_capacity")
+           "dfs_status_str", "dfs_last_hip_error", "dfs_version", "dict_csc_capacity",
+           "dict_csc_quantize8_workspace_size", "dict_csc_quantize8")
 
 
 class NV(C.Structure):
@@ -42,7 +44,7 @@ class Dict(C.Structure):
 class Csc(C.Structure):
     _fields_ = [("k", C.c_int32), ("d_out", C.c_int32), ("nnz", C.c_int64), ("dtype", C.c_int32),
                 ("_pad", C.c_int32), ("colptr", C.c_void_p), ("rowidx", C.c_void_p),
-                ("vals", C.c_void_p), ("nv", NV)]
+                ("vals", C.c_void_p), ("nv", NV), ("col_scale", C.c_void_p)]
 
 
 class DfsError(RuntimeError):
@@ -83,6 +85,8 @@ def lib():
                                 sz, vp],
             "dict_xd_workspace_size": [i32, i32, C.POINTER(Dict), psz],
             "dict_zc_forward": [i32, vp, i32, i32, C.POINTER(Csc), C.POINTER(vp), i32, i64, vp],
+            "dict_csc_quantize8_workspace_size": [i32, psz],
+            "dict_csc_quantize8": [C.POINTER(Csc), i32, vp, vp, vp, sz, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -171,13 +175,28 @@ class DeviceCSC:
     rowidx: torch.Tensor          # uint16 storage (int16 tensor) [>= nnz]
     vals: torch.Tensor | None = None
     nv: DeviceNVFP4 | None = None
+    codes8: torch.Tensor | None = None     # uint8[capacity] FP8 / INT8 codes
+    col_scale: torch.Tensor | None = None  # float32[d_out]
+    code_kind: str | None = None           # "fp8" or "int8"
 
     def desc(self) -> Csc:
         if self.nv is not None:
             return Csc(self.k, self.d_out, self.nnz, DFS_NVFP4, 0, self.colptr.data_ptr(),
-                       self.rowidx.data_ptr(), None, self.nv.nv())
+                       self.rowidx.data_ptr(), None, self.nv.nv(), None)
+        if self.codes8 is not None:
+            return Csc(self.k, self.d_out, self.nnz, CODE8[self.code_kind], 0,
+                       self.colptr.data_ptr(), self.rowidx.data_ptr(), self.codes8.data_ptr(),
+                       NV(), self.col_scale.data_ptr())
         return Csc(self.k, self.d_out, self.nnz, _dt(self.vals), 0, self.colptr.data_ptr(),
-                   self.rowidx.data_ptr(), self.vals.data_ptr(), NV())
+                   self.rowidx.data_ptr(), self.vals.data_ptr(), NV(), None)
+
+    @property
+    def fmt(self) -> str:
+        if self.nv is not None:
+            return "nvfp4"
+        if self.codes8 is not None:
+            return self.code_kind
+        return "f16" if self.vals.dtype == torch.float16 else "f32"
 
 
 def dict_csc_capacity(nnz: int) -> int:
@@ -237,6 +256,26 @@ def csc_to_nvfp4(c: DeviceCSC, stream=None) -> DeviceCSC:
     """Quantise a DeviceCSC's values (CSC order) to NVFP4, support unchanged."""
     v = c.vals[:c.nnz].float().contiguous()
     return DeviceCSC(c.k, c.d_out, c.nnz, c.colptr, c.rowidx, nv=nvfp4_pack(v, stream))
+
+
+def csc_quantize8(c: DeviceCSC, kind: str, stream=None) -> DeviceCSC:
+    """Quantise a DeviceCSC's f16/f32 values to 8-bit codes (``kind`` "fp8"
+    or "int8", one scale per column); support shared with ``c``."""
+    if kind not in CODE8:
+        raise ValueError(kind)
+    dev = c.colptr.device
+    codes = torch.zeros(dict_csc_capacity(c.nnz), dtype=torch.uint8, device=dev)
+    scale = torch.empty(c.d_out, dtype=torch.float32, device=dev)
+    ws_n = C.c_size_t(0)
+    _check("dict_csc_quantize8_workspace_size",
+           lib().dict_csc_quantize8_workspace_size(c.d_out, C.byref(ws_n)))
+    ws = torch.empty(ws_n.value, dtype=torch.uint8, device=dev)
+    d = c.desc()
+    _check("dict_csc_quantize8",
+           lib().dict_csc_quantize8(C.byref(d), CODE8[kind], codes.data_ptr(), scale.data_ptr(),
+                                    ws.data_ptr(), ws_n.value, _stream(stream)))
+    return DeviceCSC(c.k, c.d_out, c.nnz, c.colptr, c.rowidx, codes8=codes, col_scale=scale,
+                     code_kind=kind)
 
 
 # ----------------------------------------------------------------- forward
@@ -342,7 +381,15 @@ def to_device_dict(atoms_np, device, nvfp4: bool = False) -> DeviceDict:
     return DeviceDict.from_atoms(t)
 
 
-def to_device_csc(dense_np, device, nvfp4: bool = False) -> DeviceCSC:
-    """Dense numpy coefficients (k, d_out) -> DeviceCSC packed on the GPU."""
+def to_device_csc(dense_np, device, nvfp4: bool = False, fmt: str | None = None) -> DeviceCSC:
+    """Dense numpy coefficients (k, d_out) -> DeviceCSC packed on the GPU.
+    ``fmt``: None (the dense dtype, or NVFP4 when ``nvfp4``), "nvfp4", "fp8"
+    or "int8" (values quantised by the library's own packers)."""
     c = dict_pack_csc(torch.from_numpy(dense_np).to(device))
-    return csc_to_nvfp4(c) if nvfp4 else c
+    if fmt is None and nvfp4:
+        fmt = "nvfp4"
+    if fmt == "nvfp4":
+        return csc_to_nvfp4(c)
+    if fmt in CODE8:
+        return csc_quantize8(c, fmt)
+    return c

@@ -28,7 +28,7 @@ ARCH = os.environ.get("DFS_OFFLOAD_ARCH", "gfx950")
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-PER_FILE = {"nvfp4.hip": ["-ffp-contract=off"]}
+PER_FILE = {"nvfp4.hip": ["-ffp-contract=off"], "quant8.hip": ["-ffp-contract=off"]}
 
 
 def _hipcc() -> str:

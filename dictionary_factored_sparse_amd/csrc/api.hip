@@ -42,6 +42,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t esize(int32_t dt) { return dt == DFS_F32 ? 4 : 2; }
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 bool is_act_dtype(int32_t dt) { return dt == DFS_F16 || dt == DFS_F32; }
+bool is_code8(int32_t dt) { return dt == DFS_FP8 || dt == DFS_INT8; }
 
 dfs_status check_nvfp4(const dfs_nvfp4& nv) {
   if (!nv.codes || !nv.scales || !nv.tensor_scale) return DFS_E_INVALID;
@@ -81,7 +82,8 @@ dfs_status check_csc(const dfs_csc* C, int32_t k, int32_t d_out) {
     else if (!C->nv.tensor_scale) return DFS_E_INVALID;
     return DFS_OK;
   }
-  if (!is_act_dtype(C->dtype)) return DFS_E_UNSUPPORTED;
+  if (!is_act_dtype(C->dtype) && !is_code8(C->dtype)) return DFS_E_UNSUPPORTED;
+  if (is_code8(C->dtype) && !C->col_scale) return DFS_E_INVALID;
   if (C->nnz > 0) {
     if (!C->vals) return DFS_E_INVALID;
     if (!aligned16(C->vals)) return DFS_E_ALIGN;
@@ -160,6 +162,9 @@ ZcLaunch make_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc
       a.vals[i] = C[i].nv.codes;
       a.vscales[i] = C[i].nv.scales;
       a.vts[i] = C[i].nv.tensor_scale;
+    } else if (is_code8(C[i].dtype)) {
+      a.vals[i] = C[i].vals;
+      a.vts[i] = C[i].col_scale;
     } else {
       a.vals[i] = C[i].vals;
     }
@@ -235,7 +240,7 @@ const char* dfs_status_str(dfs_status st) {
 
 int32_t dfs_last_hip_error(void) { return g_last_hip; }
 
-int32_t dfs_version(void) { return 200; }
+int32_t dfs_version(void) { return 300; }
 
 int64_t dict_csc_capacity(int64_t nnz) {
   if (nnz < 8) return 8;
@@ -272,6 +277,36 @@ dfs_status dict_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out,
   if (!rowidx) return DFS_OK;
   if (capacity < dict_csc_capacity(total)) return DFS_E_RANGE;
   DFS_HIP(launch_pack_csc_scatter(C, dtype, k, d_out, ldc, rowidx, vals, ws, s));
+  return DFS_OK;
+}
+
+dfs_status dict_csc_quantize8_workspace_size(int32_t d_out, size_t* bytes) {
+  if (!bytes || d_out <= 0) return DFS_E_INVALID;
+  *bytes = quant8_ws_bytes(d_out);
+  return DFS_OK;
+}
+
+dfs_status dict_csc_quantize8(const dfs_csc* src, int32_t dtype, uint8_t* codes, float* col_scale,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (!src || !col_scale) return DFS_E_INVALID;
+  if (!is_code8(dtype)) return DFS_E_UNSUPPORTED;
+  if (!is_act_dtype(src->dtype)) return DFS_E_UNSUPPORTED;
+  if (src->k <= 0) return DFS_E_INVALID;
+  if (src->k > kMaxK) return DFS_E_RANGE;
+  DFS_TRY(check_csc(src, src->k, src->d_out));
+  if (src->nnz > 0) {
+    if (!codes) return DFS_E_INVALID;
+    if (!aligned16(codes)) return DFS_E_ALIGN;
+  }
+  if (!ws || ws_bytes < quant8_ws_bytes(src->d_out)) return DFS_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  DFS_HIP(launch_quant8_amax(src->vals, src->dtype, src->colptr, src->nnz, src->d_out, ws, s));
+  uint32_t bad = 0;
+  DFS_HIP(hipMemcpyAsync(&bad, ws, sizeof(bad), hipMemcpyDeviceToHost, s));
+  DFS_HIP(hipStreamSynchronize(s));
+  if (bad != 0) return DFS_E_INVALID;
+  DFS_HIP(launch_quant8_encode(src->vals, src->dtype, src->colptr, src->nnz, src->d_out, dtype,
+                               ws, codes, col_scale, s));
   return DFS_OK;
 }
 

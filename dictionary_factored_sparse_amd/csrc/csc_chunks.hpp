@@ -2,8 +2,9 @@
 //
 // The coefficient kernels read C_l as aligned groups of 8 consecutive stored
 // entries: 16 bytes of uint16 row indices plus the matching values (16 bytes
-// of f16, 32 bytes of f32, or 4 bytes of E2M1 codes and the one E4M3 block
-// scale that covers them: 8 divides the 16-entry NVFP4 block).  The arrays
+// of f16, 32 bytes of f32, 8 bytes of FP8 or INT8 codes, or 4 bytes of E2M1
+// codes and the one E4M3 block scale that covers them: 8 divides the
+// 16-entry NVFP4 block).  The arrays
 // are allocated for a whole number of chunks (dict_csc_capacity), so every
 // chunk is one unconditional load; entries past nnz are masked by the caller.
 // `p` is always a multiple of 8 below the capacity.
@@ -80,6 +81,44 @@ struct ValChunk<DFS_NVFP4> {
       default: v = e2m1x2_f2<3>(word); break;
     }
     return v[i & 1] * s;
+  }
+};
+
+// FP8 (E4M3) and INT8 codes: 8 bytes per chunk.  get() returns the code's
+// value without its column scale; the kernels multiply the finished dot
+// product by col_scale[j] * kCodeScale<VT>.  An E4M3 code, its exponent and
+// mantissa bits moved into the matching positions of an f16 (exponent field
+// e, top three fraction bits m), is the f16 value 2^(e-15) (1 + m/8), or
+// 2^-14 m/8 when e = 0: exactly 2^-8 times the E4M3 value, subnormals
+// included.  So the decode is two bit operations and an f16 that multiplies
+// straight into fp32 (v_fma_mix), and kCodeScale<DFS_FP8> = 256 restores the
+// factor, exactly.  INT8 codes are exact in f16 and fp32.
+template <int VT>
+constexpr bool kIsCode8 = VT == DFS_FP8 || VT == DFS_INT8;
+template <int VT>
+constexpr float kCodeScale = VT == DFS_FP8 ? 256.0f : 1.0f;
+
+template <>
+struct ValChunk<DFS_FP8> {
+  u2 w;
+  __device__ __forceinline__ void load(const void* vals, const uint8_t*, int64_t p) {
+    w = *gptr(reinterpret_cast<const u2*>((const uint8_t*)vals + p));
+  }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t b = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    const uint32_t h = ((b & 0x7Fu) << 7) | ((b & 0x80u) << 8);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  }
+};
+
+template <>
+struct ValChunk<DFS_INT8> {
+  u2 w;
+  __device__ __forceinline__ void load(const void* vals, const uint8_t*, int64_t p) {
+    w = *gptr(reinterpret_cast<const u2*>((const uint8_t*)vals + p));
+  }
+  __device__ __forceinline__ float get(int i) const {
+    return (float)(int8_t)(uint8_t)(w[i >> 2] >> (8 * (i & 3)));
   }
 };
 

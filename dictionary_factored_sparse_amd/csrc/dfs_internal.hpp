@@ -20,6 +20,7 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ DPP
 // Cross-lane moves inside a 16-lane DPP row.  Controls: quad_perm [1,0,3,2]
@@ -54,6 +55,25 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t e = (c >> 3) & 15u, m = c & 7u;
   float mag = e == 0 ? (float)m * 0x1p-9f : __builtin_ldexpf((float)(8u + m), (int)e - 10);
   return (c & 0x80u) ? -mag : mag;
+}
+
+// Nearest E4M3 code for s >= 0 (finite), ties to even, saturating at 448
+// (the NVFP4 block scales and the FP8 coefficient codes).
+__device__ __forceinline__ uint32_t e4m3_rne_satfinite(float s) {
+  if (s >= 448.0f) return 0x7Eu;
+  const uint32_t b = __float_as_uint(s);
+  const int e = (int)(b >> 23) - 127;
+  if (e < -6) {
+    // subnormal range of E4M3 (and fp32 subnormals): multiples of 2^-9;
+    // the scaling by 2^9 is exact and rintf rounds half to even.  A result
+    // of 8 is the smallest normal, code 0x08.
+    return (uint32_t)__builtin_rintf(s * 512.0f);
+  }
+  const uint32_t mant = b & 0x7FFFFFu;
+  const uint32_t keep = mant >> 20, rest = mant & 0xFFFFFu;
+  uint32_t code = ((uint32_t)(e + 7) << 3) | keep;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) code += 1;  // may carry
+  return code > 0x7Eu ? 0x7Eu : code;
 }
 
 // Two E2M1 codes (byte SEL of `word`: low nibble -> .x, high nibble -> .y)
@@ -117,7 +137,7 @@ struct ZcLaunch {
   const uint16_t* rowidx[kMaxLayers];
   const void* vals[kMaxLayers];       // f16/f32 values, or NVFP4 codes
   const uint8_t* vscales[kMaxLayers]; // NVFP4 block scales
-  const float* vts[kMaxLayers];       // NVFP4 tensor scale
+  const float* vts[kMaxLayers];       // NVFP4 tensor scale, or FP8/INT8 column scales
   void* Y[kMaxLayers];
   int32_t ydt;
   int64_t ldy;
@@ -152,6 +172,14 @@ hipError_t launch_pack_csc_count(const void* C, int32_t dtype, int32_t k, int32_
 hipError_t launch_pack_csc_scatter(const void* C, int32_t dtype, int32_t k, int32_t d_out,
                                    int64_t ldc, uint16_t* rowidx, void* vals, const void* ws,
                                    hipStream_t s);
+
+// 8-bit coefficient codes (FP8 / INT8), one scale per column
+size_t quant8_ws_bytes(int32_t d_out);
+hipError_t launch_quant8_amax(const void* vals, int32_t dt, const int32_t* colptr, int64_t nnz,
+                              int32_t d_out, void* ws, hipStream_t s);
+hipError_t launch_quant8_encode(const void* vals, int32_t dt, const int32_t* colptr, int64_t nnz,
+                                int32_t d_out, int32_t kind, const void* ws, uint8_t* codes,
+                                float* col_scale, hipStream_t s);
 
 // NVFP4 packing
 size_t nvfp4_ws_bytes(int64_t n);

@@ -17,6 +17,8 @@
 // C stream, instead of a second launch.  The grid never exceeds one
 // workgroup per CU, so every workgroup is resident; every wait is bounded
 // anyway (see receive_z), so the kernel always terminates.
+#include <type_traits>
+
 #include "csc_chunks.hpp"
 #include "gemv_common.hpp"
 
@@ -152,7 +154,7 @@ struct FusedArgs {
   const uint16_t* rowidx[kFusedMaxLayers];
   const void* vals[kFusedMaxLayers];
   const uint8_t* vscales[kFusedMaxLayers];
-  const float* vts[kFusedMaxLayers];
+  const float* vts[kFusedMaxLayers];  // NVFP4 tensor scale, or FP8/INT8 column scales
   void* Y[kFusedMaxLayers];
   int64_t nnz[kFusedMaxLayers];
   const float* dts;
@@ -164,13 +166,20 @@ struct FusedArgs {
   int32_t G;  // workgroups in the grid
 };
 
+// A column's entry in LDS: [start, end) of its stored entries, and for 8-bit
+// codes the bits of its scale (times kCodeScale).
+template <int VT>
+using ColEntry = typename std::conditional<kIsCode8<VT>, int4, int2>::type;
+
 template <int DT, int VT, int RT, int A, int NX>
 __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   using Cf = Cfg<DT, DFS_F16, RT>;
+  using CE_t = ColEntry<VT>;
+  constexpr bool Q8 = kIsCode8<VT>;
   constexpr int CE = Cf::CE, SEGC = Cf::SEGC, SEG = Cf::SEG;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   LayerRow* lt = reinterpret_cast<LayerRow*>(smem);            // [kFusedMaxLayers]
-  int2* cse = reinterpret_cast<int2*>(smem + kLayerTableBytes);  // [ncols] column [start, end)
+  CE_t* cse = reinterpret_cast<CE_t*>(smem + kLayerTableBytes);  // [ncols]
   char* big = smem + kLayerTableBytes + f.col_bytes;           // X rows, later all of Z
   _Float16* xs = reinterpret_cast<_Float16*>(big);
   float* zs = reinterpret_cast<float*>(big);
@@ -182,9 +191,15 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   // Every kernel argument needed before the first wait is fetched in one
   // batch of scalar loads (one round trip instead of one per first use).
   const int d_in = f.d_in, k = f.k, d_out = f.d_out, nl = f.n_layers;
-  asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
-               "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
-               "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G));
+  if constexpr (Q8)  // the column scales are read with the column bounds
+    asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
+                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
+                 "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G), "s"(f.vts[0]),
+                 "s"(f.vts[1]), "s"(f.vts[2]), "s"(f.vts[3]));
+  else
+    asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
+                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
+                 "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G));
   static_assert(SEG % (8 * kFT) == 0, "an X row is a whole number of 512-thread passes");
   constexpr int NR = NX / RT;  // passes of the workgroup per X row
   static_assert(NR * RT == NX, "X register count");
@@ -241,6 +256,14 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   for (int i = 1; i < kFusedMaxLayers; ++i)
     if (cl == i) cp = sreg_ptr(f.colptr[i]);
   const int s_raw = gptr(cp)[cj], e_raw = gptr(cp)[cj + 1];
+  float cs_raw = 1.0f;
+  if constexpr (Q8) {
+    const float* vp = sreg_ptr(f.vts[0]);
+#pragma unroll
+    for (int i = 1; i < kFusedMaxLayers; ++i)
+      if (cl == i) vp = sreg_ptr(f.vts[i]);
+    cs_raw = gptr(vp)[cj];
+  }
 
   // ---- 3. this workgroup's atoms of D_g.  Out-of-range reads are clamped,
   // not masked: an atom past k reads atom k - 1 (its Z is never published),
@@ -320,7 +343,11 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   if (tid < ncols) {
     const int nz = (int)lt[cl].nnz;
     const int s0 = min(max(s_raw, 0), nz);
-    cse[tid] = make_int2(s0, min(max(e_raw, s0), nz));
+    const int e0 = min(max(e_raw, s0), nz);
+    if constexpr (Q8)
+      cse[tid] = make_int4(s0, e0, __float_as_int(cs_raw * kCodeScale<VT>), 0);
+    else
+      cse[tid] = make_int2(s0, e0);
   }
   // A lane loads only the chunks inside its column: here nothing waits for
   // an exact count of these loads (the Z polls issued after them wait for
@@ -366,7 +393,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
     const int ci = r * kSlots + slot;
     if (ci < ncols) {
-      const int2 se = cse[ci];
+      const CE_t se = cse[ci];
       const LayerRow& L = lt[(c0 + ci) / d_out];
       load_chunks(ic, vc, se.x, se.y, L.rowidx, L.vals, L.vsc);
     }
@@ -386,11 +413,13 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int r) {
     const int ci = r * kSlots + slot;
     int s = 0, e = 0, l = 0;
+    float ts = 1.0f;
     if (ci < ncols) {
-      const int2 se = cse[ci];
+      const CE_t se = cse[ci];
       s = se.x;
       e = se.y;
       l = (c0 + ci) / d_out;
+      if constexpr (Q8) ts = __int_as_float(se.z);
     }
     const float* zl = zs + l * k;
     float sum = 0.0f;
@@ -418,7 +447,6 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     }
     sum = row16_sum(sum);
     if (ci < ncols && g == 0) {
-      float ts = 1.0f;
       if constexpr (VT == DFS_NVFP4) ts = *gptr(lt[l].vts);
       const int j = c0 + ci - l * d_out;
       void* y = lt[l].Y;
@@ -457,6 +485,7 @@ struct Plan {
 };
 
 bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
+  const bool q8 = zc.vdt == DFS_FP8 || zc.vdt == DFS_INT8;
   const int G = device_cus();
   if (G <= 0 || G > kMaxFusedGroups) return false;
   const int nl = zc.n_layers;
@@ -482,7 +511,7 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   p->A = A;
   p->RT = RT;
   p->NX = NX;
-  p->col_bytes = ((size_t)max_cols * 8 + 15) / 16 * 16;
+  p->col_bytes = ((size_t)max_cols * (q8 ? 16 : 8) + 15) / 16 * 16;
   p->smem = kLayerTableBytes + p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
   return p->smem <= 128 * 1024;
 }
@@ -524,6 +553,16 @@ hipError_t launch2(FusedArgs f, const Plan& p, hipStream_t s) {
   }
 }
 
+template <int DT>
+hipError_t launch1(FusedArgs f, const Plan& p, int vdt, hipStream_t s) {
+  switch (vdt) {
+    case DFS_NVFP4: return launch2<DT, DFS_NVFP4>(f, p, s);
+    case DFS_FP8: return launch2<DT, DFS_FP8>(f, p, s);
+    case DFS_INT8: return launch2<DT, DFS_INT8>(f, p, s);
+    default: return launch2<DT, DFS_F16>(f, p, s);
+  }
+}
+
 }  // namespace
 
 bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc) {
@@ -531,7 +570,8 @@ bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc) {
   if (zc.n_layers < 1 || zc.n_layers > kFusedMaxLayers) return false;
   if (xd.xdt != DFS_F16) return false;
   if (xd.ddt != DFS_F16 && xd.ddt != DFS_NVFP4) return false;
-  if (zc.vdt != DFS_F16 && zc.vdt != DFS_NVFP4) return false;
+  if (zc.vdt != DFS_F16 && zc.vdt != DFS_NVFP4 && zc.vdt != DFS_FP8 && zc.vdt != DFS_INT8)
+    return false;
   if (xd.d_in % (xd.ddt == DFS_NVFP4 ? 32 : 8) != 0 || xd.k % 4 != 0) return false;
   Plan p;
   return plan(xd, zc, &p);
@@ -565,11 +605,8 @@ hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, float* zw
   f.ydt = zc.ydt;
   f.spin_limit = 1u << 22;
   f.col_bytes = 0;
-  if (xd.ddt == DFS_NVFP4)
-    return zc.vdt == DFS_NVFP4 ? launch2<DFS_NVFP4, DFS_NVFP4>(f, p, s)
-                               : launch2<DFS_NVFP4, DFS_F16>(f, p, s);
-  return zc.vdt == DFS_NVFP4 ? launch2<DFS_F16, DFS_NVFP4>(f, p, s)
-                             : launch2<DFS_F16, DFS_F16>(f, p, s);
+  return xd.ddt == DFS_NVFP4 ? launch1<DFS_NVFP4>(f, p, zc.vdt, s)
+                             : launch1<DFS_F16>(f, p, zc.vdt, s);
 }
 
 }  // namespace dfs

@@ -84,24 +84,6 @@ __global__ __launch_bounds__(kThreads) void amax_final_kernel(const uint32_t* pa
   }
 }
 
-// Nearest E4M3 code for s >= 0 (finite), ties to even, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_rne_satfinite(float s) {
-  if (s >= 448.0f) return 0x7Eu;
-  const uint32_t b = __float_as_uint(s);
-  const int e = (int)(b >> 23) - 127;
-  if (e < -6) {
-    // subnormal range of E4M3 (and fp32 subnormals): multiples of 2^-9;
-    // the scaling by 2^9 is exact and rintf rounds half to even.  A result
-    // of 8 is the smallest normal, code 0x08.
-    return (uint32_t)__builtin_rintf(s * 512.0f);
-  }
-  const uint32_t mant = b & 0x7FFFFFu;
-  const uint32_t keep = mant >> 20, rest = mant & 0xFFFFFu;
-  uint32_t code = ((uint32_t)(e + 7) << 3) | keep;
-  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) code += 1;  // may carry
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
 // Nearest E2M1 magnitude code to a = |v| (ties to even code, saturating at 6).
 __device__ __forceinline__ uint32_t e2m1_rne_sat(float a) {
   return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +

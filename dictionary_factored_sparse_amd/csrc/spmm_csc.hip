@@ -23,9 +23,10 @@ namespace dfs {
 namespace {
 
 constexpr int kThreads = 512;
-// 8-entry chunks per batch (NVFP4 decodes on use and needs the registers)
+// 8-entry chunks per batch (NVFP4 and 8-bit codes decode on use and need
+// the registers)
 template <int VT>
-constexpr int kUnroll = VT == DFS_NVFP4 ? 2 : 4;
+constexpr int kUnroll = (VT == DFS_NVFP4 || kIsCode8<VT>) ? 2 : 4;
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
@@ -125,6 +126,10 @@ __global__ __launch_bounds__(kThreads) void spmm_csc_kernel(ZcLaunch a) {
   const void* vals = a.vals[layer];
   const uint8_t* vsc = a.vscales[layer];
   const int64_t lastc = last_chunk(e);
+  // 8-bit codes: the column's scale, loaded with the column bounds
+  float cs = 1.0f;
+  if constexpr (kIsCode8<VT>)
+    if (col_ok) cs = a.vts[layer][col] * kCodeScale<VT>;
 
   IdxChunk ia[kU], ib[kU];
   ValChunk<VT> va[kU], vb[kU];
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void spmm_csc_kernel(ZcLaunch a) {
   }
 
   if (col_ok) {
-    float ts = 1.0f;
+    float ts = cs;
     if constexpr (VT == DFS_NVFP4) ts = *a.vts[layer];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -244,6 +249,10 @@ hipError_t launch_spmm_csc(const ZcLaunch& a, hipStream_t s) {
       return launch1<DFS_F16>(a, s);
     case DFS_F32:
       return launch1<DFS_F32>(a, s);
+    case DFS_FP8:
+      return launch1<DFS_FP8>(a, s);
+    case DFS_INT8:
+      return launch1<DFS_INT8>(a, s);
     default:
       return launch1<DFS_NVFP4>(a, s);
   }

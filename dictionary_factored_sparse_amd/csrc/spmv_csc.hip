@@ -36,7 +36,7 @@ constexpr int threads_of() { return ZH ? kThreadsH : kThreads; }
 // tiles keep fewer chunks so that the accumulators and Z reads fit.
 template <int VT, int TT, bool ZH>
 struct Unroll {
-  static constexpr int U = ZH ? (TT >= 16 ? 2 : TT >= 8 ? 3 : (VT == DFS_F32 ? 3 : 4))
+  static constexpr int U = ZH ? (TT >= 16 ? 2 : TT >= 8 ? 3 : (VT == DFS_F32 || VT == DFS_INT8 ? 3 : 4))
                               : TT >= 16 ? 1 : TT >= 8 ? 2 : TT >= 4 ? 4 : (VT == DFS_F32 ? 3 : 6);
 };
 
@@ -194,14 +194,17 @@ __global__ __launch_bounds__(threads_of<ZH>()) void spmv_csc_kernel(ZcLaunch a,
   struct Col {
     int col, s, e, first;
     int64_t lastc;
+    float cs;  // 8-bit codes: the column's scale (times kCodeScale)
   };
   auto col_of = [&](int cg) {
     Col c;
     c.col = cg * CPG + wave * 4 + (lane >> 4);
     c.s = c.e = 0;
+    c.cs = 1.0f;
     if (c.col < a.d_out) {  // clamp to [0, nnz]: a malformed colptr cannot index out of bounds
       c.s = (int)min<int64_t>(max(a.colptr[layer][c.col], 0), nnz);
       c.e = (int)min<int64_t>(max(a.colptr[layer][c.col + 1], c.s), nnz);
+      if constexpr (kIsCode8<VT>) c.cs = a.vts[layer][c.col] * kCodeScale<VT>;
     }
     c.first = (c.s & ~7) + g * 8;
     c.lastc = last_chunk(c.e);
@@ -285,7 +288,10 @@ __global__ __launch_bounds__(threads_of<ZH>()) void spmv_csc_kernel(ZcLaunch a,
       }
       if (c.col < a.d_out && g < rows) {
         const int64_t o = (int64_t)(t0 + g) * a.ldy + c.col;
-        out *= ts;
+        if constexpr (kIsCode8<VT>)
+          out *= c.cs;
+        else
+          out *= ts;
         if (a.ydt == DFS_F16)
           ((_Float16*)a.Y[layer])[o] = (_Float16)out;
         else
@@ -368,6 +374,10 @@ hipError_t launch_spmv_csc(const ZcLaunch& a, hipStream_t s) {
       return launch1<DFS_F16>(a, s);
     case DFS_F32:
       return launch1<DFS_F32>(a, s);
+    case DFS_FP8:
+      return launch1<DFS_FP8>(a, s);
+    case DFS_INT8:
+      return launch1<DFS_INT8>(a, s);
     default:
       return launch1<DFS_NVFP4>(a, s);
   }

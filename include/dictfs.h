@@ -9,7 +9,10 @@
  * "Prerequisites: projections, rank and calibration", Eq. (1)).  Either
  * factor may be stored in NVFP4: 4-bit E2M1 values with one 8-bit E4M3 scale
  * per block of sixteen values (same review, "From retained values to measured
- * decoding"), plus one fp32 tensor scale.
+ * decoding"), plus one fp32 tensor scale.  The coefficients may also be
+ * 8-bit codes, FP8 (E4M3) or INT8, each column with one fp32 scale: the
+ * mixed-precision pairs of the paper's figures and tables page, Table 4
+ * (NVFP4 dictionary with FP16, FP8 or INT8 coefficients).
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -51,8 +54,13 @@ typedef enum {
   DFS_E_HIP = 6          /* the HIP runtime returned an error */
 } dfs_status;
 
-/* Element types. */
-enum { DFS_F32 = 0, DFS_F16 = 1, DFS_NVFP4 = 2 };
+/* Element types.  DFS_FP8 and DFS_INT8 are coefficient (dfs_csc) types only:
+ *   DFS_FP8   one E4M3 code per value (sign bit 7, 4-bit exponent with bias
+ *             7, 3-bit mantissa, exponent 0 subnormal; largest finite 448).
+ *             The codes 0x7F and 0xFF (NaN in E4M3) are not supported: the
+ *             kernels decode them as +-480.
+ *   DFS_INT8  one two's-complement byte per value. */
+enum { DFS_F32 = 0, DFS_F16 = 1, DFS_NVFP4 = 2, DFS_FP8 = 3, DFS_INT8 = 4 };
 
 /* An NVFP4 tensor of n elements (device pointers):
  *   codes[(n+1)/2]   two E2M1 codes per byte, element 2i in the low nibble;
@@ -89,14 +97,17 @@ typedef struct {
 /* Coefficients C_l, k x d_out, column-compressed (CSC):
  *   colptr[d_out+1] int32, colptr[0] = 0, non-decreasing, colptr[d_out] = nnz;
  *   rowidx[nnz] uint16 atom indices, strictly increasing within a column;
- *   values in CSC order: `vals` (F16/F32) or `nv` (NVFP4, blocks of 16 run
- *   over the flat CSC value array and may straddle column boundaries).
+ *   values in CSC order: `vals` (F16/F32), `nv` (NVFP4, blocks of 16 run
+ *   over the flat CSC value array and may straddle column boundaries), or
+ *   `vals` as one code byte per entry with `col_scale` (FP8/INT8): entry p
+ *   of column j is value(code_p) * col_scale[j], col_scale[d_out] fp32.
  * k <= 65536 (16-bit indices), nnz < 2^31.
  * Padding: the forward kernels read rowidx and the values in aligned chunks
  * of 8 entries, so rowidx and vals must be allocated for
  * dict_csc_capacity(nnz) entries (NVFP4 codes: half that many bytes; block
- * scales: ceil(nnz / 16) bytes).  Entries past nnz are never used and may
- * hold anything.  The caller owns all arrays. */
+ * scales: ceil(nnz / 16) bytes; FP8/INT8 codes: that many bytes).  Entries
+ * past nnz are never used and may hold anything.  The caller owns all
+ * arrays. */
 typedef struct {
   int32_t k;
   int32_t d_out;
@@ -107,6 +118,7 @@ typedef struct {
   const uint16_t* rowidx;
   const void* vals;
   dfs_nvfp4 nv;
+  const float* col_scale; /* FP8 / INT8 only: one scale per column */
 } dfs_csc;
 
 /* ---------------------------------------------------------------------- */
@@ -136,6 +148,29 @@ dfs_status dict_pack_csc_workspace_size(int32_t k, int32_t d_out, size_t* bytes)
 dfs_status dict_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out, int64_t ldc,
                          int32_t* colptr, uint16_t* rowidx, void* vals, int64_t capacity,
                          int64_t* nnz_host, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes dict_csc_quantize8 needs for d_out columns. */
+dfs_status dict_csc_quantize8_workspace_size(int32_t d_out, size_t* bytes);
+
+/* Quantise the values of a CSC (src->dtype F16 or F32, src->vals holding
+ * nnz values in CSC order) to 8-bit codes, `dtype` DFS_FP8 or DFS_INT8, with
+ * one scale per column: the coefficient formats of the mixed-precision rows
+ * of Table 4 on the paper's figures and tables page.  The pages do not fix
+ * the scaling; this library uses, each step a correctly rounded fp32
+ * operation:
+ *   amax_j = max |v| over column j's stored values;
+ *   s_j = amax_j / 448 (FP8) or amax_j / 127 (INT8), or 1 if that is 0;
+ *   q = v / s_j;
+ *   FP8:  code = (sign bit of v) << 7 | E4M3 magnitude code nearest to |q|
+ *         (ties to even, saturating at 448);
+ *   INT8: code = integer nearest to q (ties to even), clamped to [-127, 127].
+ * Writes codes[0..nnz) (device, 16-byte aligned; allocate
+ * dict_csc_capacity(nnz) bytes to pass it to a forward call) and
+ * col_scale[0..d_out) (device).  The support (colptr, rowidx) is unchanged
+ * and shared with src.  Values holding NaN or Inf give DFS_E_INVALID and
+ * nothing written; detecting it synchronises `stream`. */
+dfs_status dict_csc_quantize8(const dfs_csc* src, int32_t dtype, uint8_t* codes, float* col_scale,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes nvfp4_pack needs for n elements. */
 dfs_status nvfp4_pack_workspace_size(int64_t n, size_t* bytes);
@@ -189,8 +224,9 @@ dfs_status dict_proj_forward(const void* X, int32_t xdt, int32_t T, int64_t ldx,
  * for l in [0, n_layers): Y[l] = (X[l] D_g) C[l].  The n_layers * T rows are
  * contracted against D_g in one pass, so D_g is read from memory once per
  * group rather than once per layer; then one launch applies every C_l.
- * Decode (T = 1, <= 4 layers, f16 X, f16/NVFP4 D and C) runs both halves in
- * a single launch, Z handed between workgroups through the workspace
+ * Decode (T = 1, <= 4 layers, f16 X, f16/NVFP4 D, f16/NVFP4/FP8/INT8 C)
+ * runs both halves in a single launch, Z handed between workgroups through
+ * the workspace
  * (environment variable DFS_DECODE_PATH=two selects the two-launch path).
  *   X, Y: host arrays of n_layers device pointers; C: host array of n_layers
  *   descriptors sharing k and d_out.  1 <= n_layers <= 16 (the largest

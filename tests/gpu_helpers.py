@@ -35,7 +35,8 @@ def assert_close(y_gpu: torch.Tensor, y_ref: np.ndarray, what: str):
 
 
 def _fmts(nvfp4, dfmt, cfmt):
-    """Storage of (D, C): "plain" (the synth dtype) or "nvfp4"; `nvfp4` sets both."""
+    """Storage of (D, C): "plain" (the synth dtype) or "nvfp4"; C may also be
+    "fp8" or "int8" (8-bit codes, one scale per column); `nvfp4` sets both."""
     base = "nvfp4" if nvfp4 else "plain"
     return dfmt or base, cfmt or base
 
@@ -44,18 +45,21 @@ def device_group(g, nvfp4: bool = False, dfmt=None, cfmt=None):
     """Upload a synth.Group: D (atom-major), packed C_l, X_l."""
     dfmt, cfmt = _fmts(nvfp4, dfmt, cfmt)
     D = B.to_device_dict(g.D, DEV, nvfp4=dfmt == "nvfp4")
-    Cs = [B.to_device_csc(Cd, DEV, nvfp4=cfmt == "nvfp4") for Cd in g.Cs]
+    Cs = [B.to_device_csc(Cd, DEV, fmt=None if cfmt == "plain" else cfmt) for Cd in g.Cs]
     Xs = [torch.from_numpy(X).to(DEV) for X in g.Xs]
     return D, Cs, Xs
 
 
 def oracle_group(g, nvfp4: bool = False, rows=None, dfmt=None, cfmt=None):
-    """Oracle outputs for every layer (optionally for a subset of tokens); NVFP4
-    factors enter as the oracle's own quantisation of the same values."""
+    """Oracle outputs for every layer (optionally for a subset of tokens);
+    quantised factors enter as the oracle's own quantisation of the same
+    values."""
     dfmt, cfmt = _fmts(nvfp4, dfmt, cfmt)
     D = O.nvfp4_pack(g.D.astype(np.float32)) if dfmt == "nvfp4" else g.D
     if cfmt == "nvfp4":
         cs = [O.csc_to_nvfp4(O.pack_csc(Cd.astype(np.float32))) for Cd in g.Cs]
+    elif cfmt in ("fp8", "int8"):
+        cs = [O.quantize8_csc(O.pack_csc(Cd), cfmt) for Cd in g.Cs]
     else:
         cs = [O.pack_csc(Cd) for Cd in g.Cs]
     Xs = g.Xs if rows is None else [X[rows] for X in g.Xs]

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert fns == set(B.SYMBOLS)
     for name in fns:
         assert hasattr(L, name), name
-    assert L.dfs_version() == 200
+    assert L.dfs_version() == 300
     assert L.dfs_status_str(0) == b"ok"
     assert L.dfs_status_str(6) == b"HIP runtime error"
 
@@ -49,8 +49,9 @@ def _dict(d_in=256, k=128, dtype=B.DFS_F16, data=P, ldd=None, nv=None):
     return B.Dict(d_in, k, dtype, 0, data, d_in if ldd is None else ldd, nv or B.NV())
 
 
-def _csc(k=128, d_out=64, nnz=100, dtype=B.DFS_F16, colptr=P, rowidx=P, vals=P, nv=None):
-    return B.Csc(k, d_out, nnz, dtype, 0, colptr, rowidx, vals, nv or B.NV())
+def _csc(k=128, d_out=64, nnz=100, dtype=B.DFS_F16, colptr=P, rowidx=P, vals=P, nv=None,
+         col_scale=None):
+    return B.Csc(k, d_out, nnz, dtype, 0, colptr, rowidx, vals, nv or B.NV(), col_scale)
 
 
 def _group(n=1, X=P, xdt=B.DFS_F16, T=1, ldx=256, D=None, Cs=None, Y=P, ydt=B.DFS_F16, ldy=64,
@@ -98,6 +99,42 @@ def test_group_forward_validation():
     assert _group(D=_dict(d_in=272, dtype=B.DFS_NVFP4, data=None, nv=nv), ldx=272) == UNSUPPORTED
     assert _group(D=_dict(dtype=B.DFS_NVFP4, data=None, nv=B.NV(P + 1, P, P))) == ALIGN
     assert _group(D=_dict(dtype=B.DFS_NVFP4, data=None, nv=B.NV(P, 0, P))) == INVALID
+    # 8-bit coefficient codes need their column scales and aligned codes
+    for dt in (B.DFS_FP8, B.DFS_INT8):
+        assert _group(Cs=[_csc(dtype=dt)]) == INVALID            # no col_scale
+        assert _group(Cs=[_csc(dtype=dt, col_scale=P, vals=P + 8)]) == ALIGN
+        assert _group(Cs=[_csc(dtype=dt, col_scale=P, vals=0)]) == INVALID
+        assert _group(T=0, Cs=[_csc(dtype=dt, col_scale=P)]) == OK
+    # the 8-bit types are coefficient types only
+    assert _group(D=_dict(dtype=B.DFS_FP8)) == UNSUPPORTED
+    assert _group(xdt=B.DFS_INT8) == UNSUPPORTED
+
+
+def test_quantize8_validation():
+    L = B.lib()
+    n = C.c_size_t(0)
+    assert L.dict_csc_quantize8_workspace_size(0, C.byref(n)) == INVALID
+    assert L.dict_csc_quantize8_workspace_size(64, None) == INVALID
+    assert L.dict_csc_quantize8_workspace_size(64, C.byref(n)) == OK and n.value >= 64 * 4
+
+    def call(src=None, dt=B.DFS_FP8, codes=P, scale=P, ws=P, wsb=1 << 20):
+        src = _csc() if src is None else src
+        return L.dict_csc_quantize8(C.byref(src), dt, codes, scale, ws, wsb, None)
+
+    assert L.dict_csc_quantize8(None, B.DFS_FP8, P, P, P, 1 << 20, None) == INVALID
+    assert call(dt=B.DFS_F16) == UNSUPPORTED
+    assert call(dt=B.DFS_NVFP4) == UNSUPPORTED
+    assert call(src=_csc(dtype=B.DFS_NVFP4, nv=B.NV(P, P, P))) == UNSUPPORTED
+    assert call(src=_csc(dtype=B.DFS_FP8, col_scale=P)) == UNSUPPORTED   # already codes
+    assert call(scale=0) == INVALID
+    assert call(codes=0) == INVALID
+    assert call(codes=P + 4) == ALIGN
+    assert call(src=_csc(vals=P + 2)) == ALIGN
+    assert call(src=_csc(colptr=0)) == INVALID
+    assert call(src=_csc(k=0)) == INVALID
+    assert call(src=_csc(k=70000)) == RANGE
+    assert call(ws=0) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
 
 
 def test_proj_forward_validation():

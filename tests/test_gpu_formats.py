@@ -163,3 +163,53 @@ def test_pack_csc_capacity_too_small():
     assert st == 3 and nnz.value == 128
     torch.cuda.synchronize()
     assert bool((rowidx == 7).all())
+
+
+# ------------------------------------------------------------ 8-bit codes
+
+def _gpu_quant8(c, kind):
+    q = B.csc_quantize8(c, kind)
+    torch.cuda.synchronize()
+    return q.codes8[: c.nnz].cpu().numpy(), q.col_scale.cpu().numpy()
+
+
+@pytest.mark.parametrize("kind", ["fp8", "int8"])
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+@pytest.mark.parametrize("k,d_out,density,spread", [(128, 256, 0.25, 0.0), (2048, 4096, 0.3, 0.0),
+                                                    (65, 7, 0.5, 8.0), (300, 1, 0.9, 0.0),
+                                                    (64, 64, 0.0, 0.0), (3000, 37, 0.8, 12.0)])
+def test_quantize8_bit_exact(kind, dtype, k, d_out, density, spread):
+    say(f"case: dict_csc_quantize8 {kind} {np.dtype(dtype).name} k={k} d_out={d_out} "
+        f"density={density} spread={spread}")
+    rng = np.random.default_rng(k * 7 + d_out)
+    Cd = synth.coefficients(rng, k, d_out, density, np.float32)
+    if spread:  # columns spread over many binades (subnormal E4M3 codes appear)
+        Cd = Cd * np.exp2(rng.uniform(-spread, spread, d_out)).astype(np.float32)[None, :]
+    Cd = Cd.astype(dtype)
+    c = B.dict_pack_csc(torch.from_numpy(Cd).to(DEV))
+    codes, scale = _gpu_quant8(c, kind)
+    ref = O.quantize8_csc(O.pack_csc(Cd), kind).vals
+    assert np.array_equal(scale.view(np.uint32), ref.col_scale.view(np.uint32))
+    assert np.array_equal(codes, ref.codes)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "int8"])
+def test_quantize8_rejects_non_finite_and_writes_nothing(kind):
+    say(f"case: dict_csc_quantize8 {kind} with NaN / Inf")
+    import ctypes as C
+    for bad in (np.nan, -np.inf):
+        Cd = np.ones((16, 4), np.float32)
+        Cd[5, 2] = bad
+        c = B.dict_pack_csc(torch.from_numpy(Cd).to(DEV))
+        codes = torch.full((B.dict_csc_capacity(c.nnz),), 0xAB, dtype=torch.uint8, device=DEV)
+        scale = torch.full((4,), 7.0, dtype=torch.float32, device=DEV)
+        n = C.c_size_t(0)
+        assert B.lib().dict_csc_quantize8_workspace_size(4, C.byref(n)) == 0
+        ws = torch.empty(n.value, dtype=torch.uint8, device=DEV)
+        d = c.desc()
+        st = B.lib().dict_csc_quantize8(C.byref(d), B.CODE8[kind], codes.data_ptr(),
+                                        scale.data_ptr(), ws.data_ptr(), n.value,
+                                        torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert st == 1
+        assert bool((codes == 0xAB).all()) and bool((scale == 7.0).all())

@@ -304,6 +304,48 @@ def test_mixed_precision_factors(dfmt, cfmt):
         assert_close(Ys[l], ref, f"prefill layer {l}")
 
 
+@pytest.mark.parametrize("cfmt", ["fp8", "int8"])
+@pytest.mark.parametrize("dfmt", ["nvfp4", "plain"])
+def test_8bit_coefficients_every_path(dfmt, cfmt):
+    # Table 4's mixed-precision pairs (NVFP4 D with FP8 or INT8 C), and f16 D
+    # with the same codes: one-launch and two-launch decode, stacked-row SpMV
+    # (fp32 and f16 Z tiles), prefill SpMM with ragged token and column tiles
+    say(f"case: 8-bit coefficients, D {dfmt}, C {cfmt}")
+    g = synth.make_group("qproj", d_in=1024, d_out=776, k=512, T=1, n_layers=2)
+    out = _both_paths(g, dfmt=dfmt, cfmt=cfmt)
+    refs = oracle_group(g, dfmt=dfmt, cfmt=cfmt)
+    for l, ref in enumerate(refs):
+        assert_close(out["fused"][l], ref, f"fused layer {l}")
+        assert_close(out["two"][l], ref, f"two-launch layer {l}")
+    # T = 16 at k = 2048: the SpMV stages Z as f16 (an fp32 tile exceeds 64 KiB)
+    for T, k, d_in in ((3, 512, 1024), (16, 2048, 2048), (40, 512, 1024)):
+        say(f"  T={T} k={k}")
+        gp = synth.make_group("qproj", d_in=d_in, d_out=776, k=k, T=T, n_layers=2)
+        assert gp.k == k
+        D, Cs, Xs = device_group(gp, dfmt=dfmt, cfmt=cfmt)
+        Ys = B.dict_group_forward(Xs, D, Cs)
+        torch.cuda.synchronize()
+        for l, ref in enumerate(oracle_group(gp, dfmt=dfmt, cfmt=cfmt)):
+            assert_close(Ys[l], ref, f"T={T} layer {l}")
+
+
+@pytest.mark.parametrize("cfmt", ["fp8", "int8"])
+def test_8bit_coefficients_full_size_decode(cfmt):
+    # the q_proj decode group at full size with an NVFP4 dictionary, and the
+    # MLP down group (d_in = 11008: X in three register passes) with f16 D
+    say(f"case: q_proj group NVFP4 D + {cfmt} C, full size")
+    g = synth.make_group("qproj", T=1, n_layers=2)
+    out = _both_paths(g, dfmt="nvfp4", cfmt=cfmt)
+    for l, ref in enumerate(oracle_group(g, dfmt="nvfp4", cfmt=cfmt)):
+        assert_close(out["fused"][l], ref, f"qproj fused layer {l}")
+        assert_close(out["two"][l], ref, f"qproj two-launch layer {l}")
+    say(f"case: MLP down group f16 D + {cfmt} C, full size")
+    g = synth.make_group("mlp", ptype="down", n_layers=2, T=1)
+    out = _both_paths(g, cfmt=cfmt)
+    for l, ref in enumerate(oracle_group(g, cfmt=cfmt)):
+        assert_close(out["fused"][l], ref, f"down fused layer {l}")
+
+
 def test_one_launch_decode_repeated_launches_identical():
     say("case: one-launch decode, 50 back-to-back launches on one workspace")
     g = synth.make_group("qproj", d_in=2048, d_out=3000, k=1024, T=1, n_layers=2)
