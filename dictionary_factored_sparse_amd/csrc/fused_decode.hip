@@ -122,9 +122,10 @@ __device__ __forceinline__ T* sreg_ptr(T* p) {
 // in [s, e); the other entries are masked without a branch, so the 8 LDS
 // gathers of a chunk are issued back to back.
 template <int VT>
-__device__ __forceinline__ float gather_chunk(const float* zl, const IdxChunk& ic,
-                                              const ValChunk<VT>& vc, int p, int s, int e,
-                                              float sum) {
+__device__ __forceinline__ float gather_chunk(const float* zl, IdxChunk ic, ValChunk<VT> vc,
+                                              int p, int s, int e, float sum) {
+  ic.touch();
+  vc.touch();
   const uint32_t len = (uint32_t)(e - s);
   const int base = p - s;
   float z[8];

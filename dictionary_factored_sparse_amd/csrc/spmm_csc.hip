@@ -155,13 +155,15 @@ __global__ __launch_bounds__(kThreads) void spmm_csc_kernel(ZcLaunch a) {
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int pb) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
+      ValChunk<VT> vu = vc[u];
+      vu.touch();
       const int base = pb + 8 * u - s;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // entries outside [s, e) read the zero row with a zero value
         const bool ok = (uint32_t)(base + i) < len;
         const uint32_t r = ok ? ic[u].get(i) : (uint32_t)k;
-        const float v = ok ? vc[u].get(i) : 0.0f;
+        const float v = ok ? vu.get(i) : 0.0f;
         ZRow<NT> z;
         z.read(zl + r * TT);
 #pragma unroll

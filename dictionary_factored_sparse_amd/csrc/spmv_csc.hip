@@ -241,6 +241,7 @@ __global__ __launch_bounds__(threads_of<ZH>()) void spmv_csc_kernel(ZcLaunch a,
       while (p0 < c.e) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+          vc[u].touch();
           const int base = p0 + 128 * u - c.s;
           // entries outside [s, e) are masked without a branch, so the LDS
           // gathers of a chunk issue back to back
