@@ -165,6 +165,11 @@ struct FusedArgs {
   uint32_t spin_limit;
   int32_t col_bytes;
   int32_t G;  // workgroups in the grid
+  // Byte offset of the received Z from the X rows in LDS.  0: Z overlays X
+  // (when both do not fit side by side), so the waves of a workgroup meet at
+  // a barrier before any of them writes Z: a wave that has finished its dot
+  // products would otherwise overwrite X under a wave still reading it.
+  int32_t z_off;
 };
 
 // A column's entry in LDS: [start, end) of its stored entries, and for 8-bit
@@ -181,9 +186,9 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   LayerRow* lt = reinterpret_cast<LayerRow*>(smem);            // [kFusedMaxLayers]
   CE_t* cse = reinterpret_cast<CE_t*>(smem + kLayerTableBytes);  // [ncols]
-  char* big = smem + kLayerTableBytes + f.col_bytes;           // X rows, later all of Z
+  char* big = smem + kLayerTableBytes + f.col_bytes;           // X rows, then Z
   _Float16* xs = reinterpret_cast<_Float16*>(big);
-  float* zs = reinterpret_cast<float*>(big);
+  float* zs = reinterpret_cast<float*>(big + f.z_off);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -339,6 +344,10 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     }
   }
 
+  // Z overlays X: every wave's reads of X have returned (its published sums
+  // used them), so a barrier here is enough before Z is written.
+  if (f.z_off == 0) asm volatile("s_barrier" ::: "memory");
+
   // ---- 7. the column ranges into LDS; rounds 0 and 1 of C in flight (their
   // bounds are older than D, so nothing here waits)
   if (tid < ncols) {
@@ -481,8 +490,9 @@ int device_cus() {
 }
 
 struct Plan {
-  int G, A, RT, NX;  // NX = RT (d_in <= 4096) or 2 * RT (d_in <= 8192)
+  int G, A, RT, NX;  // NX = RT, 2 * RT or 3 * RT (X passes per row)
   size_t col_bytes, smem;
+  int z_off;         // 0 when Z overlays X
 };
 
 bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
@@ -513,8 +523,17 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   p->RT = RT;
   p->NX = NX;
   p->col_bytes = ((size_t)max_cols * (q8 ? 16 : 8) + 15) / 16 * 16;
-  p->smem = kLayerTableBytes + p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
-  return p->smem <= 128 * 1024;
+  // X and Z side by side when they fit, else Z over X (with a barrier)
+  constexpr size_t kMaxSmem = 144 * 1024;
+  const size_t xalign = (xbytes + 15) / 16 * 16;
+  if (kLayerTableBytes + p->col_bytes + xalign + zbytes <= kMaxSmem) {
+    p->z_off = (int)xalign;
+    p->smem = kLayerTableBytes + p->col_bytes + xalign + zbytes;
+  } else {
+    p->z_off = 0;
+    p->smem = kLayerTableBytes + p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
+  }
+  return p->smem <= kMaxSmem;
 }
 
 template <int DT, int VT, int RT, int A, int NX>
@@ -529,6 +548,7 @@ hipError_t launch5(FusedArgs f, const Plan& p, hipStream_t s) {
   if (per_cu < 1) return hipErrorInvalidConfiguration;  // grid must be co-resident
   f.col_bytes = (int)p.col_bytes;
   f.G = p.G;
+  f.z_off = p.z_off;
   hipLaunchKernelGGL(kern, dim3(p.G), dim3(kFT), p.smem, s, f);
   return hipGetLastError();
 }

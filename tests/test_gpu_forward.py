@@ -346,6 +346,27 @@ def test_8bit_coefficients_full_size_decode(cfmt):
         assert_close(out["fused"][l], ref, f"down fused layer {l}")
 
 
+def test_one_launch_decode_x_and_z_lds_regions():
+    # The one-launch decode keeps X rows and the received Z side by side in
+    # LDS when both fit (MLP down, 2 layers) and lays Z over X otherwise (MLP
+    # down, 4 layers: 96 KiB of X rows), where the waves of a workgroup must
+    # meet before Z is written.  A missing barrier there once let a wave
+    # overwrite X under a slower wave of its workgroup (wrong Z for its atoms,
+    # only now and then); each layout is run repeatedly against the oracle.
+    for n, cfmt in ((2, "fp8"), (4, "plain")):
+        say(f"case: one-launch decode, MLP down n={n}, C {cfmt}, 8 launches")
+        g = synth.make_group("mlp", ptype="down", n_layers=n, T=1)
+        D, Cs, Xs = device_group(g, cfmt=cfmt)
+        refs = oracle_group(g, cfmt=cfmt)
+        ws = B.workspace(n, 1, D, Cs[0], DEV)
+        for it in range(8):
+            Ys = B.dict_group_forward(Xs, D, Cs, ws=ws)
+            torch.cuda.synchronize()
+            assert B.workspace_error_word(ws) == 0
+            for l, ref in enumerate(refs):
+                assert_close(Ys[l], ref, f"n={n} launch {it} layer {l}")
+
+
 def test_one_launch_decode_repeated_launches_identical():
     say("case: one-launch decode, 50 back-to-back launches on one workspace")
     g = synth.make_group("qproj", d_in=2048, d_out=3000, k=1024, T=1, n_layers=2)
