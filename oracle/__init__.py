@@ -83,6 +83,8 @@ def lib():
                                   C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
                                   C.c_void_p, C.c_void_p, C.POINTER(_Tensor), C.c_void_p]
         L.orc_max_threads.restype = C.c_int
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [C.c_int]
         _lib = L
     return _lib
 
@@ -276,3 +278,7 @@ def group_forward(Xs, D, d_in: int, cs) -> list:
 
 def max_threads() -> int:
     return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))

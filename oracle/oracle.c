@@ -364,6 +364,16 @@ int orc_forward(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_in,
   return 0;
 }
 
+/* Set the number of threads of the parallel loops above (n >= 1). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Threads the OpenMP runtime will use for the parallel loops above. */
 int orc_max_threads(void) {
 #ifdef _OPENMP
