@@ -16,6 +16,9 @@ Pages (cited by title and section):
   scale per 16 values (Review, "From retained values to measured decoding")
   and one fp32 tensor scale.  The scale recipe is a reading; parity unpinned
   against the pages, pinned against format definitions and bounds.
+* ``gram_inverse``, ``obs_delete``, ``obs_prune``, ``refit`` -- the producer
+  steps of the Review ("Method II: prune in coefficient space", Eq. (6)-(7)
+  and Algorithm 1; "Method III: refit the dictionary", Eq. (9)).
 * ``quantize8_csc`` -- 8-bit coefficient codes, FP8 (E4M3) or INT8, for the
   mixed-precision rows of Table 4 on the tables page ("DictLLM: Post-training
   Compression of Large Language Model with Dictionary Kernels").  Reading:
@@ -82,6 +85,17 @@ def lib():
         L.orc_forward.argtypes = [C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
                                   C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
                                   C.c_void_p, C.c_void_p, C.POINTER(_Tensor), C.c_void_p]
+        L.orc_gram_inverse.restype = C.c_int
+        L.orc_gram_inverse.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_double,
+                                       C.c_void_p]
+        L.orc_obs_delete.restype = C.c_double
+        L.orc_obs_delete.argtypes = [C.c_int32, C.c_void_p, C.c_void_p, C.c_int32]
+        L.orc_obs_prune.restype = C.c_int
+        L.orc_obs_prune.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
+                                    C.c_void_p, C.c_void_p]
+        L.orc_refit.restype = C.c_int
+        L.orc_refit.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                C.c_double, C.c_void_p]
         L.orc_max_threads.restype = C.c_int
         L.orc_set_threads.restype = None
         L.orc_set_threads.argtypes = [C.c_int]
@@ -274,6 +288,60 @@ def group_forward(Xs, D, d_in: int, cs) -> list:
     """The group's layers share D; each layer has its own X_l and C_l
     (Review, Figure 2: shared weights with separate activations)."""
     return [forward(X, D, d_in, c) for X, c in zip(Xs, cs)]
+
+
+# ---------------------------------------------------------------- producer steps
+
+def gram_inverse(Dt: np.ndarray, S: np.ndarray, lam: float) -> np.ndarray:
+    """P = (D^T S D + lam I)^-1 (Review Eq. (6)-(7)).  Dt: k x d_in (atom
+    a is row a), S: d_in x d_in; both taken as fp32.  Returns float64 k x k."""
+    Dt = np.ascontiguousarray(Dt, np.float32)
+    S = np.ascontiguousarray(S, np.float32)
+    k, d_in = Dt.shape
+    P = np.zeros((k, k), np.float64)
+    rc = lib().orc_gram_inverse(d_in, k, _ptr(Dt), _ptr(S), float(lam), _ptr(P))
+    if rc != 0:
+        raise ValueError("gram_inverse: matrix not positive definite")
+    return P
+
+
+def obs_delete(P: np.ndarray, c: np.ndarray, i: int):
+    """One Eq. (7) deletion of coordinate i with compensation: returns the
+    moved vector and the saliency c_i^2 / P_ii."""
+    P = np.ascontiguousarray(P, np.float64)
+    c = np.array(c, np.float64)
+    s = lib().orc_obs_delete(P.shape[0], _ptr(P), _ptr(c), int(i))
+    return c, s
+
+
+def obs_prune(C: np.ndarray, P: np.ndarray, n_prune: int):
+    """Fixed-inverse pruning of every column of C (k x d_out, fp32) with the
+    fixed inverse P (k x k, fp32), n_prune rows per column (Review Algorithm
+    1).  Returns (float64 pruned C, uint8 keep mask)."""
+    C = np.ascontiguousarray(C, np.float32)
+    P = np.ascontiguousarray(P, np.float32)
+    k, d_out = C.shape
+    out = np.zeros((k, d_out), np.float64)
+    keep = np.zeros((k, d_out), np.uint8)
+    rc = lib().orc_obs_prune(k, d_out, _ptr(C), _ptr(P), int(n_prune), _ptr(out), _ptr(keep))
+    if rc != 0:
+        raise ValueError("obs_prune: non-positive P_ii or allocation failure")
+    return out, keep
+
+
+def refit(W: np.ndarray, Cm: np.ndarray, lam: float) -> np.ndarray:
+    """Dictionary refit, Review Eq. (9): D (C C^T + lam I) = W C^T.  W: d_in x N,
+    Cm: k x N (pruned coefficients of the group's layers side by side), both
+    fp32.  Returns D atom by atom (k x d_in, row a = atom a), float64."""
+    W = np.ascontiguousarray(W, np.float32)
+    Cm = np.ascontiguousarray(Cm, np.float32)
+    d_in, N = W.shape
+    k = Cm.shape[0]
+    Dt = np.zeros((k, d_in), np.float64)
+    rc = lib().orc_refit(d_in, N, k, _ptr(W), _ptr(Cm), float(lam), _ptr(Dt))
+    if rc != 0:
+        raise ValueError("refit: Gram matrix not positive definite")
+    return Dt
 
 
 def max_threads() -> int:

@@ -34,6 +34,14 @@
  *              how those codes are scaled; the reading taken here is one
  *              fp32 scale per column of C, symmetric, amax / 448 (E4M3) or
  *              amax / 127 (INT8), nearest code with ties to even.
+ *   producer   The steps that produce D and C ([Review] "Method II: prune in
+ *              coefficient space" and "Method III: refit the dictionary"):
+ *              the inverse P = (D^T S D + lambda I)^-1 of Eq. (6)-(7), the
+ *              fixed-inverse pruning of each coefficient column (the
+ *              Review's Algorithm 1), with the compensation and saliency of
+ *              Eq. (7), and the refit D (C C^T + lambda I) = W C^T of
+ *              Eq. (9).  Symmetric positive definite systems are solved by
+ *              Cholesky factorisation, written out below.
  *
  * Every floating-point step that decides an integer code is done in fp32,
  * each operation correctly rounded (compile with -ffp-contract=off, no
@@ -362,6 +370,209 @@ int orc_forward(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_in,
   free(Z);
   free(Xd);
   return 0;
+}
+
+/* ---------------------------------------------------------------- producer */
+
+/* In-place Cholesky factorisation of the n x n symmetric positive definite
+ * matrix A (row-major, lower triangle used): A = L L^T, L left in the lower
+ * triangle.  Returns 0, or -1 if a pivot is not positive. */
+static int cholesky(int n, double* A) {
+  for (int j = 0; j < n; ++j) {
+    double d = A[(size_t)j * n + j];
+    for (int q = 0; q < j; ++q) d -= A[(size_t)j * n + q] * A[(size_t)j * n + q];
+    if (!(d > 0.0)) return -1;
+    double ljj = sqrt(d);
+    A[(size_t)j * n + j] = ljj;
+    for (int i = j + 1; i < n; ++i) {
+      double v = A[(size_t)i * n + j];
+      for (int q = 0; q < j; ++q) v -= A[(size_t)i * n + q] * A[(size_t)j * n + q];
+      A[(size_t)i * n + j] = v / ljj;
+    }
+  }
+  return 0;
+}
+
+/* Solve (L L^T) x = b in place for one right-hand side (stride 1). */
+static void cholesky_solve(int n, const double* L, double* b) {
+  for (int i = 0; i < n; ++i) {
+    double v = b[i];
+    for (int q = 0; q < i; ++q) v -= L[(size_t)i * n + q] * b[q];
+    b[i] = v / L[(size_t)i * n + i];
+  }
+  for (int i = n - 1; i >= 0; --i) {
+    double v = b[i];
+    for (int q = i + 1; q < n; ++q) v -= L[(size_t)q * n + i] * b[q];
+    b[i] = v / L[(size_t)i * n + i];
+  }
+}
+
+/* P = (D^T S D + lambda I)^-1, Eq. (6)-(7) of [Review].  D is d_in x k,
+ * given atom by atom: Dt[a * d_in + i] = D[i, a] (fp32); S is d_in x d_in
+ * row-major fp32 (symmetric).  P out: k x k row-major float64.  Returns 0,
+ * -1 if K is not positive definite, -2 on allocation failure. */
+int orc_gram_inverse(int32_t d_in, int32_t k, const float* Dt, const float* S, double lambda,
+                     double* P) {
+  double* U = (double*)malloc(sizeof(double) * (size_t)k * d_in);
+  double* K = (double*)malloc(sizeof(double) * (size_t)k * k);
+  double* e = (double*)malloc(sizeof(double) * (size_t)k);
+  if (!U || !K || !e) {
+    free(U);
+    free(K);
+    free(e);
+    return -2;
+  }
+  /* U = D^T S (k x d_in), then K = U D + lambda I */
+#pragma omp parallel for schedule(static)
+  for (int32_t a = 0; a < k; ++a)
+    for (int32_t j = 0; j < d_in; ++j) {
+      double v = 0.0;
+      for (int32_t i = 0; i < d_in; ++i)
+        v += (double)Dt[(size_t)a * d_in + i] * (double)S[(size_t)i * d_in + j];
+      U[(size_t)a * d_in + j] = v;
+    }
+#pragma omp parallel for schedule(static)
+  for (int32_t a = 0; a < k; ++a)
+    for (int32_t b = 0; b < k; ++b) {
+      double v = 0.0;
+      for (int32_t j = 0; j < d_in; ++j) v += U[(size_t)a * d_in + j] * (double)Dt[(size_t)b * d_in + j];
+      K[(size_t)a * k + b] = v + (a == b ? lambda : 0.0);
+    }
+  int rc = cholesky(k, K);
+  if (rc == 0) {
+    /* column b of P solves K x = e_b */
+    for (int32_t b = 0; b < k; ++b) {
+      for (int32_t a = 0; a < k; ++a) e[a] = a == b ? 1.0 : 0.0;
+      cholesky_solve(k, K, e);
+      for (int32_t a = 0; a < k; ++a) P[(size_t)a * k + b] = e[a];
+    }
+  }
+  free(U);
+  free(K);
+  free(e);
+  return rc;
+}
+
+/* One deletion with compensation, Eq. (7): remove coordinate i of c by the
+ * move delta = -(c_i / P_ii) P e_i (P symmetric, row-major k x k), applied
+ * to c in place (c_i becomes 0 up to rounding).  Returns the saliency
+ * c_i^2 / P_ii of the deleted value. */
+double orc_obs_delete(int32_t k, const double* P, double* c, int32_t i) {
+  double ci = c[i], pii = P[(size_t)i * k + i];
+  double f = ci / pii;
+  for (int32_t a = 0; a < k; ++a) c[a] -= P[(size_t)i * k + a] * f;
+  return ci * ci / pii;
+}
+
+typedef struct {
+  float s;
+  int32_t row;
+} score_t;
+
+static int score_cmp(const void* x, const void* y) {
+  const score_t* a = (const score_t*)x;
+  const score_t* b = (const score_t*)y;
+  if (a->s < b->s) return -1;
+  if (a->s > b->s) return 1;
+  return a->row < b->row ? -1 : (a->row > b->row);
+}
+
+/* Fixed-inverse pruning of every column of C ([Review] Algorithm 1, a
+ * reading of the paper's Algorithm 2).  C: k x d_out row-major fp32, the
+ * unpruned coefficients.  P: k x k row-major fp32 (the fixed inverse).  Per
+ * column j, independently (the blocks of the algorithm only batch work):
+ *   score_i = (c_i * c_i) / P_ii in fp32 (each operation rounded), from the
+ *   column's values before any deletion;
+ *   the n_prune rows of smallest score, ties to the lower row, are marked;
+ *   for each marked row i in that order: read the current c_i and apply the
+ *   Eq. (7) move c -= P[:, i] * c_i / P_ii (float64);
+ *   finally every marked entry is set to exactly 0.
+ * C_out: k x d_out row-major float64.  keep: k x d_out bytes, 1 where the
+ * entry stays in the support, 0 where it was pruned.  Returns 0, or -1 on
+ * allocation failure or a non-positive P_ii. */
+int orc_obs_prune(int32_t k, int32_t d_out, const float* C, const float* P, int32_t n_prune,
+                  double* C_out, uint8_t* keep) {
+  if (n_prune < 0) n_prune = 0;
+  if (n_prune > k) n_prune = k;
+  for (int32_t i = 0; i < k; ++i)
+    if (!(P[(size_t)i * k + i] > 0.0f)) return -1;
+  double* Pd = (double*)malloc(sizeof(double) * (size_t)k * k);
+  if (!Pd) return -1;
+  for (size_t q = 0; q < (size_t)k * k; ++q) Pd[q] = (double)P[q];
+  int bad = 0;
+#pragma omp parallel
+  {
+    score_t* sc = (score_t*)malloc(sizeof(score_t) * (size_t)k);
+    double* c = (double*)malloc(sizeof(double) * (size_t)k);
+    if (!sc || !c) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int32_t j = 0; j < d_out; ++j) {
+      if (!sc || !c) continue;
+      for (int32_t i = 0; i < k; ++i) {
+        float ci = C[(size_t)i * d_out + j];
+        float sq = ci * ci;
+        sc[i].s = sq / P[(size_t)i * k + i];
+        sc[i].row = i;
+        c[i] = (double)ci;
+      }
+      qsort(sc, (size_t)k, sizeof(score_t), score_cmp);
+      for (int32_t t = 0; t < n_prune; ++t) orc_obs_delete(k, Pd, c, sc[t].row);
+      for (int32_t i = 0; i < k; ++i) keep[(size_t)i * d_out + j] = 1;
+      for (int32_t t = 0; t < n_prune; ++t) {
+        c[sc[t].row] = 0.0;
+        keep[(size_t)sc[t].row * d_out + j] = 0;
+      }
+      for (int32_t i = 0; i < k; ++i) C_out[(size_t)i * d_out + j] = c[i];
+    }
+    free(sc);
+    free(c);
+  }
+  free(Pd);
+  return bad ? -1 : 0;
+}
+
+/* Dictionary refit, Eq. (9) of [Review]: D (C C^T + lambda I) = W C^T, with
+ * W = [W_1 .. W_n] (d_in x N row-major fp32, N = n d_out) and the pruned
+ * coefficients C = [C_1 .. C_n] (k x N row-major fp32, zeros kept).  The
+ * result is returned atom by atom: Dt[a * d_in + i] = D[i, a] (float64),
+ * i.e. Dt = (C C^T + lambda I)^-1 (W C^T)^T.  Returns 0, -1 if the Gram
+ * matrix is not positive definite, -2 on allocation failure. */
+int orc_refit(int32_t d_in, int32_t N, int32_t k, const float* W, const float* Cm, double lambda,
+              double* Dt) {
+  double* G = (double*)malloc(sizeof(double) * (size_t)k * k);
+  if (!G) return -2;
+#pragma omp parallel for schedule(static)
+  for (int32_t a = 0; a < k; ++a)
+    for (int32_t b = 0; b < k; ++b) {
+      double v = 0.0;
+      for (int32_t j = 0; j < N; ++j) v += (double)Cm[(size_t)a * N + j] * (double)Cm[(size_t)b * N + j];
+      G[(size_t)a * k + b] = v + (a == b ? lambda : 0.0);
+    }
+  int rc = cholesky(k, G);
+  if (rc == 0) {
+#pragma omp parallel
+    {
+      double* r = (double*)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+      for (int32_t i = 0; i < d_in; ++i) {
+        if (!r) continue;
+        /* row i of W C^T, then solve G x = that row: x is row i of D */
+        for (int32_t a = 0; a < k; ++a) {
+          double v = 0.0;
+          for (int32_t j = 0; j < N; ++j) v += (double)W[(size_t)i * N + j] * (double)Cm[(size_t)a * N + j];
+          r[a] = v;
+        }
+        cholesky_solve(k, G, r);
+        for (int32_t a = 0; a < k; ++a) Dt[(size_t)a * d_in + i] = r[a];
+      }
+      free(r);
+    }
+  }
+  free(G);
+  return rc;
 }
 
 /* Set the number of threads of the parallel loops above (n >= 1). */
