@@ -29,7 +29,9 @@ SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspac
            "nvfp4_pack", "nvfp4_unpack", "dict_workspace_size", "dict_proj_forward",
            "dict_group_forward", "dict_xd_forward", "dict_xd_workspace_size", "dict_zc_forward",
            "dfs_status_str", "dfs_last_hip_error", "dfs_version", "dict_csc_capacity",
-           "dict_csc_quantize8_workspace_size", "dict_csc_quantize8")
+           "dict_csc_quantize8_workspace_size", "dict_csc_quantize8",
+           "dict_gram_inverse_workspace_size", "dict_gram_inverse", "dict_obs_prune",
+           "dict_refit_workspace_size", "dict_refit")
 
 
 class NV(C.Structure):
@@ -87,6 +89,11 @@ def lib():
             "dict_zc_forward": [i32, vp, i32, i32, C.POINTER(Csc), C.POINTER(vp), i32, i64, vp],
             "dict_csc_quantize8_workspace_size": [i32, psz],
             "dict_csc_quantize8": [C.POINTER(Csc), i32, vp, vp, vp, sz, vp],
+            "dict_gram_inverse_workspace_size": [C.POINTER(Dict), psz],
+            "dict_gram_inverse": [C.POINTER(Dict), vp, i64, C.c_float, vp, i64, vp, sz, vp],
+            "dict_obs_prune": [i32, i32, vp, i64, vp, i64, i32, vp, i64, vp, i64, vp],
+            "dict_refit_workspace_size": [i32, i32, psz],
+            "dict_refit": [i32, i32, i32, vp, i64, vp, i64, C.c_float, vp, i64, vp, sz, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -367,6 +374,58 @@ def dict_zc_forward(Z, T: int, Cs, Ys=None, ydtype=torch.float16, stream=None):
            lib().dict_zc_forward(n, Z.data_ptr(), _dt(Z), T, cs, yp, _dt(Ys[0]),
                                  Ys[0].stride(0), _stream(stream)))
     return Ys
+
+
+# ----------------------------------------------------------------- producer steps
+
+def dict_gram_inverse(D: DeviceDict, S: torch.Tensor, lam: float, stream=None):
+    """P = (D^T S D + lam I)^-1 (k x k fp32).  Returns (P, error word): the
+    error word is non-zero if the matrix was not positive definite."""
+    assert S.dtype == torch.float32 and S.dim() == 2 and S.stride(1) == 1
+    dev = S.device
+    d = D.desc()
+    n = C.c_size_t(0)
+    _check("dict_gram_inverse_workspace_size",
+           lib().dict_gram_inverse_workspace_size(C.byref(d), C.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    P = torch.empty(D.k, D.k, dtype=torch.float32, device=dev)
+    _check("dict_gram_inverse", lib().dict_gram_inverse(C.byref(d), S.data_ptr(), S.stride(0),
+                                                        float(lam), P.data_ptr(), P.stride(0),
+                                                        ws.data_ptr(), n.value, _stream(stream)))
+    return P, ws[:4].view(torch.int32)
+
+
+def dict_obs_prune(Cm: torch.Tensor, P: torch.Tensor, n_prune: int, stream=None):
+    """Fixed-inverse pruning of every column of Cm (k x d_out fp32); returns
+    (pruned coefficients fp32, keep mask uint8)."""
+    assert Cm.dtype == torch.float32 and Cm.stride(1) == 1
+    assert P.dtype == torch.float32 and P.stride(1) == 1
+    k, d_out = Cm.shape
+    out = torch.empty(k, d_out, dtype=torch.float32, device=Cm.device)
+    keep = torch.empty(k, d_out, dtype=torch.uint8, device=Cm.device)
+    _check("dict_obs_prune", lib().dict_obs_prune(k, d_out, Cm.data_ptr(), Cm.stride(0),
+                                                  P.data_ptr(), P.stride(0), int(n_prune),
+                                                  out.data_ptr(), out.stride(0), keep.data_ptr(),
+                                                  keep.stride(0), _stream(stream)))
+    return out, keep
+
+
+def dict_refit(W: torch.Tensor, Cm: torch.Tensor, lam: float, stream=None):
+    """Refit D (C C^T + lam I) = W C^T.  W: d_in x N, Cm: k x N (fp32).
+    Returns (Dt: k x d_in fp32 atom-major, error word)."""
+    assert W.dtype == torch.float32 and Cm.dtype == torch.float32
+    assert W.stride(1) == 1 and Cm.stride(1) == 1
+    d_in, N = W.shape
+    k = Cm.shape[0]
+    assert Cm.shape[1] == N
+    n = C.c_size_t(0)
+    _check("dict_refit_workspace_size", lib().dict_refit_workspace_size(d_in, k, C.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=W.device)
+    Dt = torch.empty(k, d_in, dtype=torch.float32, device=W.device)
+    _check("dict_refit", lib().dict_refit(d_in, N, k, W.data_ptr(), W.stride(0), Cm.data_ptr(),
+                                          Cm.stride(0), float(lam), Dt.data_ptr(), Dt.stride(0),
+                                          ws.data_ptr(), n.value, _stream(stream)))
+    return Dt, ws[:4].view(torch.int32)
 
 
 # ----------------------------------------------------------------- host -> device helpers

@@ -214,6 +214,16 @@ bool fused_allowed() {
 
 constexpr size_t kCtrlBytes = kCtrlBlockBytes;  // control block at the start of the workspace
 
+constexpr int32_t kMaxProducerK = 8192;  // the pruning kernel keeps a column's sort keys in LDS
+size_t gram_ws_bytes(const dfs_dict* D) {
+  size_t b = spd_inverse_ws_bytes(D->k) + round256((size_t)D->k * D->d_in * 4);  // U = D^T S
+  if (D->dtype == DFS_F16) b += round256((size_t)D->k * D->d_in * 4);            // f32 atoms
+  return b;
+}
+size_t refit_ws_bytes(int32_t d_in, int32_t k) {
+  return spd_inverse_ws_bytes(k) + round256((size_t)k * k * 4) + round256((size_t)d_in * k * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +355,93 @@ dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream) {
   if (!y) return DFS_E_INVALID;
   DFS_TRY(check_nvfp4(in));
   DFS_HIP(launch_nvfp4_decode(in, n, y, (hipStream_t)stream));
+  return DFS_OK;
+}
+
+// ------------------------------------------------------------------ producer steps
+
+dfs_status dict_gram_inverse_workspace_size(const dfs_dict* D, size_t* bytes) {
+  if (!bytes || !D) return DFS_E_INVALID;
+  if (D->d_in <= 0 || D->k <= 0) return DFS_E_INVALID;
+  if (D->k > kMaxProducerK) return DFS_E_RANGE;
+  if (D->dtype != DFS_F16 && D->dtype != DFS_F32) return DFS_E_UNSUPPORTED;
+  *bytes = gram_ws_bytes(D);
+  return DFS_OK;
+}
+
+dfs_status dict_gram_inverse(const dfs_dict* D, const float* S, int64_t lds, float lambda, float* P,
+                             int64_t ldp, void* ws, size_t ws_bytes, void* stream) {
+  if (!D || !S || !P) return DFS_E_INVALID;
+  if (D->d_in <= 0 || D->k <= 0 || !D->data) return DFS_E_INVALID;
+  if (D->k > kMaxProducerK) return DFS_E_RANGE;
+  if (D->dtype != DFS_F16 && D->dtype != DFS_F32) return DFS_E_UNSUPPORTED;
+  if (D->ldd < D->d_in || lds < D->d_in || ldp < D->k) return DFS_E_INVALID;
+  if (!(lambda >= 0.0f) || !(lambda < __builtin_inff())) return DFS_E_INVALID;
+  if (!ws || ws_bytes < gram_ws_bytes(D)) return DFS_E_WORKSPACE;
+  if (!aligned16(ws)) return DFS_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int d_in = D->d_in, k = D->k;
+  char* w = (char*)ws;
+  void* inv_ws = w;
+  w += spd_inverse_ws_bytes(k);
+  float* U = (float*)w;
+  w += round256((size_t)k * d_in * 4);
+  const float* Dt = (const float*)D->data;
+  int64_t ldd = D->ldd;
+  if (D->dtype == DFS_F16) {
+    float* Df = (float*)w;
+    DFS_HIP(launch_atoms_to_f32((const _Float16*)D->data, D->ldd, d_in, k, Df, s));
+    Dt = Df;
+    ldd = d_in;
+  }
+  // U = D^T S (S symmetric: S^T = S), then K = U D + lambda I into P, then P = K^-1
+  DFS_HIP(launch_gemm_nt_f32(Dt, ldd, S, lds, U, d_in, k, d_in, d_in, 1.0f, 0.0f, 0.0f, s));
+  DFS_HIP(launch_gemm_nt_f32(U, d_in, Dt, ldd, P, ldp, k, k, d_in, 1.0f, 0.0f, lambda, s));
+  DFS_HIP(launch_spd_inverse(P, ldp, k, inv_ws, s));
+  return DFS_OK;
+}
+
+dfs_status dict_obs_prune(int32_t k, int32_t d_out, const float* C, int64_t ldc, const float* P,
+                          int64_t ldp, int32_t n_prune, float* C_out, int64_t ldo, uint8_t* keep,
+                          int64_t ldkeep, void* stream) {
+  if (!C || !P || !C_out || !keep) return DFS_E_INVALID;
+  if (k <= 0 || d_out <= 0 || n_prune < 0 || n_prune > k) return DFS_E_INVALID;
+  if (k > kMaxProducerK) return DFS_E_RANGE;
+  if (ldc < d_out || ldo < d_out || ldkeep < d_out || ldp < k) return DFS_E_INVALID;
+  DFS_HIP(launch_obs_prune(C, ldc, P, ldp, k, d_out, n_prune, C_out, ldo, keep, ldkeep,
+                           (hipStream_t)stream));
+  return DFS_OK;
+}
+
+dfs_status dict_refit_workspace_size(int32_t d_in, int32_t k, size_t* bytes) {
+  if (!bytes || d_in <= 0 || k <= 0) return DFS_E_INVALID;
+  if (k > kMaxProducerK) return DFS_E_RANGE;
+  *bytes = refit_ws_bytes(d_in, k);
+  return DFS_OK;
+}
+
+dfs_status dict_refit(int32_t d_in, int32_t N, int32_t k, const float* W, int64_t ldw,
+                      const float* C, int64_t ldc, float lambda, float* Dt, int64_t ldd, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!W || !C || !Dt) return DFS_E_INVALID;
+  if (d_in <= 0 || N <= 0 || k <= 0) return DFS_E_INVALID;
+  if (k > kMaxProducerK) return DFS_E_RANGE;
+  if (ldw < N || ldc < N || ldd < d_in) return DFS_E_INVALID;
+  if (!(lambda >= 0.0f) || !(lambda < __builtin_inff())) return DFS_E_INVALID;
+  if (!ws || ws_bytes < refit_ws_bytes(d_in, k)) return DFS_E_WORKSPACE;
+  if (!aligned16(ws)) return DFS_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  void* inv_ws = w;
+  w += spd_inverse_ws_bytes(k);
+  float* G = (float*)w;
+  w += round256((size_t)k * k * 4);
+  float* R = (float*)w;
+  // G = C C^T + lambda I, R = W C^T (d_in x k), G <- G^-1, D^T = G^-1 R^T
+  DFS_HIP(launch_gemm_nt_f32(C, ldc, C, ldc, G, k, k, k, N, 1.0f, 0.0f, lambda, s));
+  DFS_HIP(launch_gemm_nt_f32(W, ldw, C, ldc, R, k, d_in, k, N, 1.0f, 0.0f, 0.0f, s));
+  DFS_HIP(launch_spd_inverse(G, k, k, inv_ws, s));
+  DFS_HIP(launch_gemm_nt_f32(G, k, R, k, Dt, ldd, k, d_in, k, 1.0f, 0.0f, 0.0f, s));
   return DFS_OK;
 }
 

@@ -181,6 +181,21 @@ hipError_t launch_quant8_encode(const void* vals, int32_t dt, const int32_t* col
                                 int32_t d_out, int32_t kind, const void* ws, uint8_t* codes,
                                 float* col_scale, hipStream_t s);
 
+// producer steps (fp32): C = alpha A B^T + beta C (+ diag on m == n), the
+// in-place inverse of a symmetric positive definite matrix, coefficient
+// pruning with a fixed inverse
+hipError_t launch_gemm_nt_f32(const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
+                              int64_t ldc, int M, int N, int K, float alpha, float beta, float diag,
+                              hipStream_t s);
+size_t spd_inverse_ws_bytes(int n);
+hipError_t launch_spd_inverse(float* A, int64_t lda, int n, void* ws, hipStream_t s);
+size_t obs_prune_smem(int k);
+hipError_t launch_obs_prune(const float* C, int64_t ldc, const float* P, int64_t ldp, int k,
+                            int d_out, int n_prune, float* Co, int64_t ldo, uint8_t* keep,
+                            int64_t ldkeep, hipStream_t s);
+hipError_t launch_atoms_to_f32(const _Float16* D, int64_t ldd, int d_in, int k, float* out,
+                               hipStream_t s);
+
 // NVFP4 packing
 size_t nvfp4_ws_bytes(int64_t n);
 hipError_t launch_nvfp4_amax(const float* x, int64_t n, void* ws, hipStream_t s);

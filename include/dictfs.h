@@ -254,6 +254,57 @@ dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t
                            void* stream);
 
 /* ---------------------------------------------------------------------- */
+/* Producer steps (offline, fp32)                                          */
+/* ---------------------------------------------------------------------- */
+/* The steps that produce D_g and C_l ("DictLLM: Shared Dictionaries for
+ * Post-Training Compression", "Method II: prune in coefficient space" and
+ * "Method III: refit the dictionary and quantize the factors").  All
+ * matrices are fp32, row-major, device memory owned by the caller, with the
+ * given leading dimensions (in elements).  k <= 8192. */
+
+/* Workspace bytes of dict_gram_inverse for this dictionary. */
+dfs_status dict_gram_inverse_workspace_size(const dfs_dict* D, size_t* bytes);
+
+/* P = (D^T S D + lambda I)^-1 (Eq. (6); the fixed inverse of Eq. (7)).
+ * D: F16 or F32 dictionary (atom-major, as for the forward); S: d_in x d_in
+ * symmetric positive semidefinite (the group's calibration metric), leading
+ * dimension lds; lambda >= 0; P: k x k, leading dimension ldp.  The inverse
+ * is taken by Gauss-Jordan elimination without pivoting, one launch per
+ * pivot; if D^T S D + lambda I is not positive definite, the 32-bit word at
+ * the start of the workspace is set non-zero and P is undefined.
+ * NVFP4 dictionaries give DFS_E_UNSUPPORTED. */
+dfs_status dict_gram_inverse(const dfs_dict* D, const float* S, int64_t lds, float lambda, float* P,
+                             int64_t ldp, void* ws, size_t ws_bytes, void* stream);
+
+/* Fixed-inverse pruning of every column of the coefficients (the review's
+ * Algorithm 1, a reading of the paper's Algorithm 2, with the compensation
+ * and saliency of Eq. (7)).  C: k x d_out (ldc), the unpruned coefficients;
+ * P: k x k (ldp), symmetric, positive diagonal (from dict_gram_inverse).
+ * Each column independently: score_i = (c_i * c_i) / P_ii in fp32 from the
+ * column before any deletion; the n_prune rows of least score (ties to the
+ * lower row) are deleted in that order, each by c -= P[i, :] * (c_i / P_ii)
+ * with the current c_i; then the deleted entries are set to exactly 0.
+ * Writes C_out (k x d_out, ldo; may not alias C) and keep (k x d_out bytes,
+ * ldkeep: 1 = in the support, 0 = pruned).  0 <= n_prune <= k. */
+dfs_status dict_obs_prune(int32_t k, int32_t d_out, const float* C, int64_t ldc, const float* P,
+                          int64_t ldp, int32_t n_prune, float* C_out, int64_t ldo, uint8_t* keep,
+                          int64_t ldkeep, void* stream);
+
+/* Workspace bytes of dict_refit. */
+dfs_status dict_refit_workspace_size(int32_t d_in, int32_t k, size_t* bytes);
+
+/* Dictionary refit, Eq. (9): D (C C^T + lambda I) = W C^T.  W = [W_1 .. W_n]
+ * (d_in x N, ldw: the group's dense weights side by side, N = n d_out);
+ * C = [C_1 .. C_n] (k x N, ldc: the pruned coefficients, zeros included).
+ * Writes D atom by atom, Dt (k x d_in, ldd), the layout the forward takes
+ * for an F32 dictionary.  lambda >= 0; with lambda = 0 every atom must have
+ * a coefficient somewhere (else the Gram matrix is singular: the 32-bit
+ * word at the start of the workspace is set non-zero and Dt is undefined). */
+dfs_status dict_refit(int32_t d_in, int32_t N, int32_t k, const float* W, int64_t ldw,
+                      const float* C, int64_t ldc, float lambda, float* Dt, int64_t ldd, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
 /* Diagnostics                                                            */
 /* ---------------------------------------------------------------------- */
 

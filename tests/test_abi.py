@@ -209,3 +209,48 @@ def test_csc_capacity_is_whole_chunks():
     for nnz, cap in ((-1, 8), (0, 8), (1, 8), (7, 8), (8, 8), (9, 16), (2516386, 2516392),
                      ((1 << 31) - 1, 1 << 31)):
         assert L.dict_csc_capacity(nnz) == cap, nnz
+
+
+def test_producer_validation():
+    L = B.lib()
+    n = C.c_size_t(0)
+    D = _dict()
+    assert L.dict_gram_inverse_workspace_size(C.byref(D), C.byref(n)) == OK and n.value > 0
+    assert L.dict_gram_inverse_workspace_size(C.byref(_dict(k=9000)), C.byref(n)) == RANGE
+    assert L.dict_gram_inverse_workspace_size(
+        C.byref(_dict(dtype=B.DFS_NVFP4, data=None, nv=B.NV(P, P, P))), C.byref(n)) == UNSUPPORTED
+
+    def gi(D=None, S=P, lds=256, lam=0.1, Pout=P, ldp=128, ws=P, wsb=1 << 30):
+        D = D or _dict()
+        return L.dict_gram_inverse(C.byref(D), S, lds, lam, Pout, ldp, ws, wsb, None)
+    assert gi(S=0) == INVALID
+    assert gi(lds=100) == INVALID
+    assert gi(ldp=100) == INVALID
+    assert gi(lam=-1.0) == INVALID
+    assert gi(lam=float("nan")) == INVALID
+    assert gi(ws=0) == WORKSPACE
+    assert gi(wsb=16) == WORKSPACE
+    assert gi(ws=P + 4) == ALIGN
+
+    def pr(k=128, d_out=64, Cp=P, ldc=64, Pp=P, ldp=128, n_prune=10, Co=P, ldo=64, kp=P, ldk=64):
+        return L.dict_obs_prune(k, d_out, Cp, ldc, Pp, ldp, n_prune, Co, ldo, kp, ldk, None)
+    assert pr(n_prune=129) == INVALID
+    assert pr(n_prune=-1) == INVALID
+    assert pr(k=9000, ldp=9000) == RANGE
+    assert pr(Cp=0) == INVALID
+    assert pr(kp=0) == INVALID
+    assert pr(ldc=10) == INVALID
+    assert pr(ldp=10) == INVALID
+
+    assert L.dict_refit_workspace_size(0, 8, C.byref(n)) == INVALID
+    assert L.dict_refit_workspace_size(16, 9000, C.byref(n)) == RANGE
+
+    def rf(d_in=64, N=100, k=32, W=P, ldw=100, Cm=P, ldc=100, lam=0.0, Dt=P, ldd=64, ws=P,
+           wsb=1 << 30):
+        return L.dict_refit(d_in, N, k, W, ldw, Cm, ldc, lam, Dt, ldd, ws, wsb, None)
+    assert rf(W=0) == INVALID
+    assert rf(ldw=50) == INVALID
+    assert rf(ldd=10) == INVALID
+    assert rf(lam=-0.5) == INVALID
+    assert rf(k=9000) == RANGE
+    assert rf(wsb=8) == WORKSPACE
