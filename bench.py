@@ -454,6 +454,56 @@ def main():
         extras["sequential_mode_D_resident"] = seq
         _log(f"sequential mode: {seq}")
 
+        # producer steps at the q_proj group's scale (offline, fp32): the fixed
+        # inverse for d_in = 4096, k = 2048; pruning half of every column of
+        # both layers' coefficients; the refit from both layers' weights
+        t2 = time.time()
+        rng = np.random.default_rng(5)
+        d_in, kq, d_out = g.d_in, g.k, g.d_out
+        Dq = B.DeviceDict(d_in, kq, data=torch.from_numpy(g.D.astype(np.float32)).to(dev))
+        Xc = torch.randn(2 * d_in, d_in, device=dev)
+        Sq = (Xc.T @ Xc / (2 * d_in)).contiguous()
+        del Xc
+        Cq = torch.randn(kq, 2 * d_out, device=dev) / math.sqrt(kq)
+        Wq = torch.randn(d_in, 2 * d_out, device=dev)
+        B.dict_gram_inverse(Dq, Sq, 1e-3)
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        Pq, errq = B.dict_gram_inverse(Dq, Sq, 1e-3)
+        torch.cuda.synchronize()
+        gi_ms = (time.perf_counter() - tg) * 1e3
+        Pq = Pq.contiguous()
+        pr_out = torch.empty_like(Cq)
+        keep = torch.empty(kq, 2 * d_out, dtype=torch.uint8, device=dev)
+        ev0.record()
+        for l in range(2):
+            o, kp_ = B.dict_obs_prune(Cq[:, l * d_out:(l + 1) * d_out].contiguous(), Pq, kq // 2)
+            pr_out[:, l * d_out:(l + 1) * d_out] = o
+        ev1.record()
+        torch.cuda.synchronize()
+        pr_ms = ev0.elapsed_time(ev1)
+        B.dict_refit(Wq, pr_out, 1e-3)
+        torch.cuda.synchronize()
+        tr = time.perf_counter()
+        Dt_new, errr = B.dict_refit(Wq, pr_out, 1e-3)
+        torch.cuda.synchronize()
+        rf_ms = (time.perf_counter() - tr) * 1e3
+        steps_per_col = kq // 2
+        extras["producer_qproj_group"] = {
+            "gram_inverse_ms": round(gi_ms, 2),
+            "gram_inverse_note": "2 fp32 GEMMs (k x d_in x d_in, k x k x d_in: 103 GFLOP) and "
+                                 "2048 Gauss-Jordan pivot launches, wall clock",
+            "obs_prune_ms": round(pr_ms, 2),
+            "obs_prune_note": f"2 x {d_out} columns, {steps_per_col} deletions each, k = {kq}",
+            "obs_prune_GB/s_of_P_rows": round(2 * d_out * steps_per_col * kq * 4 / (pr_ms * 1e-3) / 1e9, 1),
+            "refit_ms": round(rf_ms, 2),
+            "refit_note": "3 fp32 GEMMs (69 + 137 + 34 GFLOP) and 2048 Gauss-Jordan launches, wall clock",
+            "error_words": [int(errq.item()), int(errr.item())],
+        }
+        del Sq, Pq, Cq, Wq, pr_out, keep, Dt_new
+        torch.cuda.empty_cache()
+        _log(f"producer steps: {extras['producer_qproj_group']} ({time.time() - t2:.1f} s)")
+
         # packers (offline steps, timed for information): dense -> CSC of one
         # q_proj C (2048 x 4096 f16), NVFP4 pack and unpack of one D_g
         Cdense = torch.from_numpy(g.Cs[0]).to(dev)
