@@ -99,6 +99,23 @@ def csc_bytes(d_out: int, nnz: int, dtype: str) -> int:
     return base + int(nnz * ELEM_BYTES[dtype])
 
 
+def bcsc_bytes(d_out: int, nblk: int, dtype: str) -> int:
+    """Block-structured coefficients, blocks of 8 consecutive atoms:
+    colptr int32[d_out+1] + one uint16 block index and 8 values per kept
+    block."""
+    return 4 * (d_out + 1) + nblk * (2 + int(8 * ELEM_BYTES[dtype]))
+
+
+def bcsc_density_at_equal_bytes(k: int, d_out: int, nnz: int, dtype: str) -> float:
+    """Fraction of blocks a block-structured C may keep for the bytes of an
+    unstructured CSC with nnz entries in the same dtype (the equal packed
+    bytes comparison of the Review, "Let the accelerator constrain the
+    support")."""
+    per_block = 2 + 8 * ELEM_BYTES[dtype]
+    nblk = (csc_bytes(d_out, nnz, dtype) - 4 * (d_out + 1)) / per_block
+    return nblk / (((k + 7) // 8) * d_out)
+
+
 def act_bytes(T: int, width: int, dtype: str) -> int:
     return int(T * width * ELEM_BYTES[dtype])
 

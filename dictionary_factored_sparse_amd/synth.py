@@ -111,6 +111,25 @@ class Group:
         return len(self.Cs)
 
 
+def block_coefficients(rng: np.random.Generator, k: int, d_out: int, block_density: float,
+                       dtype) -> np.ndarray:
+    """Dense k x d_out coefficients with block-structured support: each block
+    of 8 consecutive rows of a column (the last may be shorter) is kept with
+    probability ``block_density`` (independently); every entry of a kept
+    block is N(0, 1/k) in ``dtype``, redrawn until nonzero; the rest is 0."""
+    nb = (k + 7) // 8
+    keep = rng.random((nb, d_out), dtype=np.float32) < np.float32(block_density)
+    mask = np.repeat(keep, 8, axis=0)[:k]
+    vals = (rng.standard_normal((k, d_out), dtype=np.float32)
+            * np.float32(1.0 / np.sqrt(k))).astype(dtype)
+    bad = mask & (vals == 0)
+    while bad.any():
+        vals[bad] = (rng.standard_normal(int(bad.sum()), dtype=np.float32)
+                     * np.float32(1.0 / np.sqrt(k))).astype(dtype)
+        bad = mask & (vals == 0)
+    return np.where(mask, vals, np.zeros((), dtype)).astype(dtype)
+
+
 def make_group(workload: str, *, group: int = 0, ptype: str = "q", T: int | None = None,
                n_layers: int | None = None, d_in: int | None = None, d_out: int | None = None,
                k: int | None = None, density: float | None = None,

@@ -16,6 +16,9 @@ Pages (cited by title and section):
   scale per 16 values (Review, "From retained values to measured decoding")
   and one fp32 tensor scale.  The scale recipe is a reading; parity unpinned
   against the pages, pinned against format definitions and bounds.
+* ``pack_bcsc``/``forward_bcsc`` -- block-structured support, blocks of 8
+  consecutive atoms per column (Review, "Let the accelerator constrain the
+  support").
 * ``gram_inverse``, ``obs_delete``, ``obs_prune``, ``refit`` -- the producer
   steps of the Review ("Method II: prune in coefficient space", Eq. (6)-(7)
   and Algorithm 1; "Method III: refit the dictionary", Eq. (9)).
@@ -85,6 +88,13 @@ def lib():
         L.orc_forward.argtypes = [C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
                                   C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
                                   C.c_void_p, C.c_void_p, C.POINTER(_Tensor), C.c_void_p]
+        L.orc_pack_bcsc.restype = C.c_int64
+        L.orc_pack_bcsc.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int64,
+                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64]
+        L.orc_forward_bcsc.restype = C.c_int
+        L.orc_forward_bcsc.argtypes = [C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
+                                       C.c_int32, C.POINTER(_Tensor), C.c_int64, C.c_int32,
+                                       C.c_void_p, C.c_void_p, C.POINTER(_Tensor), C.c_void_p]
         L.orc_gram_inverse.restype = C.c_int
         L.orc_gram_inverse.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_double,
                                        C.c_void_p]
@@ -288,6 +298,61 @@ def group_forward(Xs, D, d_in: int, cs) -> list:
     """The group's layers share D; each layer has its own X_l and C_l
     (Review, Figure 2: shared weights with separate activations)."""
     return [forward(X, D, d_in, c) for X, c in zip(Xs, cs)]
+
+
+# ---------------------------------------------------------------- block-structured support
+
+@dataclass
+class BCSC:
+    """k x d_out coefficients kept in blocks of 8 consecutive atoms: kept
+    block q of column j has block index bidx[q] (rows 8*bidx[q] .. +7) and
+    values vals[8q .. 8q+7]."""
+    k: int
+    d_out: int
+    colptr: np.ndarray  # int32[d_out+1], counts blocks
+    bidx: np.ndarray    # uint16[nblk]
+    vals: np.ndarray    # float16/float32[8 * nblk]
+
+    @property
+    def nblk(self) -> int:
+        return int(self.colptr[-1])
+
+
+def pack_bcsc(Cd: np.ndarray) -> BCSC:
+    """Dense row-major k x d_out (float16/float32) -> block-structured CSC."""
+    Cd = np.ascontiguousarray(Cd)
+    k, d_out = Cd.shape
+    dt = _dtype_code(Cd)
+    colptr = np.zeros(d_out + 1, np.int32)
+    n = lib().orc_pack_bcsc(_ptr(Cd), dt, k, d_out, d_out, _ptr(colptr), None, None, 0)
+    bidx = np.zeros(max(n, 1), np.uint16)
+    vals = np.zeros(8 * max(n, 1), Cd.dtype)
+    got = lib().orc_pack_bcsc(_ptr(Cd), dt, k, d_out, d_out, _ptr(colptr), _ptr(bidx),
+                              _ptr(vals), n)
+    assert got == n
+    return BCSC(k, d_out, colptr, bidx[:n], vals[:8 * n])
+
+
+def forward_bcsc(X: np.ndarray, D, d_in: int, b: BCSC) -> np.ndarray:
+    """Y = (X D) C with block-structured C, float64 (zeros inside kept
+    blocks included)."""
+    X = np.ascontiguousarray(X)
+    T = X.shape[0]
+    keep: list = []
+    tx = _tensor(X, keep)
+    td = _tensor(D, keep)
+    vals = b.vals if b.vals.size else np.zeros(8, np.float32)
+    tc = _tensor(vals, keep)
+    colptr = np.ascontiguousarray(b.colptr, np.int32)
+    bidx = np.ascontiguousarray(b.bidx, np.uint16)
+    if bidx.size == 0:
+        bidx = np.zeros(1, np.uint16)
+    Y = np.zeros((T, b.d_out), np.float64)
+    rc = lib().orc_forward_bcsc(T, C.byref(tx), d_in, d_in, b.k, C.byref(td), d_in, b.d_out,
+                                _ptr(colptr), _ptr(bidx), C.byref(tc), _ptr(Y))
+    if rc != 0:
+        raise MemoryError("oracle forward_bcsc: allocation failed")
+    return Y
 
 
 # ---------------------------------------------------------------- producer steps
