@@ -31,7 +31,7 @@ SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspac
            "dfs_status_str", "dfs_last_hip_error", "dfs_version", "dict_csc_capacity",
            "dict_csc_quantize8_workspace_size", "dict_csc_quantize8",
            "dict_gram_inverse_workspace_size", "dict_gram_inverse", "dict_obs_prune",
-           "dict_refit_workspace_size", "dict_refit")
+           "dict_refit_workspace_size", "dict_refit", "dict_pack_bcsc")
 
 
 class NV(C.Structure):
@@ -45,7 +45,7 @@ class Dict(C.Structure):
 
 class Csc(C.Structure):
     _fields_ = [("k", C.c_int32), ("d_out", C.c_int32), ("nnz", C.c_int64), ("dtype", C.c_int32),
-                ("_pad", C.c_int32), ("colptr", C.c_void_p), ("rowidx", C.c_void_p),
+                ("block_rows", C.c_int32), ("colptr", C.c_void_p), ("rowidx", C.c_void_p),
                 ("vals", C.c_void_p), ("nv", NV), ("col_scale", C.c_void_p)]
 
 
@@ -89,6 +89,8 @@ def lib():
             "dict_zc_forward": [i32, vp, i32, i32, C.POINTER(Csc), C.POINTER(vp), i32, i64, vp],
             "dict_csc_quantize8_workspace_size": [i32, psz],
             "dict_csc_quantize8": [C.POINTER(Csc), i32, vp, vp, vp, sz, vp],
+            "dict_pack_bcsc": [vp, i32, i32, i32, i64, vp, vp, vp, i64, C.POINTER(C.c_int64), vp,
+                               sz, vp],
             "dict_gram_inverse_workspace_size": [C.POINTER(Dict), psz],
             "dict_gram_inverse": [C.POINTER(Dict), vp, i64, C.c_float, vp, i64, vp, sz, vp],
             "dict_obs_prune": [i32, i32, vp, i64, vp, i64, i32, vp, i64, vp, i64, vp],
@@ -185,6 +187,7 @@ class DeviceCSC:
     codes8: torch.Tensor | None = None     # uint8[capacity] FP8 / INT8 codes
     col_scale: torch.Tensor | None = None  # float32[d_out]
     code_kind: str | None = None           # "fp8" or "int8"
+    block_rows: int = 0                    # 8: colptr/nnz count blocks of 8 atoms
 
     def desc(self) -> Csc:
         if self.nv is not None:
@@ -194,8 +197,9 @@ class DeviceCSC:
             return Csc(self.k, self.d_out, self.nnz, CODE8[self.code_kind], 0,
                        self.colptr.data_ptr(), self.rowidx.data_ptr(), self.codes8.data_ptr(),
                        NV(), self.col_scale.data_ptr())
-        return Csc(self.k, self.d_out, self.nnz, _dt(self.vals), 0, self.colptr.data_ptr(),
-                   self.rowidx.data_ptr(), self.vals.data_ptr(), NV(), None)
+        return Csc(self.k, self.d_out, self.nnz, _dt(self.vals), self.block_rows,
+                   self.colptr.data_ptr(), self.rowidx.data_ptr(), self.vals.data_ptr(), NV(),
+                   None)
 
     @property
     def fmt(self) -> str:
@@ -238,6 +242,33 @@ def dict_pack_csc(Cd: torch.Tensor, stream=None) -> DeviceCSC:
                                                 vals.data_ptr(), rowidx.numel(), C.byref(nnz),
                                                 ws.data_ptr(), ws_n.value, st))
     return DeviceCSC(k, d_out, n, colptr, rowidx, vals=vals)
+
+
+def dict_pack_bcsc(Cd: torch.Tensor, stream=None) -> DeviceCSC:
+    """Dense (k, d_out) f16/f32 device tensor -> block-structured DeviceCSC
+    (blocks of 8 consecutive atoms per column; count call, then fill)."""
+    assert Cd.dim() == 2 and Cd.stride(1) == 1
+    k, d_out = Cd.shape
+    dev = Cd.device
+    ws_n = C.c_size_t(0)
+    _check("dict_pack_csc_workspace_size",
+           lib().dict_pack_csc_workspace_size(k, d_out, C.byref(ws_n)))
+    ws = torch.empty(ws_n.value, dtype=torch.uint8, device=dev)
+    colptr = torch.empty(d_out + 1, dtype=torch.int32, device=dev)
+    nb = C.c_int64(0)
+    st = _stream(stream)
+    _check("dict_pack_bcsc", lib().dict_pack_bcsc(Cd.data_ptr(), _dt(Cd), k, d_out, Cd.stride(0),
+                                                  colptr.data_ptr(), None, None, 0, C.byref(nb),
+                                                  ws.data_ptr(), ws_n.value, st))
+    n = nb.value
+    cap = dict_csc_capacity(n)
+    bidx = torch.zeros(cap, dtype=torch.int16, device=dev)
+    vals = torch.zeros(8 * cap, dtype=Cd.dtype, device=dev)
+    _check("dict_pack_bcsc", lib().dict_pack_bcsc(Cd.data_ptr(), _dt(Cd), k, d_out, Cd.stride(0),
+                                                  colptr.data_ptr(), bidx.data_ptr(),
+                                                  vals.data_ptr(), cap, C.byref(nb),
+                                                  ws.data_ptr(), ws_n.value, st))
+    return DeviceCSC(k, d_out, n, colptr, bidx, vals=vals, block_rows=8)
 
 
 def nvfp4_pack(x: torch.Tensor, stream=None) -> DeviceNVFP4:
@@ -443,7 +474,10 @@ def to_device_dict(atoms_np, device, nvfp4: bool = False) -> DeviceDict:
 def to_device_csc(dense_np, device, nvfp4: bool = False, fmt: str | None = None) -> DeviceCSC:
     """Dense numpy coefficients (k, d_out) -> DeviceCSC packed on the GPU.
     ``fmt``: None (the dense dtype, or NVFP4 when ``nvfp4``), "nvfp4", "fp8"
-    or "int8" (values quantised by the library's own packers)."""
+    or "int8" (values quantised by the library's own packers), or "block8"
+    (block-structured support, blocks of 8 atoms)."""
+    if fmt == "block8":
+        return dict_pack_bcsc(torch.from_numpy(dense_np).to(device))
     c = dict_pack_csc(torch.from_numpy(dense_np).to(device))
     if fmt is None and nvfp4:
         fmt = "nvfp4"

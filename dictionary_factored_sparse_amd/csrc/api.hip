@@ -77,6 +77,8 @@ dfs_status check_csc(const dfs_csc* C, int32_t k, int32_t d_out) {
     if (!C->rowidx) return DFS_E_INVALID;
     if (!aligned16(C->rowidx)) return DFS_E_ALIGN;
   }
+  if (C->block_rows != 0 && C->block_rows != 8) return DFS_E_UNSUPPORTED;
+  if (C->block_rows == 8 && !is_act_dtype(C->dtype)) return DFS_E_UNSUPPORTED;
   if (C->dtype == DFS_NVFP4) {
     if (C->nnz > 0) DFS_TRY(check_nvfp4(C->nv));
     else if (!C->nv.tensor_scale) return DFS_E_INVALID;
@@ -172,6 +174,7 @@ ZcLaunch make_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc
   }
   a.ydt = ydt;
   a.ldy = ldy;
+  a.block_rows = C[0].block_rows;
   return a;
 }
 
@@ -199,7 +202,9 @@ dfs_status run_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64
 dfs_status run_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc* C,
                   void* const* Y, int32_t ydt, int64_t ldy, hipStream_t s) {
   ZcLaunch a = make_zc(n, Z, zdt, T, C, Y, ydt, ldy);
-  if (T <= kGemvMaxRows)
+  if (a.block_rows != 0)
+    DFS_HIP(launch_spmv_bcsc(a, s));  // T <= kGemvMaxRows (checked by the callers)
+  else if (T <= kGemvMaxRows)
     DFS_HIP(launch_spmv_csc(a, s));
   else
     DFS_HIP(launch_spmm_csc(a, s));
@@ -317,6 +322,28 @@ dfs_status dict_csc_quantize8(const dfs_csc* src, int32_t dtype, uint8_t* codes,
   if (bad != 0) return DFS_E_INVALID;
   DFS_HIP(launch_quant8_encode(src->vals, src->dtype, src->colptr, src->nnz, src->d_out, dtype,
                                ws, codes, col_scale, s));
+  return DFS_OK;
+}
+
+dfs_status dict_pack_bcsc(const void* C, int32_t dtype, int32_t k, int32_t d_out, int64_t ldc,
+                          int32_t* colptr, uint16_t* bidx, void* vals, int64_t capacity,
+                          int64_t* nblk_host, void* ws, size_t ws_bytes, void* stream) {
+  if (!C || !colptr || !nblk_host) return DFS_E_INVALID;
+  if (dtype != DFS_F16 && dtype != DFS_F32) return DFS_E_UNSUPPORTED;
+  if (k <= 0 || d_out <= 0 || ldc < d_out) return DFS_E_INVALID;
+  if (k > kMaxK) return DFS_E_RANGE;
+  if ((bidx == nullptr) != (vals == nullptr)) return DFS_E_INVALID;
+  if (capacity < 0) return DFS_E_INVALID;
+  if (!ws || ws_bytes < pack_csc_ws_bytes(k, d_out)) return DFS_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  DFS_HIP(launch_pack_csc_count(C, dtype, k, d_out, ldc, colptr, ws, s, 8));
+  int64_t total = 0;
+  DFS_HIP(hipMemcpyAsync(&total, ws, sizeof(total), hipMemcpyDeviceToHost, s));
+  DFS_HIP(hipStreamSynchronize(s));
+  *nblk_host = total;
+  if (!bidx) return DFS_OK;
+  if (capacity < dict_csc_capacity(total)) return DFS_E_RANGE;
+  DFS_HIP(launch_pack_csc_scatter(C, dtype, k, d_out, ldc, bidx, vals, ws, s, 8));
   return DFS_OK;
 }
 
@@ -495,9 +522,11 @@ dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t
   if (C[0].k > kMaxKForward) return DFS_E_RANGE;
   for (int i = 0; i < n_layers; ++i) {
     DFS_TRY(check_csc(&C[i], C[0].k, C[0].d_out));
-    if (C[i].dtype != C[0].dtype) return DFS_E_UNSUPPORTED;
+    if (C[i].dtype != C[0].dtype || C[i].block_rows != C[0].block_rows)
+      return DFS_E_UNSUPPORTED;
   }
   if (!is_act_dtype(ydt)) return DFS_E_UNSUPPORTED;
+  if (C[0].block_rows != 0 && T > kGemvMaxRows) return DFS_E_UNSUPPORTED;
   if (T == 0) return DFS_OK;
   DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
   if (!Z) return DFS_E_INVALID;
@@ -513,9 +542,12 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
   DFS_TRY(check_dict(D));
   for (int i = 0; i < n_layers; ++i) {
     DFS_TRY(check_csc(&C[i], D->k, C[0].d_out));
-    if (C[i].dtype != C[0].dtype) return DFS_E_UNSUPPORTED;
+    if (C[i].dtype != C[0].dtype || C[i].block_rows != C[0].block_rows)
+      return DFS_E_UNSUPPORTED;
   }
   if (!is_act_dtype(xdt) || !is_act_dtype(ydt)) return DFS_E_UNSUPPORTED;
+  // block-structured coefficients: decode and small batches only
+  if (C[0].block_rows != 0 && (int64_t)n_layers * T > kGemvMaxRows) return DFS_E_UNSUPPORTED;
   if (T == 0) return DFS_OK;  // no rows: the activation pointers may be null
   DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
   DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));

@@ -141,6 +141,7 @@ struct ZcLaunch {
   void* Y[kMaxLayers];
   int32_t ydt;
   int64_t ldy;
+  int32_t block_rows;  // 0, or 8: colptr counts blocks of 8 atoms, rowidx holds block indices
 };
 
 // Rows at or below which X.D runs on VALU dot products instead of MFMA.
@@ -167,11 +168,15 @@ int spmm_token_tile(int k);
 
 // CSC packing
 size_t pack_csc_ws_bytes(int32_t k, int32_t d_out);
+// block_rows: 0 (one entry per stored element) or 8 (blocks of 8 atoms)
 hipError_t launch_pack_csc_count(const void* C, int32_t dtype, int32_t k, int32_t d_out,
-                                 int64_t ldc, int32_t* colptr, void* ws, hipStream_t s);
+                                 int64_t ldc, int32_t* colptr, void* ws, hipStream_t s,
+                                 int block_rows = 0);
 hipError_t launch_pack_csc_scatter(const void* C, int32_t dtype, int32_t k, int32_t d_out,
                                    int64_t ldc, uint16_t* rowidx, void* vals, const void* ws,
-                                   hipStream_t s);
+                                   hipStream_t s, int block_rows = 0);
+// Y_l = Z_l C_l for block-structured C (T <= 16 tokens per layer)
+hipError_t launch_spmv_bcsc(const ZcLaunch& a, hipStream_t s);
 
 // 8-bit coefficient codes (FP8 / INT8), one scale per column
 size_t quant8_ws_bytes(int32_t d_out);

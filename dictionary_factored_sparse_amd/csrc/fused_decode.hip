@@ -588,6 +588,7 @@ hipError_t launch1(FusedArgs f, const Plan& p, int vdt, hipStream_t s) {
 
 bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc) {
   if (xd.T != 1 || zc.T != 1) return false;
+  if (zc.block_rows != 0) return false;  // block-structured C: two-launch path
   if (zc.n_layers < 1 || zc.n_layers > kFusedMaxLayers) return false;
   if (xd.xdt != DFS_F16) return false;
   if (xd.ddt != DFS_F16 && xd.ddt != DFS_NVFP4) return false;

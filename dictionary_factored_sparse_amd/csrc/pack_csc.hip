@@ -14,6 +14,10 @@
 //            (j, chunk) its output offset, colptr[j] = offset of (j, 0);
 //   scatter  thread (j, chunk) rewrites its nonzeros at its offset, rows
 //            ascending, so the result is the unique canonical CSC.
+// The same phases pack the block-structured variant (blocks of BR = 8
+// consecutive rows of a column, kept whole when one entry is nonzero; the
+// Review's "Let the accelerator constrain the support"): counts are of kept
+// blocks, and the scatter writes the block index and its 8 values.
 #include "dfs_internal.hpp"
 
 namespace dfs {
@@ -58,7 +62,18 @@ __device__ __forceinline__ bool nonzero_at(const void* C, int64_t i) {
     return (((const uint16_t*)C)[i] & 0x7FFFu) != 0u;
 }
 
-template <int DT>
+// Whether block [r, r + BR) of column j (rows past k count as 0) holds a
+// nonzero; BR = 1 is a single entry.
+template <int DT, int BR>
+__device__ __forceinline__ bool block_nonzero(const void* C, int r, int k, int64_t ldc, int j) {
+  bool any = false;
+#pragma unroll
+  for (int e = 0; e < BR; ++e)
+    if (r + e < k) any |= nonzero_at<DT>(C, (int64_t)(r + e) * ldc + j);
+  return any;
+}
+
+template <int DT, int BR>
 __global__ __launch_bounds__(256) void count_kernel(const void* C, int k, int d_out, int64_t ldc,
                                                     int32_t* counts) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
@@ -66,7 +81,7 @@ __global__ __launch_bounds__(256) void count_kernel(const void* C, int k, int d_
   if (j >= d_out) return;
   const int r1 = min(k, (rc + 1) * kRowChunk);
   int c = 0;
-  for (int r = rc * kRowChunk; r < r1; ++r) c += nonzero_at<DT>(C, (int64_t)r * ldc + j);
+  for (int r = rc * kRowChunk; r < r1; r += BR) c += block_nonzero<DT, BR>(C, r, k, ldc, j);
   counts[(int64_t)j * gridDim.y + rc] = c;
 }
 
@@ -144,7 +159,7 @@ __global__ __launch_bounds__(kScanThreads) void tile_apply_kernel(int32_t* count
   if (blockIdx.x == 0 && threadIdx.x == 0) colptr[d_out] = (int32_t)total[0];
 }
 
-template <int DT>
+template <int DT, int BR>
 __global__ __launch_bounds__(256) void scatter_kernel(const void* C, int k, int d_out, int64_t ldc,
                                                       const int32_t* offsets, uint16_t* rowidx,
                                                       void* vals) {
@@ -153,16 +168,19 @@ __global__ __launch_bounds__(256) void scatter_kernel(const void* C, int k, int 
   if (j >= d_out) return;
   int64_t o = offsets[(int64_t)j * gridDim.y + rc];
   const int r1 = min(k, (rc + 1) * kRowChunk);
-  for (int r = rc * kRowChunk; r < r1; ++r) {
-    const int64_t i = (int64_t)r * ldc + j;
-    if (nonzero_at<DT>(C, i)) {
-      rowidx[o] = (uint16_t)r;
+  for (int r = rc * kRowChunk; r < r1; r += BR) {
+    if (!block_nonzero<DT, BR>(C, r, k, ldc, j)) continue;
+    rowidx[o] = (uint16_t)(r / BR);
+#pragma unroll
+    for (int e = 0; e < BR; ++e) {
+      const int64_t i = (int64_t)(r + e) * ldc + j;
+      const bool in = r + e < k;
       if constexpr (DT == DFS_F32)
-        ((uint32_t*)vals)[o] = ((const uint32_t*)C)[i];
+        ((uint32_t*)vals)[o * BR + e] = in ? ((const uint32_t*)C)[i] : 0u;
       else
-        ((uint16_t*)vals)[o] = ((const uint16_t*)C)[i];
-      ++o;
+        ((uint16_t*)vals)[o * BR + e] = in ? ((const uint16_t*)C)[i] : (uint16_t)0;
     }
+    ++o;
   }
 }
 
@@ -176,14 +194,17 @@ size_t pack_csc_ws_bytes(int32_t k, int32_t d_out) {
 }
 
 hipError_t launch_pack_csc_count(const void* C, int32_t dtype, int32_t k, int32_t d_out,
-                                 int64_t ldc, int32_t* colptr, void* ws, hipStream_t s) {
+                                 int64_t ldc, int32_t* colptr, void* ws, hipStream_t s,
+                                 int block_rows) {
   PackWs w = carve(ws, k, d_out);
   const int n_rc = n_row_chunks(k);
   dim3 grid((d_out + 255) / 256, n_rc);
+  auto kern = count_kernel<DFS_F16, 1>;
   if (dtype == DFS_F32)
-    hipLaunchKernelGGL(count_kernel<DFS_F32>, grid, dim3(256), 0, s, C, k, d_out, ldc, w.counts);
-  else
-    hipLaunchKernelGGL(count_kernel<DFS_F16>, grid, dim3(256), 0, s, C, k, d_out, ldc, w.counts);
+    kern = block_rows == 8 ? count_kernel<DFS_F32, 8> : count_kernel<DFS_F32, 1>;
+  else if (block_rows == 8)
+    kern = count_kernel<DFS_F16, 8>;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, C, k, d_out, ldc, w.counts);
   hipLaunchKernelGGL(tile_sum_kernel, dim3(w.n_tiles), dim3(kScanThreads), 0, s, w.counts,
                      w.n_items, w.bsum);
   hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, w.bsum, w.n_tiles,
@@ -195,15 +216,15 @@ hipError_t launch_pack_csc_count(const void* C, int32_t dtype, int32_t k, int32_
 
 hipError_t launch_pack_csc_scatter(const void* C, int32_t dtype, int32_t k, int32_t d_out,
                                    int64_t ldc, uint16_t* rowidx, void* vals, const void* ws,
-                                   hipStream_t s) {
+                                   hipStream_t s, int block_rows) {
   PackWs w = carve(const_cast<void*>(ws), k, d_out);
   dim3 grid((d_out + 255) / 256, n_row_chunks(k));
+  auto kern = scatter_kernel<DFS_F16, 1>;
   if (dtype == DFS_F32)
-    hipLaunchKernelGGL(scatter_kernel<DFS_F32>, grid, dim3(256), 0, s, C, k, d_out, ldc,
-                       w.counts, rowidx, vals);
-  else
-    hipLaunchKernelGGL(scatter_kernel<DFS_F16>, grid, dim3(256), 0, s, C, k, d_out, ldc,
-                       w.counts, rowidx, vals);
+    kern = block_rows == 8 ? scatter_kernel<DFS_F32, 8> : scatter_kernel<DFS_F32, 1>;
+  else if (block_rows == 8)
+    kern = scatter_kernel<DFS_F16, 8>;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, C, k, d_out, ldc, w.counts, rowidx, vals);
   return hipGetLastError();
 }
 

@@ -107,13 +107,23 @@ typedef struct {
  * dict_csc_capacity(nnz) entries (NVFP4 codes: half that many bytes; block
  * scales: ceil(nnz / 16) bytes; FP8/INT8 codes: that many bytes).  Entries
  * past nnz are never used and may hold anything.  The caller owns all
- * arrays. */
+ * arrays.
+ * Block-structured support (block_rows = 8; 0 means one entry per stored
+ * element): each column keeps whole blocks of 8 consecutive atoms (the
+ * variant of "DictLLM: Shared Dictionaries for Post-Training Compression",
+ * "Let the accelerator constrain the support").  Then colptr counts kept
+ * blocks, nnz is the number of kept blocks, rowidx[nnz] holds block indices
+ * b (atoms 8b .. 8b+7, strictly increasing within a column) and vals holds
+ * 8 values per block, 8q .. 8q+7 for the q-th block (F16 or F32 only).
+ * rowidx is allocated for dict_csc_capacity(nnz) blocks and vals for 8 times
+ * that.  Such coefficients run for T <= 16 tokens per layer on the two-launch
+ * path (DFS_E_UNSUPPORTED above that). */
 typedef struct {
   int32_t k;
   int32_t d_out;
   int64_t nnz;
   int32_t dtype;
-  int32_t _pad;
+  int32_t block_rows; /* 0, or 8 for block-structured support */
   const int32_t* colptr;
   const uint16_t* rowidx;
   const void* vals;
@@ -171,6 +181,19 @@ dfs_status dict_csc_quantize8_workspace_size(int32_t d_out, size_t* bytes);
  * nothing written; detecting it synchronises `stream`. */
 dfs_status dict_csc_quantize8(const dfs_csc* src, int32_t dtype, uint8_t* codes, float* col_scale,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* Dense row-major C (as for dict_pack_csc) -> block-structured CSC, blocks
+ * of 8 consecutive rows per column (see dfs_csc): a block is kept iff one of
+ * its entries compares unequal to zero (rows past k count as zero); kept
+ * block q stores its index in bidx[q] and its 8 values, bit-copied (rows past
+ * k as +0), in vals[8q .. 8q+7].  Workspace: dict_pack_csc_workspace_size.
+ * Otherwise as dict_pack_csc, with counts in blocks: bidx == NULL and vals
+ * == NULL fill colptr and *nblk_host only; capacity (blocks that bidx holds;
+ * vals holds 8 times as many elements) < dict_csc_capacity(nblk) gives
+ * DFS_E_RANGE.  k <= 65536.  Synchronises `stream`. */
+dfs_status dict_pack_bcsc(const void* C, int32_t dtype, int32_t k, int32_t d_out, int64_t ldc,
+                          int32_t* colptr, uint16_t* bidx, void* vals, int64_t capacity,
+                          int64_t* nblk_host, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes nvfp4_pack needs for n elements. */
 dfs_status nvfp4_pack_workspace_size(int64_t n, size_t* bytes);

@@ -254,3 +254,25 @@ def test_producer_validation():
     assert rf(lam=-0.5) == INVALID
     assert rf(k=9000) == RANGE
     assert rf(wsb=8) == WORKSPACE
+
+
+def test_block_csc_validation():
+    L = B.lib()
+    assert _group(Cs=[_csc(dtype=B.DFS_F16)]) != UNSUPPORTED
+    blk = B.Csc(128, 64, 100, B.DFS_F16, 8, P, P, P, B.NV(), None)
+    assert _group(Cs=[blk], T=0) == OK
+    assert _group(Cs=[blk], T=17) == UNSUPPORTED          # decode / small batch only
+    bad = B.Csc(128, 64, 100, B.DFS_F16, 4, P, P, P, B.NV(), None)
+    assert _group(Cs=[bad]) == UNSUPPORTED                # blocks of 8 only
+    nvb = B.Csc(128, 64, 100, B.DFS_NVFP4, 8, P, P, None, B.NV(P, P, P), None)
+    assert _group(Cs=[nvb]) == UNSUPPORTED
+    assert _group(n=2, Cs=[_csc(), blk]) == UNSUPPORTED   # one format per group
+    nb = C.c_int64(0)
+    assert L.dict_pack_bcsc(P, B.DFS_NVFP4, 128, 64, 64, P, None, None, 0, C.byref(nb), P,
+                            1 << 20, None) == UNSUPPORTED
+    assert L.dict_pack_bcsc(P, B.DFS_F16, 128, 64, 32, P, None, None, 0, C.byref(nb), P,
+                            1 << 20, None) == INVALID
+    assert L.dict_pack_bcsc(P, B.DFS_F16, 128, 64, 64, P, P, None, 0, C.byref(nb), P,
+                            1 << 20, None) == INVALID
+    assert L.dict_pack_bcsc(P, B.DFS_F16, 128, 64, 64, P, None, None, 0, C.byref(nb), P,
+                            8, None) == WORKSPACE
