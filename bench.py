@@ -312,7 +312,7 @@ def main():
                                codes8=c.codes8.clone(), col_scale=c.col_scale.clone(),
                                code_kind=c.code_kind)
         return B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
-                           vals=c.vals.clone())
+                           vals=c.vals.clone(), block_rows=c.block_rows)
 
     def time_group(gx, Ts, nvfp4, cfmt=None, sequential=False):
         """us per group forward at each T in Ts (inputs rotated over replicas
@@ -453,6 +453,44 @@ def main():
             torch.cuda.empty_cache()
         extras["sequential_mode_D_resident"] = seq
         _log(f"sequential mode: {seq}")
+
+        # Block-structured support against the unstructured CSC at equal packed
+        # bytes (the Review's "Let the accelerator constrain the support"): the
+        # q_proj group shape, f16 values; a 30%-dense CSC costs what 53.3% of
+        # 8-atom blocks cost.  Both on the two-launch decode (Z = X D, then
+        # Z C), and Z C alone; the one-launch decode of the CSC for reference.
+        qb = L.bcsc_density_at_equal_bytes(g.k, g.d_out, int(0.3 * g.k * g.d_out), "f16")
+        rngb = np.random.default_rng(11)
+        Cb = [synth.block_coefficients(rngb, g.k, g.d_out, qb, np.float16) for _ in range(2)]
+        Cbd = [B.dict_pack_bcsc(torch.from_numpy(c).to(dev)) for c in Cb]
+        del Cb
+        Ydb = [torch.empty(1, g.d_out, dtype=torch.float16, device=dev) for _ in range(2)]
+        byt_b = L.dict_bytes(g.d_in, g.k, "f16") + sum(
+            L.bcsc_bytes(g.d_out, c.nnz, "f16") + 2 * g.d_in + 2 * g.d_out for c in Cbd)
+        nrep_b = max(2, math.ceil(1.2e9 / byt_b))
+        rpb = [(reps[i % R][0], [clone_csc(c) for c in Cbd]) for i in range(nrep_b)]
+        wsb = B.workspace(2, 1, D0, Cbd[0], dev)
+
+        def step_b(i):
+            B.dict_group_forward(Xs, rpb[i % nrep_b][0], rpb[i % nrep_b][1], Ys=Ydb, ws=wsb)
+
+        def zc_b(i):
+            B.dict_zc_forward(Z, 1, rpb[i % nrep_b][1], Ys=Ydb)
+        t_b = timed_graph(step_b, K)
+        t_zb = timed_graph(zc_b, K)
+        extras["block8_equal_bytes_qproj_group"] = {
+            "block_density": round(qb, 4),
+            "retained_values_vs_csc": round(qb * 8 * (g.k // 8) / (0.3 * g.k), 3),
+            "csc": {"MB": round(step_bytes / 1e6, 2), "one_launch_us": round(ms_step * 1e3, 2),
+                    "two_launch_us": round(us_two, 2), "zc_us": round(kern["spmv_csc"]["us"], 2)},
+            "block8": {"MB": round(byt_b / 1e6, 2), "two_launch_us": round(t_b, 2),
+                       "zc_us": round(t_zb, 2),
+                       "zc_GB/s": round((byt_b - L.dict_bytes(g.d_in, g.k, "f16") - 2 * 2 * g.d_in)
+                                        / (t_zb * 1e-6) / 1e9, 1)},
+        }
+        del rpb, Cbd
+        torch.cuda.empty_cache()
+        _log(f"block8 at equal bytes: {extras['block8_equal_bytes_qproj_group']}")
 
         # producer steps at the q_proj group's scale (offline, fp32): the fixed
         # inverse for d_in = 4096, k = 2048; pruning half of every column of
