@@ -202,6 +202,15 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
                  "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
                  "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G), "s"(f.vts[0]),
                  "s"(f.vts[1]), "s"(f.vts[2]), "s"(f.vts[3]));
+  else if constexpr (DT == DFS_NVFP4)
+    // an NVFP4 dictionary streams in a quarter of the time, so a kernel
+    // argument line first touched after it (the value pointers, before the
+    // coefficient loads) shows in the step: fetch every line up front
+    // (measured 0.2-0.3 us faster; no gain with an f16 dictionary)
+    asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
+                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
+                 "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G), "s"(f.vals[0]),
+                 "s"(f.vts[0]), "s"(f.z_off));
   else
     asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
                  "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
