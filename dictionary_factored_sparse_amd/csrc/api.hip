@@ -116,11 +116,18 @@ bool mfma_path(int64_t rows, int32_t xdt, const dfs_dict* D) {
   return rows > kGemvMaxRows && xdt == DFS_F16 && D->dtype != DFS_F32 && D->d_in % 8 == 0;
 }
 
-// Bytes of the f16 expansion of an NVFP4 dictionary that the MFMA path needs.
-size_t xd_ws_bytes(int64_t rows, int32_t xdt, const dfs_dict* D) {
+// Workspace of the MFMA path: the f16 expansion of an NVFP4 dictionary, then
+// the split-K partial products (few stacked rows).
+size_t xd_expand_bytes(int64_t rows, int32_t xdt, const dfs_dict* D) {
   if (D->dtype == DFS_NVFP4 && mfma_path(rows, xdt, D))
     return round256((size_t)D->k * D->d_in * 2);
   return 0;
+}
+size_t xd_ws_bytes(int64_t rows, int32_t xdt, const dfs_dict* D) {
+  if (!mfma_path(rows, xdt, D)) return 0;
+  const int ks = gemm_split_k(rows, D->k, D->d_in);
+  const size_t part = ks > 1 ? round256((size_t)ks * rows * D->k * 4) : 0;
+  return xd_expand_bytes(rows, xdt, D) + part;
 }
 
 XdLaunch make_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64_t ldx,
@@ -184,6 +191,7 @@ dfs_status run_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64
   XdLaunch a = make_xd(n, X, xdt, T, ldx, D, Z, zdt);
   const int64_t rows = (int64_t)n * T;
   if (mfma_path(rows, xdt, D)) {
+    a.zpart = (float*)((char*)ws + xd_expand_bytes(rows, xdt, D));
     if (D->dtype == DFS_NVFP4) {
       _Float16* dh = (_Float16*)ws;
       DFS_HIP(launch_nvfp4_to_f16(D->nv.codes, D->nv.scales, D->nv.tensor_scale,

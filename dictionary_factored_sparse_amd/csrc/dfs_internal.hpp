@@ -125,6 +125,7 @@ struct XdLaunch {
   const float* dts;
   void* Z;              // (n_layers*T) x k row-major
   int32_t zdt;
+  float* zpart;         // MFMA path with split K: [ksplit][rows][k] fp32 partials
 };
 
 struct ZcLaunch {
@@ -157,6 +158,10 @@ hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, float* zw
 
 hipError_t launch_gemv_xd(const XdLaunch& a, hipStream_t s);
 hipError_t launch_gemm_xd_mfma(const XdLaunch& a, hipStream_t s);
+// Slices of K the MFMA GEMM splits into for rows x n_atoms x d_in (1 = no
+// split); with more than one, it needs ksplit * rows * n_atoms fp32 of
+// workspace for the partial products.
+int gemm_split_k(int64_t rows, int n_atoms, int d_in);
 hipError_t launch_nvfp4_to_f16(const uint8_t* codes, const uint8_t* scales, const float* ts,
                                int64_t n, _Float16* out, hipStream_t s);
 hipError_t launch_spmv_csc(const ZcLaunch& a, hipStream_t s);

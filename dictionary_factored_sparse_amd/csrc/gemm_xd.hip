@@ -89,17 +89,24 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef const __attribute__((address_space(1))) void* glob_ptr;
 
+// Split K (few stacked rows): a tile's K range is cut into `ks` slices of
+// `kslice` elements (a multiple of BK), each done by its own workgroup, which
+// writes an fp32 partial tile; a second kernel sums the slices in order.
+// Without the split, 64 rows over 3072 atoms are 48 workgroups on 256 CUs.
 template <int ZT, int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks, int kslice) {
   using TC = Tile<BM, BN>;
   constexpr int kStageBytes = TC::kStageBytes, kAInst = TC::kAInst, kBInst = TC::kBInst;
   constexpr int kLoadsPerStage = TC::kLoadsPerStage, MI = TC::MI, NJ = TC::NJ;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  const int M = a.n_layers * a.T, N = a.k, K = a.d_in;
+  const int M = a.n_layers * a.T, N = a.k;
   const int MB = (M + BM - 1) / BM, NB = (N + BN - 1) / BN;
+  const int split = (int)blockIdx.x % ks;
+  const int kbeg = split * kslice;
+  const int K = min(a.d_in - kbeg, kslice);  // this workgroup's K extent
   int mb, nb;
-  tile_of(blockIdx.x, gridDim.x, MB, NB, &mb, &nb);
+  tile_of((int)blockIdx.x / ks, (int)gridDim.x / ks, MB, NB, &mb, &nb);
   const int m0 = mb * BM, n0 = nb * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -114,12 +121,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a) {
   for (int i = 0; i < kAInst; ++i) {
     const int m = min(m0 + 8 * (wave * kAInst + i) + (lane >> 3), M - 1);
     const int l = m / a.T, t = m - l * a.T;
-    arow[i] = (const _Float16*)a.X[l] + (int64_t)t * a.ldx;
+    arow[i] = (const _Float16*)a.X[l] + (int64_t)t * a.ldx + kbeg;
   }
 #pragma unroll
   for (int i = 0; i < kBInst; ++i) {
     const int n = min(n0 + 8 * (wave * kBInst + i) + (lane >> 3), N - 1);
-    brow[i] = (const _Float16*)a.D + (int64_t)n * a.ldd;
+    brow[i] = (const _Float16*)a.D + (int64_t)n * a.ldd + kbeg;
   }
   const int nk = (K + BK - 1) / BK;
   // Loads of K tile kt into LDS stage kt % 3.  A chunk past K (only in a
@@ -253,13 +260,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a) {
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m < M && n < N) {
-          if constexpr (ZT == DFS_F32)
+          if (ks > 1)
+            a.zpart[((int64_t)split * M + m) * N + n] = acc[i][j][v];
+          else if constexpr (ZT == DFS_F32)
             ((float*)a.Z)[(int64_t)m * N + n] = acc[i][j][v];
           else
             ((_Float16*)a.Z)[(int64_t)m * N + n] = (_Float16)acc[i][j][v];
         }
       }
     }
+}
+
+// Z = the sum of the ks partial products, in slice order (deterministic).
+template <int ZT>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* part, int ks, int64_t n,
+                                                         void* Z) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = part[i];
+  for (int q = 1; q < ks; ++q) v += part[q * n + i];
+  if constexpr (ZT == DFS_F32)
+    ((float*)Z)[i] = v;
+  else
+    ((_Float16*)Z)[i] = (_Float16)v;
 }
 
 // Expand an atom-major NVFP4 dictionary to f16 (element i = e2m1 * e4m3 *
@@ -288,8 +311,16 @@ hipError_t launch_tile(const XdLaunch& a, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
   const int M = a.n_layers * a.T;
-  const unsigned G = (unsigned)(((M + BM - 1) / BM) * ((a.k + BN - 1) / BN));
-  hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), smem, s, a);
+  const int tiles = ((M + BM - 1) / BM) * ((a.k + BN - 1) / BN);
+  const int ks = BM == 64 ? gemm_split_k(M, a.k, a.d_in) : 1;
+  const int nkt = (a.d_in + BK - 1) / BK;
+  const int kslice = (nkt + ks - 1) / ks * BK;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * ks)), dim3(kThreads), smem, s, a, ks, kslice);
+  if (ks > 1) {
+    const int64_t n = (int64_t)M * a.k;
+    hipLaunchKernelGGL(splitk_sum_kernel<ZT>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       a.zpart, ks, n, a.Z);
+  }
   return hipGetLastError();
 }
 
@@ -300,6 +331,20 @@ hipError_t launch_z(const XdLaunch& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Enough slices that tiles * slices reaches about one workgroup per CU (256),
+// each slice at least 4 K tiles; only for the 64 x 64 tile (<= 128 rows).
+int gemm_split_k(int64_t rows, int n_atoms, int d_in) {
+  if (rows > 128) return 1;
+  const int tiles = (int)((rows + 63) / 64) * ((n_atoms + 63) / 64);
+  const int nkt = (d_in + BK - 1) / BK;
+  int ks = (256 + tiles - 1) / tiles;
+  ks = min(ks, nkt / 4);
+  ks = max(ks, 1);
+  // equal slices of whole K tiles: no slice may come out empty
+  while (ks > 1 && (int64_t)((nkt + ks - 1) / ks) * (ks - 1) >= nkt) --ks;
+  return ks;
+}
 
 hipError_t launch_gemm_xd_mfma(const XdLaunch& a, hipStream_t s) {
   return a.zdt == DFS_F32 ? launch_z<DFS_F32>(a, s) : launch_z<DFS_F16>(a, s);

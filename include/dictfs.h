@@ -266,8 +266,9 @@ dfs_status dict_xd_forward(int32_t n_layers, const void* const* X, int32_t xdt, 
                            int64_t ldx, const dfs_dict* D, void* Z, int32_t zdt, void* ws,
                            size_t ws_bytes, void* stream);
 
-/* Workspace bytes dict_xd_forward needs (non-zero only for an NVFP4
- * dictionary on the MFMA path, which expands D_g to f16 first). */
+/* Workspace bytes dict_xd_forward needs (non-zero only on the MFMA path:
+ * the f16 expansion of an NVFP4 dictionary, and for at most 128 stacked rows
+ * the fp32 partial products of the split K dimension). */
 dfs_status dict_xd_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, size_t* bytes);
 
 /* The second half of Eq. (1) alone: Y[l] = Z_l C[l], Z as written by
