@@ -167,8 +167,7 @@ __device__ __forceinline__ void stage_z(float* zs, const void* Z, int64_t row0, 
 }
 
 template <int VT, int ZT, int TT, bool ZH>
-__global__ __launch_bounds__(threads_of<ZH>()) void spmv_csc_kernel(ZcLaunch a,
-                                                                     int groups_per_block) {
+__global__ __launch_bounds__(threads_of<ZH>()) void spmv_csc_kernel(ZcLaunch a) {
   constexpr int NTH = threads_of<ZH>();
   constexpr int CPG = NTH / 16;  // columns per group: 4 per wave, one per DPP row
   constexpr int U = Unroll<VT, TT, ZH>::U;
@@ -179,11 +178,11 @@ __global__ __launch_bounds__(threads_of<ZH>()) void spmv_csc_kernel(ZcLaunch a,
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int g = lane & 15;
-  // this workgroup's column groups (16 columns each): one staging of Z
-  // serves all of them
+  // this workgroup's run of column groups (CPG columns each), an equal share
+  // of the layer's groups: one staging of Z serves all of them
   const int ngroups = (a.d_out + CPG - 1) / CPG;
-  const int gb = blockIdx.x * groups_per_block;
-  const int gend = min(gb + groups_per_block, ngroups);
+  const int gb = (int)((int64_t)blockIdx.x * ngroups / gridDim.x);
+  const int gend = (int)((int64_t)(blockIdx.x + 1) * ngroups / gridDim.x);
   const int64_t nnz = a.nnz[layer];
   const uint16_t* rowidx = a.rowidx[layer];
   const void* vals = a.vals[layer];
@@ -312,15 +311,16 @@ hipError_t launch3(const ZcLaunch& a, hipStream_t s) {
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess) return err;
   }
-  // enough workgroups to fill the chip twice over, each staging Z once for
-  // as many 16-column groups as that leaves it
+  // a fixed number of workgroups (one per CU when the f16 tile limits the
+  // CU to one workgroup, two per CU otherwise), split evenly over the
+  // layers; each stages Z once for an equal run of column groups
   constexpr int NTH = threads_of<ZH>();
   const int ngroups = (a.d_out + NTH / 16 - 1) / (NTH / 16);
   const int target = ZH ? 256 : 512;
-  const int per = (ngroups * a.n_layers + target - 1) / target;
-  const int gpb = per < 1 ? 1 : per;
-  dim3 grid((ngroups + gpb - 1) / gpb, a.n_layers);
-  hipLaunchKernelGGL(kern, grid, dim3(NTH), smem, s, a, gpb);
+  int per_layer = target / a.n_layers;
+  per_layer = per_layer < 1 ? 1 : (per_layer > ngroups ? ngroups : per_layer);
+  dim3 grid(per_layer, a.n_layers);
+  hipLaunchKernelGGL(kern, grid, dim3(NTH), smem, s, a);
   return hipGetLastError();
 }
 
