@@ -410,6 +410,24 @@ def main():
         extras["table4_formats_qproj_decode_group"] = t4
         _log(f"table 4 formats: {t4}")
 
+        # the same 32-layer stack in f16 at the paper's own density point (44%
+        # sparsity, the setting of its decode-speed benchmark): projection time
+        # per token, one group of each type timed and counted 16 times per type
+        st16, tok_us, tok_b = {}, 0.0, 0
+        for ptype, count in (("q", 4), ("gate", 2), ("down", 1)):
+            gx = synth.make_group("stack_nvfp4", ptype=ptype, density=0.56, wdtype=np.float16)
+            us, nb = time_group(gx, (1,), False)[1]
+            st16[ptype] = {"us_per_group": round(us, 2), "MB": round(nb / 1e6, 2),
+                           "GB/s": round(nb / us / 1e3, 1), "groups_per_token": 16 * count}
+            tok_us += 16 * count * us
+            tok_b += 16 * count * nb
+            del gx
+        st16["per_token_us"] = round(tok_us, 1)
+        st16["per_token_GB"] = round(tok_b / 1e9, 3)
+        st16["projection_tokens_per_s"] = round(1e6 / tok_us, 1)
+        extras["stack_f16_density0.56_per_token"] = st16
+        _log(f"f16 stack at density 0.56: {st16}")
+
         # the paper's own density point (44% sparsity) on the q_proj group shape
         gx = synth.make_group("qproj", density=0.56)
         us, nb = time_group(gx, (1,), False)[1]
