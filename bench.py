@@ -548,12 +548,12 @@ def main():
         extras["producer_qproj_group"] = {
             "gram_inverse_ms": round(gi_ms, 2),
             "gram_inverse_note": "2 fp32 GEMMs (k x d_in x d_in, k x k x d_in: 103 GFLOP) and "
-                                 "2048 Gauss-Jordan pivot launches, wall clock",
+                                 "32 blocked Gauss-Jordan steps (64 pivots each), wall clock",
             "obs_prune_ms": round(pr_ms, 2),
             "obs_prune_note": f"2 x {d_out} columns, {steps_per_col} deletions each, k = {kq}",
             "obs_prune_GB/s_of_P_rows": round(2 * d_out * steps_per_col * kq * 4 / (pr_ms * 1e-3) / 1e9, 1),
             "refit_ms": round(rf_ms, 2),
-            "refit_note": "3 fp32 GEMMs (69 + 137 + 34 GFLOP) and 2048 Gauss-Jordan launches, wall clock",
+            "refit_note": "3 fp32 GEMMs (69 + 137 + 34 GFLOP) and 32 blocked Gauss-Jordan steps, wall clock",
             "error_words": [int(errq.item()), int(errr.item())],
         }
         del Sq, Pq, Cq, Wq, pr_out, keep, Dt_new

@@ -293,9 +293,9 @@ dfs_status dict_gram_inverse_workspace_size(const dfs_dict* D, size_t* bytes);
  * D: F16 or F32 dictionary (atom-major, as for the forward); S: d_in x d_in
  * symmetric positive semidefinite (the group's calibration metric), leading
  * dimension lds; lambda >= 0; P: k x k, leading dimension ldp.  The inverse
- * is taken by Gauss-Jordan elimination without pivoting, one launch per
- * pivot; if D^T S D + lambda I is not positive definite, the 32-bit word at
- * the start of the workspace is set non-zero and P is undefined.
+ * is taken by Gauss-Jordan elimination without pivoting, blocked 64 pivots
+ * at a time; if D^T S D + lambda I is not positive definite, the 32-bit word
+ * at the start of the workspace is set non-zero and P is undefined.
  * NVFP4 dictionaries give DFS_E_UNSUPPORTED. */
 dfs_status dict_gram_inverse(const dfs_dict* D, const float* S, int64_t lds, float lambda, float* P,
                              int64_t ldp, void* ws, size_t ws_bytes, void* stream);
