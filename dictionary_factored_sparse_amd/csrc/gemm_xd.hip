@@ -25,6 +25,8 @@
 // numbered so that the workgroups that share an XCD (dispatch is
 // round-robin over the 8 XCDs) cover a compact 4 x 8 block of tiles and so
 // share A and B panels in their L2.
+#include <type_traits>
+
 #include "dfs_internal.hpp"
 
 namespace dfs {
@@ -109,7 +111,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
   tile_of((int)blockIdx.x / ks, (int)gridDim.x / ks, MB, NB, &mb, &nb);
   const int m0 = mb * BM, n0 = nb * BN;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses in SGPRs
   const int wm = (wave >> 1) * (MI * 32), wn = (wave & 1) * (NJ * 32);
 
   // Each load instruction fills 8 tile rows; lane j writes row rr = 8 * q +
@@ -129,6 +132,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
     brow[i] = (const _Float16*)a.D + (int64_t)n * a.ldd + kbeg;
   }
   const int nk = (K + BK - 1) / BK;
+  const int nkf = K / BK;  // whole K tiles
   // Loads of K tile kt into LDS stage kt % 3.  A chunk past K (only in a
   // short last tile; K % 8 == 0 on this path) reads the row's last chunk and
   // is zeroed once it has landed.
@@ -149,6 +153,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
       const int kk = min(kt * BK + chunk_of(q), K - 8);
       __builtin_amdgcn_global_load_lds((glob_ptr)(brow[i] + kk),
                                        (lds_ptr)(st + BM * kRowBytes + q * 1024), 16, 0, 0);
+    }
+  };
+  // Whole tiles from stage 2 on: one pointer per load instruction, advanced
+  // by one tile per issue (no clamp, no per-load index arithmetic).  Loads
+  // [lo, hi) of the stage's list (A loads first, then B).
+  const _Float16* gp[kLoadsPerStage];
+#pragma unroll
+  for (int i = 0; i < kAInst; ++i) gp[i] = arow[i] + 2 * BK + chunk_of(wave * kAInst + i);
+#pragma unroll
+  for (int i = 0; i < kBInst; ++i)
+    gp[kAInst + i] = brow[i] + 2 * BK + chunk_of(wave * kBInst + i);
+  auto issue_fast = [&](int kt, auto lo_c, auto hi_c) {
+    constexpr int lo = decltype(lo_c)::value, hi = decltype(hi_c)::value;
+    char* st = smem + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int i = lo; i < hi; ++i) {
+      char* dst = i < kAInst ? st + (wave * kAInst + i) * 1024
+                             : st + BM * kRowBytes + (wave * kBInst + i - kAInst) * 1024;
+      __builtin_amdgcn_global_load_lds((glob_ptr)gp[i], (lds_ptr)dst, 16, 0, 0);
+      gp[i] += BK;
     }
   };
   auto zero_tail = [&](int kt) {
@@ -177,8 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
 
   const int fr = lane & 31, fc = lane >> 5;
   // Fragments of 16-wide K slice ks (lane: row fr of each 32-row block, K
-  // chunk 2 * ks + fc), read into one of two register sets so that the
-  // reads of slice ks + 1 overlap the MFMAs of slice ks.
+  // chunk 2 * ks + fc).
   auto frags = [&](const char* as, const char* bs, int ks, h8* fa, h8* fb) {
     const int c = 2 * ks + fc;
 #pragma unroll
@@ -199,54 +222,89 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
-  auto compute = [&](int buf) {
-    const char* as = smem + buf * kStageBytes;
+  // Issue order of one slice for the scheduler: each MFMA followed by one
+  // fragment read and then one load (masks: 0x008 MFMA, 0x100 LDS read,
+  // 0x020 vector memory read), the rest after.
+  constexpr int kReads = MI + NJ, kMfma = MI * NJ;
+  // A slice is a scheduling region of its own (sched_barrier 0 on both sides).
+  auto interleave = [&](int loads) {
+#pragma unroll
+    for (int r = 0; r < kMfma; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (r < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (r < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Stage s's tiles are in LDS for every wave: this wave waits for its own
+  // loads of s (`newer` loads issued after them may stay in flight) and for
+  // its LDS reads, zero-fills a short last tile, then meets the others.
+  auto stage_ready = [&](int s, int newer) {
+    if (newer > 0) {
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kLoadsPerStage));
+    } else {
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+      if (s == nk - 1 && K % BK != 0) {
+        zero_tail(s);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+      }
+    }
+    lds_barrier();
+  };
+
+  // Software pipeline over K tiles, three LDS stages, one barrier per tile.
+  // Within tile kt: the MFMAs of slice j run while the fragments of slice
+  // j + 1 are read and (slices 0 and 1) tile kt + 2 is loaded into the
+  // stage tile kt - 1 used; after slice 2, tile kt + 1 is made ready, and
+  // slice 3's MFMAs cover the reads of its first slice.  Reading slice 3 of
+  // tile kt - 1 finished before the previous barrier, so the loads of
+  // tile kt + 2 never overwrite data a wave still reads.
+  issue(0);
+  if (nk > 1) issue(1);
+  stage_ready(0, nk > 1 ? 1 : 0);
+  h8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
+  frags(smem, smem + BM * kRowBytes, 0, fa0, fb0);
+  int kt = 0;
+  for (; kt + 2 < nkf; ++kt) {  // tile kt + 2 is whole: loads on advancing pointers
+    __builtin_amdgcn_sched_barrier(0);
+    const char* as = smem + (kt % kStages) * kStageBytes;
     const char* bs = as + BM * kRowBytes;
-    h8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
-    frags(as, bs, 0, fa0, fb0);
+    constexpr int h = kLoadsPerStage / 2;
+    frags(as, bs, 1, fa1, fb1);
+    mma(fa0, fb0);
+    issue_fast(kt + 2, std::integral_constant<int, 0>{}, std::integral_constant<int, h>{});
+    interleave(h);
+    frags(as, bs, 2, fa0, fb0);
+    mma(fa1, fb1);
+    issue_fast(kt + 2, std::integral_constant<int, h>{},
+               std::integral_constant<int, kLoadsPerStage>{});
+    interleave(kLoadsPerStage - h);
+    frags(as, bs, 3, fa1, fb1);
+    mma(fa0, fb0);
+    interleave(0);
+    stage_ready(kt + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const char* an = smem + ((kt + 1) % kStages) * kStageBytes;
+    frags(an, an + BM * kRowBytes, 0, fa0, fb0);
+    mma(fa1, fb1);
+    interleave(0);
+  }
+  for (; kt < nk; ++kt) {  // the last two tiles (and a short one): plain issue
+    const char* as = smem + (kt % kStages) * kStageBytes;
+    const char* bs = as + BM * kRowBytes;
+    if (kt + 2 < nk) issue(kt + 2);
     frags(as, bs, 1, fa1, fb1);
     mma(fa0, fb0);
     frags(as, bs, 2, fa0, fb0);
     mma(fa1, fb1);
     frags(as, bs, 3, fa1, fb1);
     mma(fa0, fb0);
-    mma(fa1, fb1);
-    // Issue order for the scheduler: the reads of slices 0 and 1, then the
-    // MFMAs of slices 0 and 1 each paired with one read of slices 2 and 3,
-    // then the remaining MFMAs (masks: 0x100 LDS read, 0x008 MFMA).
-    constexpr int kReads = MI + NJ;  // fragment reads per slice
-    constexpr int kPair = 2 * kReads < 2 * MI * NJ ? 2 * kReads : 2 * MI * NJ;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReads, 0);
-#pragma unroll
-    for (int r = 0; r < kPair; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if constexpr (2 * MI * NJ > kPair)
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * NJ - kPair, 0);
-    if constexpr (2 * kReads > kPair)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReads - kPair, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * NJ, 0);
-  };
-
-  issue(0);
-  if (nk > 1) issue(1);
-  for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of stage kt have landed (stage kt + 1 may still be
-    // in flight); the barrier makes every wave's loads visible and frees
-    // the buffer of stage kt - 1 for stage kt + 2
     if (kt + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kLoadsPerStage));
-    } else {
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-      if (K % BK != 0) {
-        zero_tail(kt);
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-      }
+      stage_ready(kt + 1, kt + 2 < nk ? 1 : 0);
+      const char* an = smem + ((kt + 1) % kStages) * kStageBytes;
+      frags(an, an + BM * kRowBytes, 0, fa0, fb0);
     }
-    lds_barrier();
-    if (kt + 2 < nk) issue(kt + 2);
-    compute(kt % kStages);
+    mma(fa1, fb1);
   }
 
   // Accumulator layout of a 32 x 32 block: lane l holds column l % 32 and

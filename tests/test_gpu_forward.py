@@ -77,9 +77,10 @@ def test_prefill_ragged_tiles_full(T):
         assert_close(Ys[l], ref, f"T={T} layer {l}")
 
 
-@pytest.mark.parametrize("d_in,k", [(56, 40), (120, 72), (200, 136), (1032, 264)])
+@pytest.mark.parametrize("d_in,k", [(56, 40), (120, 72), (192, 100), (200, 136), (1032, 264)])
 def test_mfma_k_tail_and_short_pipelines(d_in, k):
     # d_in % 64 != 0 leaves a short last K tile (zeroed past d_in in LDS);
+    # d_in = 192 is three whole tiles (one pass of the pipelined loop);
     # d_in < 64 and < 128 run the K pipeline with one and two tiles; M = 80
     # and N = k leave ragged row and atom tiles.
     say(f"case: MFMA X.D with d_in={d_in}, k={k}, 2 x T=40")
