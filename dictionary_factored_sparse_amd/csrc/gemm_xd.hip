@@ -223,16 +223,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
   // Issue order of one slice for the scheduler: each MFMA followed by one
-  // fragment read and then one load (masks: 0x008 MFMA, 0x100 LDS read,
-  // 0x020 vector memory read), the rest after.
+  // fragment read (masks: 0x008 MFMA, 0x100 LDS read); the slice's tile
+  // loads are left to the scheduler.  A slice is a scheduling region of its
+  // own (sched_barrier 0 on both sides).
   constexpr int kReads = MI + NJ, kMfma = MI * NJ;
-  // A slice is a scheduling region of its own (sched_barrier 0 on both sides).
-  auto interleave = [&](int loads) {
+  auto interleave = [&]() {
 #pragma unroll
     for (int r = 0; r < kMfma; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (r < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (r < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -254,9 +253,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
 
   // Software pipeline over K tiles, three LDS stages, one barrier per tile.
   // Within tile kt: the MFMAs of slice j run while the fragments of slice
-  // j + 1 are read and (slices 0 and 1) tile kt + 2 is loaded into the
-  // stage tile kt - 1 used; after slice 2, tile kt + 1 is made ready, and
-  // slice 3's MFMAs cover the reads of its first slice.  Reading slice 3 of
+  // j + 1 are read and a quarter of tile kt + 2's loads go out (into the
+  // stage tile kt - 1 used); after slice 2, tile kt + 1 is made ready (this
+  // wave's loads of it have landed: only the three quarters of tile kt + 2
+  // issued since may be pending), and slice 3's MFMAs cover the reads of
+  // its first slice.  Reading slice 3 of
   // tile kt - 1 finished before the previous barrier, so the loads of
   // tile kt + 2 never overwrite data a wave still reads.
   issue(0);
@@ -269,25 +270,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
     __builtin_amdgcn_sched_barrier(0);
     const char* as = smem + (kt % kStages) * kStageBytes;
     const char* bs = as + BM * kRowBytes;
-    constexpr int h = kLoadsPerStage / 2;
+    constexpr int q = kLoadsPerStage / 4;
+    static_assert(4 * q == kLoadsPerStage, "a quarter of the tile's loads per slice");
     frags(as, bs, 1, fa1, fb1);
     mma(fa0, fb0);
-    issue_fast(kt + 2, std::integral_constant<int, 0>{}, std::integral_constant<int, h>{});
-    interleave(h);
+    issue_fast(kt + 2, std::integral_constant<int, 0>{}, std::integral_constant<int, q>{});
+    interleave();
     frags(as, bs, 2, fa0, fb0);
     mma(fa1, fb1);
-    issue_fast(kt + 2, std::integral_constant<int, h>{},
-               std::integral_constant<int, kLoadsPerStage>{});
-    interleave(kLoadsPerStage - h);
+    issue_fast(kt + 2, std::integral_constant<int, q>{}, std::integral_constant<int, 2 * q>{});
+    interleave();
     frags(as, bs, 3, fa1, fb1);
     mma(fa0, fb0);
-    interleave(0);
-    stage_ready(kt + 1, 1);
+    issue_fast(kt + 2, std::integral_constant<int, 2 * q>{}, std::integral_constant<int, 3 * q>{});
+    interleave();
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 * q));
+    lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const char* an = smem + ((kt + 1) % kStages) * kStageBytes;
     frags(an, an + BM * kRowBytes, 0, fa0, fb0);
     mma(fa1, fb1);
-    interleave(0);
+    issue_fast(kt + 2, std::integral_constant<int, 3 * q>{}, std::integral_constant<int, kLoadsPerStage>{});
+    interleave();
   }
   for (; kt < nk; ++kt) {  // the last two tiles (and a short one): plain issue
     const char* as = smem + (kt % kStages) * kStageBytes;
