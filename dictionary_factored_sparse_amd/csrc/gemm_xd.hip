@@ -333,6 +333,230 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
     }
 }
 
+// ------------------------------------------------------------------ wide tile
+// 256 x 256 outputs per workgroup of 4 waves (2 x 2), each wave 128 x 128 =
+// 4 x 4 MFMA blocks: a 16-wide K slice costs a wave 8 fragment reads for 16
+// MFMAs, two thirds of the reads per MFMA of the 128 x 64 wave tile, and the
+// tile loads per MFMA fall by a third.  K advances 32 at a time (rows of
+// 64 bytes, 4 chunks) through four LDS stages of 32 KiB, loads issued three
+// tiles ahead; one barrier per 32 MFMAs of a wave, as above.
+constexpr int WBK = 32, kWRowBytes = WBK * 2, kWStages = 4;
+constexpr int kWAhead = kWStages - 1;  // tiles in flight ahead of the one multiplied
+template <int TM, int TN>
+struct WTile {
+  static constexpr int kStageBytes = (TM + TN) * kWRowBytes;   // 32 KiB for 256 x 256
+  static constexpr int kAInst = TM * kWRowBytes / 1024 / kWavesG;
+  static constexpr int kBInst = TN * kWRowBytes / 1024 / kWavesG;
+  static constexpr int kLoads = kAInst + kBInst;              // per wave per tile
+  static constexpr size_t kSmemBytes = (size_t)kWStages * kStageBytes;
+  static constexpr int MI = TM / 64, NJ = TN / 64;            // 32 x 32 blocks per wave
+};
+
+// Slot of chunk c of a 64-byte row r is c ^ wswz(r): the 32 rows of a
+// fragment read land in distinct 16-byte bank slots for 8- and for 16-lane
+// windows (two rows share a 128-byte window, four a 256-byte one).
+__device__ __forceinline__ int wswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int ZT, int WBM, int WBN, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_xd_wide_kernel(XdLaunch a) {
+  using WT = WTile<WBM, WBN>;
+  constexpr int MI = WT::MI, NJ = WT::NJ, kWAInst = WT::kAInst, kWBInst = WT::kBInst;
+  constexpr int kWLoads = WT::kLoads, kWStageBytes = WT::kStageBytes;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int M = a.n_layers * a.T, N = a.k, K = a.d_in;
+  const int MB = (M + WBM - 1) / WBM, NB = (N + WBN - 1) / WBN;
+  int mb, nb;
+  tile_of((int)blockIdx.x, (int)gridDim.x, MB, NB, &mb, &nb);
+  const int m0 = mb * WBM, n0 = nb * WBN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (wave >> 1) * (WBM / 2), wn = (wave & 1) * (WBN / 2);
+
+  // Load instruction q fills 16 rows: lane j writes
+  // row 16 q + j / 4, slot j % 4, and reads that row's chunk (j % 4) ^ wswz.
+  const _Float16* arow[kWAInst];
+  const _Float16* brow[kWBInst];
+#pragma unroll
+  for (int i = 0; i < kWAInst; ++i) {
+    const int m = min(m0 + 16 * (wave * kWAInst + i) + (lane >> 2), M - 1);
+    const int l = m / a.T, t = m - l * a.T;
+    arow[i] = (const _Float16*)a.X[l] + (int64_t)t * a.ldx;
+  }
+#pragma unroll
+  for (int i = 0; i < kWBInst; ++i) {
+    const int n = min(n0 + 16 * (wave * kWBInst + i) + (lane >> 2), N - 1);
+    brow[i] = (const _Float16*)a.D + (int64_t)n * a.ldd;
+  }
+  const int nk = (K + WBK - 1) / WBK;
+  const int nkf = K / WBK;
+  auto chunk_of = [&](int q) { return ((lane & 3) ^ wswz(16 * q + (lane >> 2))) * 8; };
+  auto issue = [&](int kt) {  // clamped: any tile, a short last one included
+    char* st = smem + (kt % kWStages) * kWStageBytes;
+#pragma unroll
+    for (int i = 0; i < kWAInst; ++i) {
+      const int q = wave * kWAInst + i;
+      const int kk = min(kt * WBK + chunk_of(q), K - 8);
+      __builtin_amdgcn_global_load_lds((glob_ptr)(arow[i] + kk), (lds_ptr)(st + q * 1024), 16, 0,
+                                       0);
+    }
+#pragma unroll
+    for (int i = 0; i < kWBInst; ++i) {
+      const int q = wave * kWBInst + i;
+      const int kk = min(kt * WBK + chunk_of(q), K - 8);
+      __builtin_amdgcn_global_load_lds((glob_ptr)(brow[i] + kk),
+                                       (lds_ptr)(st + WBM * kWRowBytes + q * 1024), 16, 0, 0);
+    }
+  };
+  // whole tiles from tile 3 on: pointers advanced by one tile per issue
+  const _Float16* gp[kWLoads];
+#pragma unroll
+  for (int i = 0; i < kWAInst; ++i) gp[i] = arow[i] + kWAhead * WBK + chunk_of(wave * kWAInst + i);
+#pragma unroll
+  for (int i = 0; i < kWBInst; ++i)
+    gp[kWAInst + i] = brow[i] + kWAhead * WBK + chunk_of(wave * kWBInst + i);
+  auto issue_fast = [&](int kt, auto lo_c, auto hi_c) {
+    constexpr int lo = decltype(lo_c)::value, hi = decltype(hi_c)::value;
+    char* st = smem + (kt % kWStages) * kWStageBytes;
+#pragma unroll
+    for (int i = lo; i < hi; ++i) {
+      char* dst = i < kWAInst ? st + (wave * kWAInst + i) * 1024
+                              : st + WBM * kWRowBytes + (wave * kWBInst + i - kWAInst) * 1024;
+      __builtin_amdgcn_global_load_lds((glob_ptr)gp[i], (lds_ptr)dst, 16, 0, 0);
+      gp[i] += WBK;
+    }
+  };
+  auto zero_tail = [&](int kt) {
+    char* st = smem + (kt % kWStages) * kWStageBytes;
+    const u4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kWAInst; ++i) {
+      const int q = wave * kWAInst + i;
+      if (kt * WBK + chunk_of(q) >= K) *reinterpret_cast<u4*>(st + q * 1024 + lane * 16) = z;
+    }
+#pragma unroll
+    for (int i = 0; i < kWBInst; ++i) {
+      const int q = wave * kWBInst + i;
+      if (kt * WBK + chunk_of(q) >= K)
+        *reinterpret_cast<u4*>(st + WBM * kWRowBytes + q * 1024 + lane * 16) = z;
+    }
+  };
+
+  f16v acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int fr = lane & 31, fc = lane >> 5;
+  auto frags = [&](const char* st, int ks, h8* fa, h8* fb) {
+    const int c = 2 * ks + fc;
+    const char* bs = st + WBM * kWRowBytes;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm + 32 * i + fr;
+      fa[i] = *reinterpret_cast<const h8*>(st + r * kWRowBytes + ((c ^ wswz(r)) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = wn + 32 * j + fr;
+      fb[j] = *reinterpret_cast<const h8*>(bs + r * kWRowBytes + ((c ^ wswz(r)) * 16));
+    }
+  };
+  auto mma = [&](const h8* fa, const h8* fb) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {  // each MFMA followed by one fragment read
+#pragma unroll
+    for (int r = 0; r < MI * NJ; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (r < MI + NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // stage s ready for every wave: own loads of s landed (`newer` loads of
+  // later tiles may be pending), LDS reads done, short tile zero-filled
+  auto stage_ready = [&](int s, int newer) {
+    static_assert(kWAhead <= 4, "wait counts below cover up to 3 newer tiles");
+    switch (newer) {
+      case 0:
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        if (s == nk - 1 && K % WBK != 0) {
+          zero_tail(s);
+          __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        }
+        break;
+      case 1: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kWLoads)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * kWLoads)); break;
+      default: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 * kWLoads)); break;
+    }
+    lds_barrier();
+  };
+
+  // Pipeline: tile kt in stage kt % 4.  Slice 0's MFMAs run while slice 1 is
+  // read and half of tile kt + 3 goes out (into the stage tile kt - 1 used,
+  // which every wave finished reading before the previous barrier); then
+  // tile kt + 1 is made ready (this wave's loads of it have landed: tile
+  // kt + 2 and half of kt + 3 may be pending) and slice 1's MFMAs cover the
+  // reads of its first slice while the other half of tile kt + 3 goes out.
+  for (int t = 0; t < kWAhead; ++t)
+    if (t < nk) issue(t);
+  stage_ready(0, min(nk, kWAhead) - 1);
+  h8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
+  frags(smem, 0, fa0, fb0);
+  int kt = 0;
+  for (; kt + kWAhead < nkf; ++kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    const char* st = smem + (kt % kWStages) * kWStageBytes;
+    frags(st, 1, fa1, fb1);
+    mma(fa0, fb0);
+    issue_fast(kt + kWAhead, std::integral_constant<int, 0>{},
+               std::integral_constant<int, kWLoads / 2>{});
+    interleave();
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kWAhead - 2) * kWLoads + kWLoads / 2));
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(smem + ((kt + 1) % kWStages) * kWStageBytes, 0, fa0, fb0);
+    mma(fa1, fb1);
+    issue_fast(kt + kWAhead, std::integral_constant<int, kWLoads / 2>{},
+               std::integral_constant<int, kWLoads>{});
+    interleave();
+  }
+  for (; kt < nk; ++kt) {  // the last tiles (and a short one): plain issue
+    const char* st = smem + (kt % kWStages) * kWStageBytes;
+    if (kt + kWAhead < nk) issue(kt + kWAhead);
+    frags(st, 1, fa1, fb1);
+    mma(fa0, fb0);
+    if (kt + 1 < nk) {
+      stage_ready(kt + 1, min(nk - 1, kt + kWAhead) - (kt + 1));
+      frags(smem + ((kt + 1) % kWStages) * kWStageBytes, 0, fa0, fb0);
+    }
+    mma(fa1, fb1);
+  }
+
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = n0 + wn + 32 * j + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m < M && n < N) {
+          if constexpr (ZT == DFS_F32)
+            ((float*)a.Z)[(int64_t)m * N + n] = acc[i][j][v];
+          else
+            ((_Float16*)a.Z)[(int64_t)m * N + n] = (_Float16)acc[i][j][v];
+        }
+      }
+    }
+}
+
 // Z = the sum of the ks partial products, in slice order (deterministic).
 template <int ZT>
 __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* part, int ks, int64_t n,
@@ -365,6 +589,10 @@ __global__ __launch_bounds__(256) void nvfp4_to_f16_kernel(const uint8_t* codes,
   *reinterpret_cast<h8*>(out + i8) = o;
 }
 
+int gemm_wide_tiles(int64_t rows, int n_atoms) {
+  return (int)((rows + 255) / 256) * ((n_atoms + 255) / 256);
+}
+
 template <int ZT, int BM, int BN>
 hipError_t launch_tile(const XdLaunch& a, hipStream_t s) {
   auto kern = gemm_xd_kernel<ZT, BM, BN>;
@@ -386,9 +614,23 @@ hipError_t launch_tile(const XdLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int ZT, int TM, int TN, int OCC>
+hipError_t launch_wide(const XdLaunch& a, hipStream_t s) {
+  auto kern = gemm_xd_wide_kernel<ZT, TM, TN, OCC>;
+  constexpr size_t smem = WTile<TM, TN>::kSmemBytes;
+  hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (err != hipSuccess) return err;
+  const int64_t M = (int64_t)a.n_layers * a.T;
+  const int tiles = (int)((M + TM - 1) / TM) * ((a.k + TN - 1) / TN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), smem, s, a);
+  return hipGetLastError();
+}
+
 template <int ZT>
 hipError_t launch_z(const XdLaunch& a, hipStream_t s) {
   if (a.n_layers * a.T <= 128) return launch_tile<ZT, 64, 64>(a, s);
+  if (gemm_wide_tiles(a.n_layers * a.T, a.k) >= 256) return launch_wide<ZT, 256, 256, 1>(a, s);
   return launch_tile<ZT, 256, 128>(a, s);
 }
 

@@ -68,6 +68,18 @@ def test_qproj_prefill_full_size_sampled():
         assert_close(Ys[l][torch.from_numpy(rows).to(DEV)], ref, f"prefill layer {l}")
 
 
+def test_wide_tile_prefill_ragged_sampled():
+    # 2 x 4100 stacked rows and k = 2000 make 33 x 8 tiles of 256 x 256 (the
+    # wide MFMA tile; the last row and atom tiles are partial) and d_in = 2056
+    # leaves a short last K tile of 8.
+    say("case: wide-tile prefill, 2 x T=4100, d_in=2056, k=2000 (sampled tokens)")
+    g = synth.make_group("qproj", d_in=2056, d_out=272, k=2000, T=4100, n_layers=2)
+    Ys, _ = _run_group(g)
+    rows = np.array([0, 1, 31, 255, 256, 257, 2047, 3839, 3840, 4091, 4092, 4095, 4096, 4099])
+    for l, ref in enumerate(oracle_group(g, rows=rows)):
+        assert_close(Ys[l][torch.from_numpy(rows).to(DEV)], ref, f"wide layer {l}")
+
+
 @pytest.mark.parametrize("T", [17, 100, 300])
 def test_prefill_ragged_tiles_full(T):
     say(f"case: mid-size prefill T={T} (MFMA + SpMM, ragged tiles)")
