@@ -102,8 +102,11 @@ struct Split {
   static constexpr int CPB = kThreads / LPC;         // columns per workgroup
 };
 
+// The token tile is the largest whose Z tile fits 144 KiB, so at the sizes
+// that matter a CU runs one workgroup (k = 2048: 131 KiB): two waves per
+// SIMD, which the register allocation may assume.
 template <int VT, int ZT, int TT>
-__global__ __launch_bounds__(kThreads) void spmm_csc_kernel(ZcLaunch a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void spmm_csc_kernel(ZcLaunch a) {
   constexpr int LPC = Split<TT>::LPC, NT = Split<TT>::NT, CPB = Split<TT>::CPB;
   constexpr int kU = kUnroll<VT>;
   extern __shared__ __attribute__((aligned(16))) char zraw[];
@@ -153,6 +156,25 @@ __global__ __launch_bounds__(kThreads) void spmm_csc_kernel(ZcLaunch a) {
   const _Float16* zl = zt + sub * NT;
   const uint32_t len = (uint32_t)(e - s);
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int pb) {
+    // A batch that lies inside every active lane's column (all but the
+    // first and the last one or two of a column) needs no mask: the index
+    // is the row and the value enters the multiply-add as stored.
+    if (__all(pb >= s && pb + 8 * kU <= e)) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        ValChunk<VT> vu = vc[u];
+        vu.touch();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ZRow<NT> z;
+          z.read(zl + ic[u].get(i) * TT);
+          const float v = vu.get(i);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(z.get(t), v, acc[t]);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       ValChunk<VT> vu = vc[u];
