@@ -279,11 +279,28 @@ def main():
             torch.cuda.synchronize()
             res[name] = ev0.elapsed_time(ev1) / nrep
         gemm_flop, spmm_flop = L.group_flops(d_in=gp.d_in, k=gp.k, T=gp.T, nnzs=nnzs)
+        # the matrix cores' sustained rate on this device (register-only
+        # MFMA probe, two workgroups per CU), the measured counterpart of the
+        # nominal peak
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        pb, pit = 2 * cus, 4096
+        pout = B.probe_mfma(pb, pit, device=dev)
+        torch.cuda.synchronize()
+        pts = []
+        for _ in range(5):
+            ev0.record()
+            B.probe_mfma(pb, pit, out=pout)
+            ev1.record()
+            torch.cuda.synchronize()
+            pts.append(ev0.elapsed_time(ev1))
+        probe_tflops = B.probe_mfma_flop(pb, pit) / (sorted(pts)[2] * 1e-3) / 1e12
+        gemm_tflops = gemm_flop / (res["gemm_xd_mfma"] * 1e-3) / 1e12
         extras["prefill_T2048_group2"] = {
             "gemm_xd_mfma_us": round(res["gemm_xd_mfma"] * 1e3, 2),
             "gemm_tflops": round(gemm_flop / (res["gemm_xd_mfma"] * 1e-3) / 1e12, 1),
-            "gemm_frac_of_fp16_mfma_peak": round(
-                gemm_flop / (res["gemm_xd_mfma"] * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+            "gemm_frac_of_fp16_mfma_peak": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+            "mfma_probe_tflops": round(probe_tflops, 1),
+            "gemm_frac_of_measured_mfma_rate": round(gemm_tflops / probe_tflops, 4),
             "spmm_csc_us": round(res["spmm_csc"] * 1e3, 2),
             "spmm_useful_tflops": round(spmm_flop / (res["spmm_csc"] * 1e-3) / 1e12, 2),
             "group_forward_ms": round(res["group_forward"], 4),

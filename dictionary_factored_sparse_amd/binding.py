@@ -31,7 +31,7 @@ SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspac
            "dfs_status_str", "dfs_last_hip_error", "dfs_version", "dict_csc_capacity",
            "dict_csc_quantize8_workspace_size", "dict_csc_quantize8",
            "dict_gram_inverse_workspace_size", "dict_gram_inverse", "dict_obs_prune",
-           "dict_refit_workspace_size", "dict_refit", "dict_pack_bcsc")
+           "dict_refit_workspace_size", "dict_refit", "dict_pack_bcsc", "dfs_probe_mfma")
 
 
 class NV(C.Structure):
@@ -96,6 +96,7 @@ def lib():
             "dict_obs_prune": [i32, i32, vp, i64, vp, i64, i32, vp, i64, vp, i64, vp],
             "dict_refit_workspace_size": [i32, i32, psz],
             "dict_refit": [i32, i32, i32, vp, i64, vp, i64, C.c_float, vp, i64, vp, sz, vp],
+            "dfs_probe_mfma": [i32, i32, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -486,3 +487,19 @@ def to_device_csc(dense_np, device, nvfp4: bool = False, fmt: str | None = None)
     if fmt in CODE8:
         return csc_quantize8(c, fmt)
     return c
+
+
+# ----------------------------------------------------------------- measurement support
+
+def probe_mfma(blocks: int, iters: int, device="cuda:0", out=None, stream=None):
+    """Matrix-core probe: blocks x 256 threads, each wave `iters` rounds of 8
+    independent 32x32x16 f16 MFMAs on registers (blocks * 4 * iters * 8 *
+    32768 FLOP).  Returns the per-thread outputs (blocks * 256 floats)."""
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    _check("dfs_probe_mfma", lib().dfs_probe_mfma(blocks, iters, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def probe_mfma_flop(blocks: int, iters: int) -> float:
+    return float(blocks) * 4 * iters * 8 * 32768

@@ -263,7 +263,14 @@ const char* dfs_status_str(dfs_status st) {
 
 int32_t dfs_last_hip_error(void) { return g_last_hip; }
 
-int32_t dfs_version(void) { return 300; }
+int32_t dfs_version(void) { return 301; }
+
+dfs_status dfs_probe_mfma(int32_t blocks, int32_t iters, float* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out) return DFS_E_INVALID;
+  if (blocks > (1 << 20)) return DFS_E_RANGE;
+  DFS_HIP(launch_mfma_peak(blocks, iters, out, (hipStream_t)stream));
+  return DFS_OK;
+}
 
 int64_t dict_csc_capacity(int64_t nnz) {
   if (nnz < 8) return 8;

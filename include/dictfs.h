@@ -338,6 +338,19 @@ int32_t dfs_last_hip_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t dfs_version(void);
 
+/* Matrix-core probe (measurement support, not a step of the method): blocks
+ * workgroups of 256 threads; every wave runs iters rounds of 8 independent
+ * v_mfma_f32_32x32x16_f16 on register operands, so the work is
+ * blocks * 4 * iters * 8 * 32768 FLOP with no memory traffic except one
+ * float per thread written to out (device memory, blocks * 256 floats,
+ * caller-owned).  Two workgroups fit a CU.  Timed by the caller, it gives the
+ * sustained fp16 MFMA rate of the device, the measured counterpart of the
+ * nominal peak for the prefill GEMM (Eq. (1), Z = X D_g at prefill).  Every
+ * thread's value is the same function of iters alone (exact in fp32 for
+ * iters <= 2^16), so equal outputs across blocks and out(n) = n * out(1)
+ * check it ran.  0 < blocks <= 2^20, iters > 0; enqueued on stream. */
+dfs_status dfs_probe_mfma(int32_t blocks, int32_t iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

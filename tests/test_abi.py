@@ -27,7 +27,7 @@ def header_functions():
                           re.M))
 
 
-def test_header_declares_the_north_star_calls():
+def test_header_declares_the_boundary_calls():
     fns = header_functions()
     for name in ("dict_pack_csc", "dict_proj_forward", "dict_group_forward", "nvfp4_pack",
                  "nvfp4_unpack"):
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert fns == set(B.SYMBOLS)
     for name in fns:
         assert hasattr(L, name), name
-    assert L.dfs_version() == 300
+    assert L.dfs_version() == 301
     assert L.dfs_status_str(0) == b"ok"
     assert L.dfs_status_str(6) == b"HIP runtime error"
 
@@ -276,3 +276,12 @@ def test_block_csc_validation():
                             1 << 20, None) == INVALID
     assert L.dict_pack_bcsc(P, B.DFS_F16, 128, 64, 64, P, None, None, 0, C.byref(nb), P,
                             8, None) == WORKSPACE
+
+
+def test_probe_validation():
+    # rejected before any launch (no GPU needed)
+    L = B.lib()
+    assert L.dfs_probe_mfma(0, 1, P, None) == INVALID
+    assert L.dfs_probe_mfma(4, 0, P, None) == INVALID
+    assert L.dfs_probe_mfma(4, 1, None, None) == INVALID
+    assert L.dfs_probe_mfma((1 << 20) + 1, 1, P, None) == RANGE
