@@ -7,9 +7,10 @@
 // the column's row indices and values from HBM with coalesced 16-byte loads
 // and gathers the matching Z entries from LDS.
 //
-// Mapping: a workgroup is 4 waves (8 with the f16 tile); each wave serves
-// 4 columns at once, one per 16-lane DPP row.  Lane g of a row reads the 8-entry chunks g, g+16, ...
-// of its column (128 entries per step), U steps in flight per batch, every
+// Mapping: a workgroup is 4 waves (8 with the f16 tile, 16 with its 16-token
+// form); each wave serves 4 columns at once, one per 16-lane DPP row.  Lane
+// g of a row reads the 8-entry chunks g, g+16, ... of its column (128
+// entries per step), U steps in flight per batch, every
 // lane issuing the same loads (past its column it reloads the column's last
 // chunk, masked).  The first batch is issued before Z is staged into
 // LDS (C does not depend on Z).  The Z tile is [k][TT] fp32 (TT tokens per
@@ -25,10 +26,13 @@ namespace dfs {
 namespace {
 
 constexpr int kThreads = 256;      // fp32 Z tile (small T)
-constexpr int kThreadsH = 512;     // f16 Z tile: one large tile per CU, 2 waves per SIMD share it
-
-template <bool ZH>
-constexpr int threads_of() { return ZH ? kThreadsH : kThreads; }
+// f16 Z tile: one large tile per CU, shared by 2 waves per SIMD, or by 4 for
+// the 16-token tile, whose gather chains (LDS read, then 16 multiply-adds per
+// entry) need the extra waves to cover LDS latency (MLP group of 4 at
+// b = 16: gate 68.6 -> 63.8 us, down 52.8 -> 48.5 us); it then holds one
+// chunk per lane to fit 128 registers.
+template <bool ZH, int TT>
+constexpr int threads_of() { return ZH ? (TT >= 16 ? 1024 : 512) : kThreads; }
 
 // 8-entry chunks in flight per lane per batch: with 16 lanes per column a
 // batch covers 128 * U entries, enough for a whole column at the densities of
@@ -36,7 +40,7 @@ constexpr int threads_of() { return ZH ? kThreadsH : kThreads; }
 // tiles keep fewer chunks so that the accumulators and Z reads fit.
 template <int VT, int TT, bool ZH>
 struct Unroll {
-  static constexpr int U = ZH ? (TT >= 16 ? 2 : TT >= 8 ? 3 : (VT == DFS_F32 || VT == DFS_INT8 ? 3 : 4))
+  static constexpr int U = ZH ? (TT >= 16 ? 1 : TT >= 8 ? 3 : (VT == DFS_F32 || VT == DFS_INT8 ? 3 : 4))
                               : TT >= 16 ? 1 : TT >= 8 ? 2 : TT >= 4 ? 4 : (VT == DFS_F32 ? 3 : 6);
 };
 
@@ -167,8 +171,8 @@ __device__ __forceinline__ void stage_z(float* zs, const void* Z, int64_t row0, 
 }
 
 template <int VT, int ZT, int TT, bool ZH>
-__global__ __launch_bounds__(threads_of<ZH>()) void spmv_csc_kernel(ZcLaunch a) {
-  constexpr int NTH = threads_of<ZH>();
+__global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaunch a) {
+  constexpr int NTH = threads_of<ZH, TT>();
   constexpr int CPG = NTH / 16;  // columns per group: 4 per wave, one per DPP row
   constexpr int U = Unroll<VT, TT, ZH>::U;
   extern __shared__ __attribute__((aligned(16))) float zs[];  // [k][TT] fp32, or f16 (ZH)
@@ -314,7 +318,7 @@ hipError_t launch3(const ZcLaunch& a, hipStream_t s) {
   // a fixed number of workgroups (one per CU when the f16 tile limits the
   // CU to one workgroup, two per CU otherwise), split evenly over the
   // layers; each stages Z once for an equal run of column groups
-  constexpr int NTH = threads_of<ZH>();
+  constexpr int NTH = threads_of<ZH, TT>();
   const int ngroups = (a.d_out + NTH / 16 - 1) / (NTH / 16);
   const int target = ZH ? 256 : 512;
   int per_layer = target / a.n_layers;
