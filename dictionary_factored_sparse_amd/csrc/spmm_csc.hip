@@ -16,17 +16,24 @@
 // issuing the same loads (past its column it reloads the column's last
 // chunk, masked), so the compiler can wait for exactly the batch it needs.
 // Costs per MAC: one VALU op and 2 bytes of LDS.
-// grid = (ceil(d_out / (kThreads / LPC)), ceil(T / TT), n_layers).
+// grid = (ceil(d_out / (threads / LPC)), ceil(T / TT), n_layers).
 #include "csc_chunks.hpp"
 
 namespace dfs {
 namespace {
 
-constexpr int kThreads = 512;
-// 8-entry chunks per batch (NVFP4 and 8-bit codes decode on use and need
-// the registers)
+// Threads per workgroup.  The Z tile holds most of a CU's LDS at the sizes
+// that matter (k = 2048: 131 KiB), so a CU runs one workgroup, and its waves
+// must cover the latency of each entry's chain (LDS gather, then NT
+// multiply-adds): 1024 threads (four waves per SIMD) measured 683 -> 586 us
+// against 512 for the q_proj group's prefill.  NVFP4 and 8-bit codes decode
+// on use and would not fit the 128 registers of four waves per SIMD: 512.
 template <int VT>
-constexpr int kUnroll = (VT == DFS_NVFP4 || kIsCode8<VT>) ? 2 : 4;
+constexpr int spmm_threads() { return (VT == DFS_F16 || VT == DFS_F32) ? 1024 : 512; }
+// 8-entry chunks per batch (double-buffered): two, which fits the registers
+// of four waves per SIMD
+template <int VT>
+constexpr int kUnroll = 2;
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
@@ -54,7 +61,7 @@ struct ZRow<4> {
 // Stage Z rows [row0, row0 + rows) (tokens) into the f16 tile [k + 1][TT].
 // Thread (token t, atom group) converts 8 atoms of token t per step: one
 // 16-byte load (32 for f32 Z) when k % 8 == 0, elementwise otherwise.
-template <int ZT, int TT>
+template <int ZT, int TT, int kThreads>
 __device__ __forceinline__ void stage_z(_Float16* zt, const void* Z, int64_t row0, int rows,
                                         int k) {
   constexpr int kGroups = kThreads / TT;
@@ -95,19 +102,17 @@ __device__ __forceinline__ void stage_z(_Float16* zt, const void* Z, int64_t row
   for (int i = threadIdx.x; i < TT; i += kThreads) zt[k * TT + i] = (_Float16)0.0f;
 }
 
-template <int TT>
+template <int VT, int TT>
 struct Split {
+  static constexpr int kThreads = spmm_threads<VT>();
   static constexpr int LPC = TT > 16 ? TT / 16 : 1;  // lanes per column
   static constexpr int NT = TT / LPC;                // tokens per lane
   static constexpr int CPB = kThreads / LPC;         // columns per workgroup
 };
 
-// The token tile is the largest whose Z tile fits 144 KiB, so at the sizes
-// that matter a CU runs one workgroup (k = 2048: 131 KiB): two waves per
-// SIMD, which the register allocation may assume.
 template <int VT, int ZT, int TT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void spmm_csc_kernel(ZcLaunch a) {
-  constexpr int LPC = Split<TT>::LPC, NT = Split<TT>::NT, CPB = Split<TT>::CPB;
+__global__ __launch_bounds__(spmm_threads<VT>()) void spmm_csc_kernel(ZcLaunch a) {
+  constexpr int LPC = Split<VT, TT>::LPC, NT = Split<VT, TT>::NT, CPB = Split<VT, TT>::CPB;
   constexpr int kU = kUnroll<VT>;
   extern __shared__ __attribute__((aligned(16))) char zraw[];
   _Float16* zt = reinterpret_cast<_Float16*>(zraw);
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // the first batch does not depend on Z: in flight while the tile is staged
   int p = s & ~7;
   load(ia, va, p);
-  stage_z<ZT, TT>(zt, a.Z, (int64_t)layer * a.T + t0, rows, k);
+  stage_z<ZT, TT, spmm_threads<VT>()>(zt, a.Z, (int64_t)layer * a.T + t0, rows, k);
   __syncthreads();
 
   float acc[NT];
@@ -232,9 +237,9 @@ hipError_t launch3(const ZcLaunch& a, hipStream_t s) {
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess) return err;
   }
-  constexpr int CPB = Split<TT>::CPB;
+  constexpr int CPB = Split<VT, TT>::CPB;
   dim3 grid((a.d_out + CPB - 1) / CPB, (a.T + TT - 1) / TT, a.n_layers);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
+  hipLaunchKernelGGL(kern, grid, dim3(spmm_threads<VT>()), smem, s, a);
   return hipGetLastError();
 }
 
