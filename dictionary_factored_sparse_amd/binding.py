@@ -31,7 +31,8 @@ SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspac
            "dfs_status_str", "dfs_last_hip_error", "dfs_version", "dict_csc_capacity",
            "dict_csc_quantize8_workspace_size", "dict_csc_quantize8",
            "dict_gram_inverse_workspace_size", "dict_gram_inverse", "dict_obs_prune",
-           "dict_refit_workspace_size", "dict_refit", "dict_pack_bcsc", "dfs_probe_mfma")
+           "dict_refit_workspace_size", "dict_refit", "dict_pack_bcsc", "dfs_probe_mfma",
+           "dict_multi_workspace_size", "dict_multi_forward")
 
 
 class NV(C.Structure):
@@ -97,6 +98,9 @@ def lib():
             "dict_refit_workspace_size": [i32, i32, psz],
             "dict_refit": [i32, i32, i32, vp, i64, vp, i64, C.c_float, vp, i64, vp, sz, vp],
             "dfs_probe_mfma": [i32, i32, vp, vp],
+            "dict_multi_workspace_size": [i32, i32, i32, C.POINTER(Dict), C.POINTER(Csc), psz],
+            "dict_multi_forward": [i32, i32, C.POINTER(vp), i32, i32, i64, C.POINTER(Dict),
+                                   C.POINTER(Csc), C.POINTER(vp), i32, i64, vp, sz, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -356,6 +360,41 @@ def dict_group_forward(Xs, D: DeviceDict, Cs, Ys=None, ydtype=torch.float16, ws=
     d = D.desc()
     _check("dict_group_forward",
            lib().dict_group_forward(n, xp, _dt(Xs[0]), T, Xs[0].stride(0), C.byref(d), cs, yp,
+                                    _dt(Ys[0]), Ys[0].stride(0), ws.data_ptr(), ws.numel(),
+                                    _stream(stream)))
+    return Ys
+
+
+def multi_workspace(n_dicts: int, n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC,
+                    device) -> torch.Tensor:
+    """Workspace of dict_multi_forward, zeroed (its first 4096 bytes are the
+    control block, zero before first use)."""
+    n = C.c_size_t(0)
+    d, c = D.desc(), Cs.desc()
+    _check("dict_multi_workspace_size",
+           lib().dict_multi_workspace_size(n_dicts, n_layers, T, C.byref(d), C.byref(c),
+                                           C.byref(n)))
+    return torch.zeros(n.value, dtype=torch.uint8, device=device)
+
+
+def dict_multi_forward(Xs, Ds, Cs, Ys=None, ydtype=torch.float16, ws=None, stream=None):
+    """Y[d * n + l] = (X_l D_d) C[d * n + l] for n = len(Xs) layers and the
+    dictionaries Ds (q, k, v-like groups over the same activations); Cs is
+    dictionary-major.  Returns the list of Y."""
+    n, nd = len(Xs), len(Ds)
+    assert len(Cs) == n * nd
+    T = Xs[0].shape[0]
+    dev = Xs[0].device
+    if Ys is None:
+        Ys = [torch.empty(T, Cs[0].d_out, dtype=ydtype, device=dev) for _ in range(n * nd)]
+    if ws is None:
+        ws = multi_workspace(nd, n, T, Ds[0], Cs[0], dev)
+    xp = (C.c_void_p * n)(*[x.data_ptr() for x in Xs])
+    yp = (C.c_void_p * (n * nd))(*[y.data_ptr() for y in Ys])
+    ds = (Dict * nd)(*[D.desc() for D in Ds])
+    cs = (Csc * (n * nd))(*[c.desc() for c in Cs])
+    _check("dict_multi_forward",
+           lib().dict_multi_forward(nd, n, xp, _dt(Xs[0]), T, Xs[0].stride(0), ds, cs, yp,
                                     _dt(Ys[0]), Ys[0].stride(0), ws.data_ptr(), ws.numel(),
                                     _stream(stream)))
     return Ys

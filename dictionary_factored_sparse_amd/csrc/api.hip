@@ -548,10 +548,13 @@ dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t
   return run_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy, (hipStream_t)stream);
 }
 
-dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xdt, int32_t T,
-                              int64_t ldx, const dfs_dict* D, const dfs_csc* C, void* const* Y,
-                              int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+// Every argument of a group forward, checked before anything is launched.
+dfs_status check_group(int32_t n_layers, const void* const* X, int32_t xdt, int32_t T,
+                       int64_t ldx, const dfs_dict* D, const dfs_csc* C, void* const* Y,
+                       int32_t ydt, int64_t ldy) {
   if (n_layers <= 0 || T < 0 || !X || !C || !Y) return DFS_E_INVALID;
   if (n_layers > kMaxLayers) return DFS_E_RANGE;
   DFS_TRY(check_dict(D));
@@ -566,6 +569,20 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
   if (T == 0) return DFS_OK;  // no rows: the activation pointers may be null
   DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
   DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
+  return DFS_OK;
+}
+
+constexpr int32_t kMaxMultiDicts = 8;
+}  // namespace
+
+extern "C" {
+
+dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xdt, int32_t T,
+                              int64_t ldx, const dfs_dict* D, const dfs_csc* C, void* const* Y,
+                              int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                              void* stream) {
+  DFS_TRY(check_group(n_layers, X, xdt, T, ldx, D, C, Y, ydt, ldy));
+  if (T == 0) return DFS_OK;
   const int64_t rows = (int64_t)n_layers * T;
   const bool mfma = mfma_path(rows, xdt, D);
   const int32_t zdt = mfma ? DFS_F16 : DFS_F32;
@@ -588,6 +605,62 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
   }
   DFS_TRY(run_xd(n_layers, X, xdt, T, ldx, D, Z, zdt, xws, s));
   return run_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy, s);
+}
+
+dfs_status dict_multi_workspace_size(int32_t n_dicts, int32_t n_layers, int32_t T,
+                                     const dfs_dict* D, const dfs_csc* C, size_t* bytes) {
+  if (!bytes || !D || !C || n_dicts <= 0) return DFS_E_INVALID;
+  if (n_dicts > kMaxMultiDicts) return DFS_E_RANGE;
+  size_t one = 0;
+  DFS_TRY(dict_workspace_size(n_layers, T, D, C, &one));  // one group at a time
+  const int64_t rows = (int64_t)n_layers * T;
+  size_t all = 0;  // the one-launch decode: (epoch, value) words of every unit
+  if (rows <= kGemvMaxRows) all = kCtrlBytes + round256((size_t)n_dicts * rows * D->k * 8);
+  *bytes = one > all ? one : all;
+  return DFS_OK;
+}
+
+dfs_status dict_multi_forward(int32_t n_dicts, int32_t n_layers, const void* const* X,
+                              int32_t xdt, int32_t T, int64_t ldx, const dfs_dict* D,
+                              const dfs_csc* C, void* const* Y, int32_t ydt, int64_t ldy,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (n_dicts <= 0 || !D || !C || !Y) return DFS_E_INVALID;
+  if (n_dicts > kMaxMultiDicts) return DFS_E_RANGE;
+  // every group valid, one shape and type for all dictionaries and for all
+  // coefficient matrices, before anything is launched
+  for (int d = 0; d < n_dicts; ++d) {
+    DFS_TRY(check_group(n_layers, X, xdt, T, ldx, &D[d], C + (size_t)d * n_layers,
+                        Y + (size_t)d * n_layers, ydt, ldy));
+    if (D[d].d_in != D[0].d_in || D[d].k != D[0].k || D[d].dtype != D[0].dtype ||
+        D[d].ldd != D[0].ldd)
+      return DFS_E_INVALID;
+    const dfs_csc& c = C[(size_t)d * n_layers];
+    if (c.d_out != C[0].d_out || c.dtype != C[0].dtype || c.block_rows != C[0].block_rows)
+      return DFS_E_INVALID;
+  }
+  if (T == 0) return DFS_OK;
+  size_t need = 0;
+  DFS_TRY(dict_multi_workspace_size(n_dicts, n_layers, T, D, C, &need));
+  if (!ws || ws_bytes < need) return DFS_E_WORKSPACE;
+  if (!aligned16(ws)) return DFS_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (n_dicts > 1 && n_dicts <= kFusedMaxDicts && fused_allowed()) {
+    uint32_t* ctrl = (uint32_t*)ws;
+    void* Z = (char*)ws + kCtrlBytes;
+    XdLaunch xa = make_xd(n_layers, X, xdt, T, ldx, &D[0], Z, DFS_F32);
+    xa.n_dicts = n_dicts;
+    for (int d = 1; d < n_dicts; ++d)
+      xa.more[d - 1] = {D[d].data, D[d].nv.codes, D[d].nv.scales, D[d].nv.tensor_scale};
+    ZcLaunch za = make_zc(n_dicts * n_layers, Z, DFS_F32, T, C, Y, ydt, ldy);
+    if ((int64_t)n_dicts * n_layers <= kMaxLayers && fused_decode_supported(xa, za)) {
+      DFS_HIP(launch_fused_decode(xa, za, (float*)Z, ctrl, s));
+      return DFS_OK;
+    }
+  }
+  for (int d = 0; d < n_dicts; ++d)
+    DFS_TRY(dict_group_forward(n_layers, X, xdt, T, ldx, &D[d], C + (size_t)d * n_layers,
+                               Y + (size_t)d * n_layers, ydt, ldy, ws, ws_bytes, stream));
+  return DFS_OK;
 }
 
 dfs_status dict_proj_forward(const void* X, int32_t xdt, int32_t T, int64_t ldx, const dfs_dict* D,

@@ -126,6 +126,16 @@ struct XdLaunch {
   void* Z;              // (n_layers*T) x k row-major
   int32_t zdt;
   float* zpart;         // MFMA path with split K: [ksplit][rows][k] fp32 partials
+  // Further dictionaries over the same X rows (the one-launch decode of
+  // several projections that share their input, e.g. q, k and v): same
+  // d_in, k, dtype and ldd as D; 0 means one dictionary.
+  int32_t n_dicts;
+  struct {
+    const void* D;
+    const uint8_t* dcodes;
+    const uint8_t* dscales;
+    const float* dts;
+  } more[2];
 };
 
 struct ZcLaunch {
@@ -148,8 +158,12 @@ struct ZcLaunch {
 // Rows at or below which X.D runs on VALU dot products instead of MFMA.
 constexpr int kGemvMaxRows = 16;
 
-// One-launch decode of a group (T == 1, up to 4 layers).
+// One-launch decode of a group (T == 1, up to 4 layers), or of up to 3
+// dictionaries over the same X rows (up to 2 layers; the ZcLaunch then holds
+// one unit per (dictionary, layer), dictionary-major).
 constexpr int kFusedMaxLayers = 4;
+constexpr int kFusedMaxDicts = 3;
+constexpr int kFusedMaxUnits = 8;
 constexpr int kCtrlBlockBytes = 4096;   // forward workspace control block
 constexpr int kMaxFusedGroups = 768;  // per-workgroup epoch words from byte 1024
 bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc);

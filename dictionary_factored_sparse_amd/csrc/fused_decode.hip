@@ -144,20 +144,23 @@ __device__ __forceinline__ float gather_chunk(const float* zl, IdxChunk ic, ValC
 }
 
 // Kernel arguments, compact so that they fit a few scalar-cache lines: the
-// first line holds everything the first loads need.
+// first line holds everything the first loads need.  NU units (the outputs:
+// one coefficient matrix and Y each), 4 for one dictionary (one unit per
+// layer) and 8 for several (one per dictionary and layer).
+template <int NU>
 struct FusedArgs {
   const void* D;  // f16 atoms, or NVFP4 codes
   const uint8_t* dscales;
   int64_t ldd;
   int32_t d_in, k;
   const void* X[kFusedMaxLayers];
-  const int32_t* colptr[kFusedMaxLayers];
-  const uint16_t* rowidx[kFusedMaxLayers];
-  const void* vals[kFusedMaxLayers];
-  const uint8_t* vscales[kFusedMaxLayers];
-  const float* vts[kFusedMaxLayers];  // NVFP4 tensor scale, or FP8/INT8 column scales
-  void* Y[kFusedMaxLayers];
-  int64_t nnz[kFusedMaxLayers];
+  const int32_t* colptr[NU];
+  const uint16_t* rowidx[NU];
+  const void* vals[NU];
+  const uint8_t* vscales[NU];
+  const float* vts[NU];  // NVFP4 tensor scale, or FP8/INT8 column scales
+  void* Y[NU];
+  int64_t nnz[NU];
   const float* dts;
   uint64_t* zz;    // n_layers x k epoch-tagged Z words
   uint32_t* ctrl;  // control block
@@ -170,6 +173,13 @@ struct FusedArgs {
   // a barrier before any of them writes Z: a wave that has finished its dot
   // products would otherwise overwrite X under a wave still reading it.
   int32_t z_off;
+  // several dictionaries over the same X rows: their count, and the codes,
+  // block scales and tensor scale of dictionaries 1 and 2 (same d_in, k, ldd
+  // and dtype as dictionary 0)
+  int32_t n_dicts;
+  const void* Dx[kFusedMaxDicts - 1];
+  const uint8_t* dscalesx[kFusedMaxDicts - 1];
+  const float* dtsx[kFusedMaxDicts - 1];
 };
 
 // A column's entry in LDS: [start, end) of its stored entries, and for 8-bit
@@ -177,16 +187,29 @@ struct FusedArgs {
 template <int VT>
 using ColEntry = typename std::conditional<kIsCode8<VT>, int4, int2>::type;
 
-template <int DT, int VT, int RT, int A, int NX>
-__global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
+// Units of the argument struct and bytes of the LDS unit table for ND
+// dictionaries.
+template <int ND>
+constexpr int units_of() { return ND == 1 ? kFusedMaxLayers : kFusedMaxUnits; }
+template <int ND>
+constexpr int table_bytes_of() { return ND == 1 ? kLayerTableBytes : 2 * kLayerTableBytes; }
+static_assert(sizeof(LayerRow) * kFusedMaxLayers <= kLayerTableBytes, "unit table");
+static_assert(sizeof(LayerRow) * kFusedMaxUnits <= 2 * kLayerTableBytes, "unit table");
+
+// ND dictionaries over the same X rows: atoms [d k, (d + 1) k) of the atom
+// space are dictionary d's, and unit d * n_layers + l (coefficients and Y)
+// reads Z row l of dictionary d.  ND = 1 is the group of one dictionary.
+template <int DT, int VT, int RT, int A, int NX, int ND>
+__global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of<ND>()> f) {
   using Cf = Cfg<DT, DFS_F16, RT>;
   using CE_t = ColEntry<VT>;
   constexpr bool Q8 = kIsCode8<VT>;
   constexpr int CE = Cf::CE, SEGC = Cf::SEGC, SEG = Cf::SEG;
+  constexpr int NU = units_of<ND>(), kTable = table_bytes_of<ND>();
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  LayerRow* lt = reinterpret_cast<LayerRow*>(smem);            // [kFusedMaxLayers]
-  CE_t* cse = reinterpret_cast<CE_t*>(smem + kLayerTableBytes);  // [ncols]
-  char* big = smem + kLayerTableBytes + f.col_bytes;           // X rows, then Z
+  LayerRow* lt = reinterpret_cast<LayerRow*>(smem);            // [NU]
+  CE_t* cse = reinterpret_cast<CE_t*>(smem + kTable);          // [ncols]
+  char* big = smem + kTable + f.col_bytes;                     // X rows, then Z
   _Float16* xs = reinterpret_cast<_Float16*>(big);
   float* zs = reinterpret_cast<float*>(big + f.z_off);
 
@@ -215,6 +238,9 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
                  "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
                  "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G));
+  if constexpr (ND > 1)
+    asm volatile("" ::"s"(f.Dx[0]), "s"(f.Dx[ND > 2 ? 1 : 0]), "s"(f.dscalesx[0]),
+                 "s"(f.dscalesx[ND > 2 ? 1 : 0]), "s"(f.colptr[4]), "s"(f.colptr[5]));
   static_assert(SEG % (8 * kFT) == 0, "an X row is a whole number of 512-thread passes");
   constexpr int NR = NX / RT;  // passes of the workgroup per X row
   static_assert(NR * RT == NX, "X register count");
@@ -242,7 +268,8 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     xr[jx] = ok ? v : u4{0u, 0u, 0u, 0u};
   }
   // ---- 2. this launch's epoch word and the bounds of this workgroup's columns
-  const uint32_t NC = (uint32_t)(nl * d_out);  // NC * (G + 1) < 2^32 (host check)
+  const int nu = ND == 1 ? nl : ND * nl;  // units: (dictionary, layer) pairs
+  const uint32_t NC = (uint32_t)(nu * d_out);  // NC * (G + 1) < 2^32 (host check)
   const int c0 = (int)(blockIdx.x * NC / (uint32_t)f.G);
   const int c1 = (int)((blockIdx.x + 1) * NC / (uint32_t)f.G);
   const int ncols = c1 - c0;  // <= kFT (checked on the host)
@@ -257,7 +284,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     const int l = (c0 + ci) / d_out, j = c0 + ci - l * d_out;
     const int32_t* cpr = sreg_ptr(f.colptr[0]);
 #pragma unroll
-    for (int i = 1; i < kFusedMaxLayers; ++i)
+    for (int i = 1; i < NU; ++i)
       if (l == i) cpr = sreg_ptr(f.colptr[i]);
     rs_raw[r] = gptr(cpr)[j];
     re_raw[r] = gptr(cpr)[j + 1];
@@ -268,14 +295,14 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   const int cl = (c0 + cidx) / d_out, cj = c0 + cidx - cl * d_out;
   const int32_t* cp = sreg_ptr(f.colptr[0]);
 #pragma unroll
-  for (int i = 1; i < kFusedMaxLayers; ++i)
+  for (int i = 1; i < NU; ++i)
     if (cl == i) cp = sreg_ptr(f.colptr[i]);
   const int s_raw = gptr(cp)[cj], e_raw = gptr(cp)[cj + 1];
   float cs_raw = 1.0f;
   if constexpr (Q8) {
     const float* vp = sreg_ptr(f.vts[0]);
 #pragma unroll
-    for (int i = 1; i < kFusedMaxLayers; ++i)
+    for (int i = 1; i < NU; ++i)
       if (cl == i) vp = sreg_ptr(f.vts[i]);
     cs_raw = gptr(vp)[cj];
   }
@@ -287,20 +314,32 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   const int atom0 = (blockIdx.x * kFW + wave) * A;
   u4 dreg[A][SEGC];
   uint32_t sreg[A][SEGC];
+  // atom i of this wave: dictionary dict_of(i), index atom_of(i) within it
+  // (ND = 1: dictionary 0; past the last atom, the last atom is read)
+  auto dict_of = [&](int i) {
+    if constexpr (ND == 1) return 0;
+    else return min(atom0 + i, ND * k - 1) / k;
+  };
+  auto atom_of = [&](int i) {
+    if constexpr (ND == 1) return min(atom0 + i, k - 1);
+    else return min(atom0 + i, ND * k - 1) - dict_of(i) * k;
+  };
   auto load_d = [&](int seg) {
 #pragma unroll
     for (int i = 0; i < A; ++i) {
-      const int atom = min(atom0 + i, k - 1);
+      const int atom = atom_of(i);
+      const int dd = dict_of(i);
+      const void* Dd = dd == 0 ? f.D : f.Dx[dd == 1 ? 0 : 1];
+      const uint8_t* Sd = dd == 0 ? f.dscales : f.dscalesx[dd == 1 ? 0 : 1];
 #pragma unroll
       for (int c = 0; c < SEGC; ++c) {
         const int e0 = min(seg + (c * kWave + lane) * CE, d_in - CE);
         if constexpr (DT == DFS_NVFP4) {
           const int64_t el = (int64_t)atom * d_in + e0;
-          dreg[i][c] = ld16<u4>((const uint8_t*)f.D + el / 2);
-          sreg[i][c] = (uint32_t)gptr(f.dscales)[el / 16] |
-                       ((uint32_t)gptr(f.dscales)[el / 16 + 1] << 8);
+          dreg[i][c] = ld16<u4>((const uint8_t*)Dd + el / 2);
+          sreg[i][c] = (uint32_t)gptr(Sd)[el / 16] | ((uint32_t)gptr(Sd)[el / 16 + 1] << 8);
         } else {
-          dreg[i][c] = ld16<u4>((const _Float16*)f.D + (int64_t)atom * f.ldd + e0);
+          dreg[i][c] = ld16<u4>((const _Float16*)Dd + (int64_t)atom * f.ldd + e0);
           sreg[i][c] = 0u;
         }
       }
@@ -311,7 +350,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
   // ---- 4. layer table (scalar loads) and X into LDS (waits for X only)
   if (tid == 0) {
 #pragma unroll
-    for (int l = 0; l < kFusedMaxLayers; ++l)
+    for (int l = 0; l < NU; ++l)
       lt[l] = LayerRow{f.colptr[l], f.rowidx[l], f.vals[l], f.vscales[l], f.vts[l], f.Y[l], f.nnz[l]};
   }
 #pragma unroll
@@ -339,17 +378,27 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
                                                     acc[i][r]);
     }
   }
-  float dts = 1.0f;
-  if constexpr (DT == DFS_NVFP4) dts = *gptr(f.dts);
+  float dts[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    dts[d] = 1.0f;
+    if constexpr (DT == DFS_NVFP4) dts[d] = *gptr(d == 0 ? f.dts : f.dtsx[d > 0 ? d - 1 : 0]);
+  }
   const uint32_t epoch = epoch_old + 1u;
 #pragma unroll
   for (int i = 0; i < A; ++i) {
-    const int atom = atom0 + i;
+    const int dd = dict_of(i), atom = atom_of(i);
+    const bool live = atom0 + i < ND * k;  // atoms past the last one publish nothing
+    float ts = dts[0];
+#pragma unroll
+    for (int d = 1; d < ND; ++d) ts = dd == d ? dts[d] : ts;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const float v = wave_sum(acc[i][r]) * dts;
-      if (lane == r && atom < k && r < nl)
-        st_agent64(f.zz + (int64_t)r * k + atom, ((uint64_t)epoch << 32) | __float_as_uint(v));
+      const float v = wave_sum(acc[i][r]) * ts;
+      // Z row of unit dd * nl + r (ND = 1: row r)
+      if (lane == r && live && r < nl)
+        st_agent64(f.zz + (int64_t)(dd * nl + r) * k + atom,
+                   ((uint64_t)epoch << 32) | __float_as_uint(v));
     }
   }
 
@@ -394,7 +443,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs f) {
     const uint8_t* vsc = sreg_ptr(f.vscales[0]);
     int64_t nnz = f.nnz[0];
 #pragma unroll
-    for (int i = 1; i < kFusedMaxLayers; ++i)
+    for (int i = 1; i < NU; ++i)
       if (l == i) {
         rowidx = sreg_ptr(f.rowidx[i]);
         vals = sreg_ptr(f.vals[i]);
@@ -500,6 +549,7 @@ int device_cus() {
 
 struct Plan {
   int G, A, RT, NX;  // NX = RT, 2 * RT or 3 * RT (X passes per row)
+  int ND;            // dictionaries over the X rows
   size_t col_bytes, smem;
   int z_off;         // 0 when Z overlays X
 };
@@ -508,46 +558,61 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   const bool q8 = zc.vdt == DFS_FP8 || zc.vdt == DFS_INT8;
   const int G = device_cus();
   if (G <= 0 || G > kMaxFusedGroups) return false;
-  const int nl = zc.n_layers;
-  int A = (xd.k + kFW * G - 1) / (kFW * G);  // atoms per wave
-  if (A > 2) return false;
+  const int nd = xd.n_dicts <= 1 ? 1 : xd.n_dicts;
+  if (nd > kFusedMaxDicts) return false;
+  const int nl = xd.n_layers;  // X rows
+  const int nu = zc.n_layers;  // units: one per (dictionary, layer)
+  if (nu != nd * nl) return false;
+  int A = (nd * xd.k + kFW * G - 1) / (kFW * G);  // atoms per wave
+  if (A > (nd == 1 ? 2 : 3)) return false;
   A = A < 1 ? 1 : A;
   const int RT = nl <= 1 ? 1 : (nl <= 2 ? 2 : 4);
   if (xd.ddt == DFS_NVFP4 && RT == 4 && A == 2) return false;  // would spill registers
+  if (nd > 1) {  // the instantiated multi-dictionary forms
+    if (RT > 2) return false;
+    if (xd.ddt != DFS_F16 && xd.ddt != DFS_NVFP4) return false;
+    if (zc.vdt != DFS_F16 && zc.vdt != DFS_NVFP4) return false;
+  }
   const int seg = xd.ddt == DFS_NVFP4 ? kWave * 2 * 32 : kWave * 8 * 8;  // Cfg<.., F16, RT<=4>::SEG
   const size_t ld = (size_t)(xd.d_in + seg - 1) / seg * seg;
   const size_t xbytes = (size_t)RT * ld * 2;
-  const size_t zbytes = (size_t)nl * xd.k * 4;
-  const int max_cols = (nl * zc.d_out + G - 1) / G + 1;
+  const size_t zbytes = (size_t)nu * xd.k * 4;
+  const int max_cols = (nu * zc.d_out + G - 1) / G + 1;
   if (max_cols > kFT) return false;  // one column range per thread
-  if ((uint64_t)nl * (uint64_t)zc.d_out * (uint64_t)(G + 1) >= (1ull << 32)) return false;
+  if ((uint64_t)nu * (uint64_t)zc.d_out * (uint64_t)(G + 1) >= (1ull << 32)) return false;
   const int x_items = (int)((size_t)RT * ld / 8);
   const int NX = (x_items + kFT - 1) / kFT;
   // X rows pass through registers: 1, 2 or 3 passes of the workgroup per
   // row (ld <= 12288), at most 12 16-byte registers per thread
   if (NX != RT && NX != 2 * RT && NX != 3 * RT) return false;
   if (NX > 12) return false;
+  if (nd > 1 && NX != RT) return false;  // d_in <= 4096 (f16) or 8192 (NVFP4)
   p->G = G;
   p->A = A;
   p->RT = RT;
   p->NX = NX;
+  p->ND = nd;
   p->col_bytes = ((size_t)max_cols * (q8 ? 16 : 8) + 15) / 16 * 16;
   // X and Z side by side when they fit, else Z over X (with a barrier)
   constexpr size_t kMaxSmem = 144 * 1024;
+  const size_t table = nd == 1 ? table_bytes_of<1>() : table_bytes_of<2>();
   const size_t xalign = (xbytes + 15) / 16 * 16;
-  if (kLayerTableBytes + p->col_bytes + xalign + zbytes <= kMaxSmem) {
+  if (table + p->col_bytes + xalign + zbytes <= kMaxSmem) {
     p->z_off = (int)xalign;
-    p->smem = kLayerTableBytes + p->col_bytes + xalign + zbytes;
+    p->smem = table + p->col_bytes + xalign + zbytes;
   } else {
     p->z_off = 0;
-    p->smem = kLayerTableBytes + p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
+    p->smem = table + p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
   }
   return p->smem <= kMaxSmem;
 }
 
-template <int DT, int VT, int RT, int A, int NX>
-hipError_t launch5(FusedArgs f, const Plan& p, hipStream_t s) {
-  auto kern = fused_decode_kernel<DT, VT, RT, A, NX>;
+template <int ND>
+using ArgsFor = FusedArgs<units_of<ND>()>;
+
+template <int DT, int VT, int RT, int A, int NX, int ND>
+hipError_t launch5(ArgsFor<ND> f, const Plan& p, hipStream_t s) {
+  auto kern = fused_decode_kernel<DT, VT, RT, A, NX, ND>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.smem);
   if (err != hipSuccess) return err;
@@ -562,20 +627,21 @@ hipError_t launch5(FusedArgs f, const Plan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- one dictionary: every format, up to 4 layers, d_in up to 12288
 template <int DT, int VT, int RT, int A>
-hipError_t launch4(FusedArgs f, const Plan& p, hipStream_t s) {
-  if (p.NX == 3 * RT) return launch5<DT, VT, RT, A, 3 * RT>(f, p, s);
-  if (p.NX == 2 * RT) return launch5<DT, VT, RT, A, 2 * RT>(f, p, s);
-  return launch5<DT, VT, RT, A, RT>(f, p, s);
+hipError_t launch4(ArgsFor<1> f, const Plan& p, hipStream_t s) {
+  if (p.NX == 3 * RT) return launch5<DT, VT, RT, A, 3 * RT, 1>(f, p, s);
+  if (p.NX == 2 * RT) return launch5<DT, VT, RT, A, 2 * RT, 1>(f, p, s);
+  return launch5<DT, VT, RT, A, RT, 1>(f, p, s);
 }
 
 template <int DT, int VT, int RT>
-hipError_t launch3(FusedArgs f, const Plan& p, hipStream_t s) {
+hipError_t launch3(ArgsFor<1> f, const Plan& p, hipStream_t s) {
   return p.A == 1 ? launch4<DT, VT, RT, 1>(f, p, s) : launch4<DT, VT, RT, 2>(f, p, s);
 }
 
 template <int DT, int VT>
-hipError_t launch2(FusedArgs f, const Plan& p, hipStream_t s) {
+hipError_t launch2(ArgsFor<1> f, const Plan& p, hipStream_t s) {
   switch (p.RT) {
     case 1: return launch3<DT, VT, 1>(f, p, s);
     case 2: return launch3<DT, VT, 2>(f, p, s);
@@ -584,7 +650,7 @@ hipError_t launch2(FusedArgs f, const Plan& p, hipStream_t s) {
 }
 
 template <int DT>
-hipError_t launch1(FusedArgs f, const Plan& p, int vdt, hipStream_t s) {
+hipError_t launch1(ArgsFor<1> f, const Plan& p, int vdt, hipStream_t s) {
   switch (vdt) {
     case DFS_NVFP4: return launch2<DT, DFS_NVFP4>(f, p, s);
     case DFS_FP8: return launch2<DT, DFS_FP8>(f, p, s);
@@ -593,12 +659,68 @@ hipError_t launch1(FusedArgs f, const Plan& p, int vdt, hipStream_t s) {
   }
 }
 
+// ---- 2 or 3 dictionaries: f16 or NVFP4 factors, 1 or 2 layers, NX = RT
+template <int DT, int VT, int ND, int RT>
+hipError_t mlaunch4(ArgsFor<ND> f, const Plan& p, hipStream_t s) {
+  switch (p.A) {
+    case 1: return launch5<DT, VT, RT, 1, RT, ND>(f, p, s);
+    case 2: return launch5<DT, VT, RT, 2, RT, ND>(f, p, s);
+    default: return launch5<DT, VT, RT, 3, RT, ND>(f, p, s);
+  }
+}
+
+template <int DT, int VT, int ND>
+hipError_t mlaunch3(ArgsFor<ND> f, const Plan& p, hipStream_t s) {
+  return p.RT == 1 ? mlaunch4<DT, VT, ND, 1>(f, p, s) : mlaunch4<DT, VT, ND, 2>(f, p, s);
+}
+
+template <int DT, int ND>
+hipError_t mlaunch2(ArgsFor<ND> f, const Plan& p, int vdt, hipStream_t s) {
+  return vdt == DFS_NVFP4 ? mlaunch3<DT, DFS_NVFP4, ND>(f, p, s) : mlaunch3<DT, DFS_F16, ND>(f, p, s);
+}
+
+template <int ND>
+ArgsFor<ND> make_args(const XdLaunch& xd, const ZcLaunch& zc, float* zws, uint32_t* ctrl) {
+  ArgsFor<ND> f = {};
+  f.D = xd.ddt == DFS_NVFP4 ? (const void*)xd.dcodes : xd.D;
+  f.dscales = xd.dscales;
+  f.ldd = xd.ldd;
+  f.d_in = xd.d_in;
+  f.k = xd.k;
+  for (int l = 0; l < xd.n_layers; ++l) f.X[l] = xd.X[l];
+  for (int u = 0; u < zc.n_layers; ++u) {
+    f.colptr[u] = zc.colptr[u];
+    f.rowidx[u] = zc.rowidx[u];
+    f.vals[u] = zc.vals[u];
+    f.vscales[u] = zc.vscales[u];
+    f.vts[u] = zc.vts[u];
+    f.Y[u] = zc.Y[u];
+    f.nnz[u] = zc.nnz[u];
+  }
+  f.dts = xd.dts;
+  f.zz = reinterpret_cast<uint64_t*>(zws);
+  f.ctrl = ctrl;
+  f.n_layers = xd.n_layers;
+  f.d_out = zc.d_out;
+  f.ydt = zc.ydt;
+  f.spin_limit = 1u << 22;
+  f.col_bytes = 0;
+  f.n_dicts = ND;
+  for (int d = 1; d < ND; ++d) {
+    f.Dx[d - 1] = xd.ddt == DFS_NVFP4 ? (const void*)xd.more[d - 1].dcodes : xd.more[d - 1].D;
+    f.dscalesx[d - 1] = xd.more[d - 1].dscales;
+    f.dtsx[d - 1] = xd.more[d - 1].dts;
+  }
+  return f;
+}
+
 }  // namespace
 
 bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc) {
   if (xd.T != 1 || zc.T != 1) return false;
   if (zc.block_rows != 0) return false;  // block-structured C: two-launch path
-  if (zc.n_layers < 1 || zc.n_layers > kFusedMaxLayers) return false;
+  if (xd.n_layers < 1 || xd.n_layers > kFusedMaxLayers) return false;
+  if (zc.n_layers < 1 || zc.n_layers > kFusedMaxUnits) return false;
   if (xd.xdt != DFS_F16) return false;
   if (xd.ddt != DFS_F16 && xd.ddt != DFS_NVFP4) return false;
   if (zc.vdt != DFS_F16 && zc.vdt != DFS_NVFP4 && zc.vdt != DFS_FP8 && zc.vdt != DFS_INT8)
@@ -612,32 +734,21 @@ hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, float* zw
                                uint32_t* ctrl, hipStream_t s) {
   Plan p;
   if (!plan(xd, zc, &p)) return hipErrorInvalidValue;
-  FusedArgs f = {};
-  f.D = xd.ddt == DFS_NVFP4 ? (const void*)xd.dcodes : xd.D;
-  f.dscales = xd.dscales;
-  f.ldd = xd.ldd;
-  f.d_in = xd.d_in;
-  f.k = xd.k;
-  for (int l = 0; l < zc.n_layers; ++l) {
-    f.X[l] = xd.X[l];
-    f.colptr[l] = zc.colptr[l];
-    f.rowidx[l] = zc.rowidx[l];
-    f.vals[l] = zc.vals[l];
-    f.vscales[l] = zc.vscales[l];
-    f.vts[l] = zc.vts[l];
-    f.Y[l] = zc.Y[l];
-    f.nnz[l] = zc.nnz[l];
+  const bool nv = xd.ddt == DFS_NVFP4;
+  switch (p.ND) {
+    case 1: {
+      const ArgsFor<1> f = make_args<1>(xd, zc, zws, ctrl);
+      return nv ? launch1<DFS_NVFP4>(f, p, zc.vdt, s) : launch1<DFS_F16>(f, p, zc.vdt, s);
+    }
+    case 2: {
+      const ArgsFor<2> f = make_args<2>(xd, zc, zws, ctrl);
+      return nv ? mlaunch2<DFS_NVFP4, 2>(f, p, zc.vdt, s) : mlaunch2<DFS_F16, 2>(f, p, zc.vdt, s);
+    }
+    default: {
+      const ArgsFor<3> f = make_args<3>(xd, zc, zws, ctrl);
+      return nv ? mlaunch2<DFS_NVFP4, 3>(f, p, zc.vdt, s) : mlaunch2<DFS_F16, 3>(f, p, zc.vdt, s);
+    }
   }
-  f.dts = xd.dts;
-  f.zz = reinterpret_cast<uint64_t*>(zws);
-  f.ctrl = ctrl;
-  f.n_layers = zc.n_layers;
-  f.d_out = zc.d_out;
-  f.ydt = zc.ydt;
-  f.spin_limit = 1u << 22;
-  f.col_bytes = 0;
-  return xd.ddt == DFS_NVFP4 ? launch1<DFS_NVFP4>(f, p, zc.vdt, s)
-                             : launch1<DFS_F16>(f, p, zc.vdt, s);
 }
 
 }  // namespace dfs

@@ -258,6 +258,32 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
                               int64_t ldx, const dfs_dict* D, const dfs_csc* C, void* const* Y,
                               int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
 
+/* Several layer groups that read the same activations, one dictionary each
+ * (as the q, k and v projections of the same layers do; each group is the
+ * factored projection of Eq. (1) with its own D_g, Figure 2):
+ * for d in [0, n_dicts) and l in [0, n_layers):
+ *   Y[d * n_layers + l] = (X[l] D[d]) C[d * n_layers + l].
+ * D: host array of n_dicts descriptors sharing d_in, k, dtype and ldd;
+ * C, Y: host arrays of n_dicts * n_layers descriptors / device pointers,
+ * dictionary-major, sharing d_out and dtype; X: n_layers device pointers
+ * shared by every dictionary.  1 <= n_dicts <= 8; each group obeys the
+ * limits of dict_group_forward, and every argument is checked before
+ * anything is launched.  At decode (T = 1, 2 or 3 dictionaries, at most 2
+ * layers, f16 X, f16 or NVFP4 D and C, d_in <= 4096 for f16 D) the whole
+ * set runs as one launch: one grid computes Z for the atoms of every
+ * dictionary and applies every C, so the groups share one launch and one
+ * latency chain.  Otherwise, or with DFS_DECODE_PATH=two, the groups run
+ * in turn as dict_group_forward calls on the same workspace.  Results equal
+ * those of dict_group_forward on each group.  The workspace (size from
+ * dict_multi_workspace_size) starts with the 4096-byte control block of
+ * dict_group_forward, zero before first use. */
+dfs_status dict_multi_workspace_size(int32_t n_dicts, int32_t n_layers, int32_t T,
+                                     const dfs_dict* D, const dfs_csc* C, size_t* bytes);
+dfs_status dict_multi_forward(int32_t n_dicts, int32_t n_layers, const void* const* X,
+                              int32_t xdt, int32_t T, int64_t ldx, const dfs_dict* D,
+                              const dfs_csc* C, void* const* Y, int32_t ydt, int64_t ldy,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* The first half of Eq. (1) alone: Z = X D_g for every layer of a group.
  * Z is (n_layers*T) x k row-major (row l*T + t), dtype F32 or F16, 16-byte
  * aligned.  Dense-product choice: VALU dot products for n_layers*T <= 16 rows,

@@ -285,3 +285,38 @@ def test_probe_validation():
     assert L.dfs_probe_mfma(4, 0, P, None) == INVALID
     assert L.dfs_probe_mfma(4, 1, None, None) == INVALID
     assert L.dfs_probe_mfma((1 << 20) + 1, 1, P, None) == RANGE
+
+
+def _multi(nd=2, n=1, T=1, Ds=None, Cs=None, ws=P, ws_bytes=1 << 30, X=P, Y=P):
+    Ds = Ds or [_dict() for _ in range(nd)]
+    Cs = Cs or [_csc() for _ in range(max(nd, len(Ds)) * n)]
+    xp = (C.c_void_p * n)(*([X] * n))
+    yp = (C.c_void_p * len(Cs))(*([Y] * len(Cs)))
+    ds = (B.Dict * len(Ds))(*Ds)
+    cs = (B.Csc * len(Cs))(*Cs)
+    return B.lib().dict_multi_forward(nd, n, xp, B.DFS_F16, T, 256, ds, cs, yp, B.DFS_F16, 64,
+                                      ws, ws_bytes, None)
+
+
+def test_multi_forward_validation():
+    # rejected before any launch (no GPU needed)
+    assert _multi(T=0) == OK
+    assert _multi(nd=0, Ds=[_dict()]) == INVALID
+    assert _multi(nd=9, Ds=[_dict()] * 9) == RANGE
+    assert _multi(Ds=[_dict(), _dict(k=64)], Cs=[_csc(), _csc(k=64)]) == INVALID  # k differs
+    assert _multi(Ds=[_dict(), _dict(dtype=B.DFS_F32)]) == INVALID               # dtype differs
+    assert _multi(Cs=[_csc(), _csc(d_out=65)]) == INVALID                        # d_out differs
+    assert _multi(Ds=[_dict(), _dict(data=P + 4)]) == ALIGN                      # per-group checks
+    assert _multi(Cs=[_csc(), _csc(k=64)]) == INVALID
+    assert _multi(X=0) == INVALID
+    assert _multi(ws=0) == WORKSPACE
+    assert _multi(ws_bytes=16) == WORKSPACE
+    n = C.c_size_t(0)
+    d, c = _dict(), _csc()
+    assert L_size(3, 2, 1, d, c, n) == OK and n.value >= 4096 + 3 * 2 * 128 * 8
+    assert L_size(0, 2, 1, d, c, n) == INVALID
+    assert L_size(9, 2, 1, d, c, n) == RANGE
+
+
+def L_size(nd, n, T, d, c, out):
+    return B.lib().dict_multi_workspace_size(nd, n, T, C.byref(d), C.byref(c), C.byref(out))
