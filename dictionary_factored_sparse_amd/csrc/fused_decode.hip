@@ -329,8 +329,18 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
     for (int i = 0; i < A; ++i) {
       const int atom = atom_of(i);
       const int dd = dict_of(i);
-      const void* Dd = dd == 0 ? f.D : f.Dx[dd == 1 ? 0 : 1];
-      const uint8_t* Sd = dd == 0 ? f.dscales : f.dscalesx[dd == 1 ? 0 : 1];
+      // constant indices only: a computed index into the argument arrays
+      // would make the compiler copy them to private memory
+      const void* Dd = f.D;
+      const uint8_t* Sd = f.dscales;
+      if constexpr (ND > 1) {
+        Dd = dd == 1 ? f.Dx[0] : Dd;
+        Sd = dd == 1 ? f.dscalesx[0] : Sd;
+      }
+      if constexpr (ND > 2) {
+        Dd = dd == 2 ? f.Dx[1] : Dd;
+        Sd = dd == 2 ? f.dscalesx[1] : Sd;
+      }
 #pragma unroll
       for (int c = 0; c < SEGC; ++c) {
         const int e0 = min(seg + (c * kWave + lane) * CE, d_in - CE);
@@ -379,11 +389,10 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
     }
   }
   float dts[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    dts[d] = 1.0f;
-    if constexpr (DT == DFS_NVFP4) dts[d] = *gptr(d == 0 ? f.dts : f.dtsx[d > 0 ? d - 1 : 0]);
-  }
+  dts[0] = 1.0f;
+  if constexpr (DT == DFS_NVFP4) dts[0] = *gptr(f.dts);
+  if constexpr (ND > 1) dts[1] = DT == DFS_NVFP4 ? *gptr(f.dtsx[0]) : 1.0f;
+  if constexpr (ND > 2) dts[2] = DT == DFS_NVFP4 ? *gptr(f.dtsx[1]) : 1.0f;
   const uint32_t epoch = epoch_old + 1u;
 #pragma unroll
   for (int i = 0; i < A; ++i) {
