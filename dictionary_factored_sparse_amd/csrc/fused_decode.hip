@@ -206,6 +206,12 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   constexpr bool Q8 = kIsCode8<VT>;
   constexpr int CE = Cf::CE, SEGC = Cf::SEGC, SEG = Cf::SEG;
   constexpr int NU = units_of<ND>(), kTable = table_bytes_of<ND>();
+  // Rounds of columns in flight before Z is received, and chunks per lane
+  // per batch.  Several dictionaries give a workgroup more columns (q, k, v
+  // over two layers: three rounds), so all three go out ahead, with batches
+  // of 5 chunks (640 entries per column) to fit the registers.
+  constexpr int NB = ND > 1 ? 3 : 2;
+  constexpr int KU = ND > 1 ? 5 : kU;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   LayerRow* lt = reinterpret_cast<LayerRow*>(smem);            // [NU]
   CE_t* cse = reinterpret_cast<CE_t*>(smem + kTable);          // [ncols]
@@ -275,11 +281,11 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   const int ncols = c1 - c0;  // <= kFT (checked on the host)
   const int rounds = (ncols + kSlots - 1) / kSlots;
   const uint32_t epoch_old = ld_agent(f.ctrl + kCtrlEpochs + blockIdx.x);
-  // this lane's columns in rounds 0 and 1 (16 lanes per column)
+  // this lane's columns in the first NB rounds (16 lanes per column)
   const int slot = wave * 4 + (lane >> 4);
-  int rs_raw[2], re_raw[2], rl[2];
+  int rs_raw[NB], re_raw[NB], rl[NB];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < NB; ++r) {
     const int ci = r * kSlots + slot < ncols ? r * kSlots + slot : 0;
     const int l = (c0 + ci) / d_out, j = c0 + ci - l * d_out;
     const int32_t* cpr = sreg_ptr(f.colptr[0]);
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   // used them), so a barrier here is enough before Z is written.
   if (f.z_off == 0) asm volatile("s_barrier" ::: "memory");
 
-  // ---- 7. the column ranges into LDS; rounds 0 and 1 of C in flight (their
+  // ---- 7. the column ranges into LDS; the first NB rounds of C in flight (their
   // bounds are older than D, so nothing here waits)
   if (tid < ncols) {
     const int nz = (int)lt[cl].nnz;
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
                          const void* vals, const uint8_t* vsc) {
     const int p0 = (s0 & ~7) + g * 8;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
+    for (int u = 0; u < KU; ++u) {
       const int p = p0 + 128 * u;
       if (p < e0) {
         ic[u].load(rowidx, p);
@@ -442,10 +448,10 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
       }
     }
   };
-  IdxChunk ia[kU], ib[kU];
-  ValChunk<VT> va[kU], vb[kU];
+  IdxChunk ia[KU], ib[KU], ie[NB > 2 ? KU : 1];
+  ValChunk<VT> va[KU], vb[KU], ve[NB > 2 ? KU : 1];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < NB; ++r) {
     const int l = rl[r];
     const uint16_t* rowidx = sreg_ptr(f.rowidx[0]);
     const void* vals = sreg_ptr(f.vals[0]);
@@ -464,8 +470,10 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
     const int e0 = live ? (int)min<int64_t>(max(re_raw[r], s0), nnz) : 0;
     if (r == 0)
       load_chunks(ia, va, s0, e0, rowidx, vals, vsc);
-    else if (rounds > 1)
+    else if (r == 1 && rounds > 1)
       load_chunks(ib, vb, s0, e0, rowidx, vals, vsc);
+    else if (r == 2 && rounds > 2)
+      load_chunks(ie, ve, s0, e0, rowidx, vals, vsc);
   }
   auto load_round = [&](IdxChunk* ic, ValChunk<VT>* vc, int r) {
     const int ci = r * kSlots + slot;
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   // every wave has published and received: advance this workgroup's epoch
   if (tid == 0) st_agent(f.ctrl + kCtrlEpochs + blockIdx.x, epoch);
 
-  // ---- 9. the columns, two rounds in flight
+  // ---- 9. the columns, NB rounds in flight
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int r) {
     const int ci = r * kSlots + slot;
     int s = 0, e = 0, l = 0;
@@ -502,24 +510,24 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
     float sum = 0.0f;
     int p0 = (s & ~7) + g * 8;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) sum = gather_chunk<VT>(zl, ic[u], vc[u], p0 + 128 * u, s, e, sum);
+    for (int u = 0; u < KU; ++u) sum = gather_chunk<VT>(zl, ic[u], vc[u], p0 + 128 * u, s, e, sum);
     // columns longer than one batch continue with plain loads
-    p0 += 128 * kU;
+    p0 += 128 * KU;
     if (p0 < e) {
       const LayerRow& L = lt[l];
       while (p0 < e) {
-        IdxChunk tc[kU];
-        ValChunk<VT> tv[kU];
+        IdxChunk tc[KU];
+        ValChunk<VT> tv[KU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
+        for (int u = 0; u < KU; ++u)
           if (p0 + 128 * u < e) {
             tc[u].load(L.rowidx, p0 + 128 * u);
             tv[u].load(L.vals, L.vsc, p0 + 128 * u);
           }
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
+        for (int u = 0; u < KU; ++u)
           sum = gather_chunk<VT>(zl, tc[u], tv[u], p0 + 128 * u, s, e, sum);
-        p0 += 128 * kU;
+        p0 += 128 * KU;
       }
     }
     sum = row16_sum(sum);
@@ -533,12 +541,27 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
         gptr_w((float*)y)[j] = sum * ts;
     }
   };
-  for (int r = 0; r < rounds; r += 2) {
-    consume(ia, va, r);
-    if (r + 2 < rounds) load_round(ia, va, r + 2);
-    if (r + 1 < rounds) {
-      consume(ib, vb, r + 1);
-      if (r + 3 < rounds) load_round(ib, vb, r + 3);
+  if constexpr (NB == 2) {
+    for (int r = 0; r < rounds; r += 2) {
+      consume(ia, va, r);
+      if (r + 2 < rounds) load_round(ia, va, r + 2);
+      if (r + 1 < rounds) {
+        consume(ib, vb, r + 1);
+        if (r + 3 < rounds) load_round(ib, vb, r + 3);
+      }
+    }
+  } else {
+    for (int r = 0; r < rounds; r += 3) {
+      consume(ia, va, r);
+      if (r + 3 < rounds) load_round(ia, va, r + 3);
+      if (r + 1 < rounds) {
+        consume(ib, vb, r + 1);
+        if (r + 4 < rounds) load_round(ib, vb, r + 4);
+      }
+      if (r + 2 < rounds) {
+        consume(ie, ve, r + 2);
+        if (r + 5 < rounds) load_round(ie, ve, r + 5);
+      }
     }
   }
 }
