@@ -408,14 +408,15 @@ def main():
             del gx
         # q, k and v (and gate and up) read the same activations: each set as
         # one multi-dictionary launch, o and down alone
-        def time_multi(gxs):
+        def time_multi(gxs, nvfp4=True):
             nd = len(gxs)
-            Ds = [B.to_device_dict(g.D, dev, nvfp4=True) for g in gxs]
-            Cs = [B.to_device_csc(c, dev, fmt="nvfp4") for g in gxs for c in g.Cs]
+            wdt = "nvfp4" if nvfp4 else "f16"
+            Ds = [B.to_device_dict(g.D, dev, nvfp4=nvfp4) for g in gxs]
+            Cs = [B.to_device_csc(c, dev, fmt="nvfp4" if nvfp4 else None) for g in gxs for c in g.Cs]
             n = len(gxs[0].Xs)
             nb = sum(L.group_bytes(d_in=g.d_in, d_out=g.d_out, k=g.k, T=1,
-                                   nnzs=[c.nnz for c in Cs[d * n:(d + 1) * n]], wdtype="nvfp4",
-                                   cdtype="nvfp4", xdtype="f16", ydtype="f16")
+                                   nnzs=[c.nnz for c in Cs[d * n:(d + 1) * n]], wdtype=wdt,
+                                   cdtype=wdt, xdtype="f16", ydtype="f16")
                      for d, g in enumerate(gxs)) - (nd - 1) * n * gxs[0].d_in * 2  # X read once
             nrep = max(2, math.ceil(1.2e9 / nb))
             rp = [(Ds, Cs)] + [([clone_dict(D) for D in Ds], [clone_csc(c) for c in Cs])
@@ -448,6 +449,17 @@ def main():
             "note": "q, k, v of a layer group as one dict_multi_forward launch and gate, up as "
                     "one (they read the same activations), o and down alone: 64 launches per "
                     "token instead of 112"}
+        # the q_proj group's shape in f16 at density 0.30 for q, k and v
+        # together: three groups' bytes behind one latency chain
+        qkv16_us, qkv16_b = time_multi([synth.make_group("qproj", ptype=p) for p in ("q", "k", "v")],
+                                       nvfp4=False)
+        extras["qkv_f16_qproj_shape_one_launch"] = {
+            "us": round(qkv16_us, 2), "MB": round(qkv16_b / 1e6, 2),
+            "GB/s": round(qkv16_b / qkv16_us / 1e3, 1),
+            "frac_of_8TBs": round(qkv16_b / qkv16_us / 1e3 / HBM_PEAK_GBS, 4),
+            "note": "q, k, v groups of the headline's shape (2 layers, 4096 -> 4096, k = 2048, f16, "
+                    "C density 0.30) sharing their activations, one dict_multi_forward launch"}
+        _log(f"q,k,v f16 one launch: {extras['qkv_f16_qproj_shape_one_launch']}")
         stack["per_token_us"] = round(per_tok_us, 1)
         stack["per_token_GB"] = round(per_tok_b / 1e9, 3)
         stack["per_token_GB/s"] = round(per_tok_b / per_tok_us / 1e3, 1)
