@@ -644,7 +644,10 @@ dfs_status dict_multi_forward(int32_t n_dicts, int32_t n_layers, const void* con
   if (!ws || ws_bytes < need) return DFS_E_WORKSPACE;
   if (!aligned16(ws)) return DFS_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (n_dicts > 1 && n_dicts <= kFusedMaxDicts && fused_allowed()) {
+  // the launch structs hold at most kFusedMaxLayers X rows and
+  // kFusedMaxUnits (dictionary, layer) units: checked before they are filled
+  if (n_dicts > 1 && n_dicts <= kFusedMaxDicts && n_layers <= kFusedMaxLayers &&
+      n_dicts * n_layers <= kFusedMaxUnits && fused_allowed()) {
     uint32_t* ctrl = (uint32_t*)ws;
     void* Z = (char*)ws + kCtrlBytes;
     XdLaunch xa = make_xd(n_layers, X, xdt, T, ldx, &D[0], Z, DFS_F32);
@@ -652,7 +655,7 @@ dfs_status dict_multi_forward(int32_t n_dicts, int32_t n_layers, const void* con
     for (int d = 1; d < n_dicts; ++d)
       xa.more[d - 1] = {D[d].data, D[d].nv.codes, D[d].nv.scales, D[d].nv.tensor_scale};
     ZcLaunch za = make_zc(n_dicts * n_layers, Z, DFS_F32, T, C, Y, ydt, ldy);
-    if ((int64_t)n_dicts * n_layers <= kMaxLayers && fused_decode_supported(xa, za)) {
+    if (fused_decode_supported(xa, za)) {
       DFS_HIP(launch_fused_decode(xa, za, (float*)Z, ctrl, s));
       return DFS_OK;
     }

@@ -164,6 +164,7 @@ constexpr int kGemvMaxRows = 16;
 constexpr int kFusedMaxLayers = 4;
 constexpr int kFusedMaxDicts = 3;
 constexpr int kFusedMaxUnits = 8;
+static_assert(kFusedMaxUnits <= kMaxLayers, "units fit the launch structs");
 constexpr int kCtrlBlockBytes = 4096;   // forward workspace control block
 constexpr int kMaxFusedGroups = 768;  // per-workgroup epoch words from byte 1024
 bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc);
