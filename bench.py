@@ -69,6 +69,17 @@ def _traffic_bytes():
     return int(round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +104,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the factored projection is measured on one "
-              "MI355X (see DESIGN.md for how it would shard); --gpus must be 1.", flush=True)
+              "MI355X, and no multi-GPU path is built; --gpus must be 1.", flush=True)
         sys.exit(2)
 
     import numpy as np
@@ -709,7 +720,8 @@ def main():
                "cores": cores, "kind": "oracle",
                "sample": f"{n_done} group forwards of the same q_proj decode group "
                          f"(float64 oracle, {t_cpu:.1f} s)",
-               "value_1_thread": round(step_bytes * n1 / t1s / 1e9, 3)}
+               "value_1_thread": round(step_bytes * n1 / t1s / 1e9, 3),
+               "cpu_model": _cpu_model()}
         _log(f"cpu oracle: {cpu}")
 
     d = kern[dom]

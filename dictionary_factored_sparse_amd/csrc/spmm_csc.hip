@@ -38,22 +38,23 @@ constexpr int kUnroll = 2;
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 // NT f16 tokens of one Z row, read from LDS in 16-byte pieces (8 bytes for
-// NT = 4); `row` points at the lane's first token of the row.
+// NT = 4).  The two pieces of a 16-token read come from `p0` and `p1`, which
+// point at the lane's first and second 8 tokens of the row, or the other way
+// round (see the piece order in the kernel); `p1` is unused for NT < 16.
 template <int NT>
 struct ZRow {
   h8 v[NT / 8];
-  __device__ __forceinline__ void read(const _Float16* row) {
-    const h8* p = reinterpret_cast<const h8*>(row);
-#pragma unroll
-    for (int j = 0; j < NT / 8; ++j) v[j] = p[j];
+  __device__ __forceinline__ void read(const _Float16* p0, const _Float16* p1) {
+    v[0] = *reinterpret_cast<const h8*>(p0);
+    if constexpr (NT == 16) v[1] = *reinterpret_cast<const h8*>(p1);
   }
   __device__ __forceinline__ float get(int t) const { return (float)v[t / 8][t % 8]; }
 };
 template <>
 struct ZRow<4> {
   h4 v;
-  __device__ __forceinline__ void read(const _Float16* row) {
-    v = *reinterpret_cast<const h4*>(row);
+  __device__ __forceinline__ void read(const _Float16* p0, const _Float16*) {
+    v = *reinterpret_cast<const h4*>(p0);
   }
   __device__ __forceinline__ float get(int t) const { return (float)v[t]; }
 };
@@ -158,7 +159,15 @@ __global__ __launch_bounds__(spmm_threads<VT>()) void spmm_csc_kernel(ZcLaunch a
   float acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-  const _Float16* zl = zt + sub * NT;
+  // Piece order.  A 16-token read is two 16-byte pieces of a row; rows are
+  // gathered at random atoms, and a row's bank window depends only on the
+  // atom's low bits, so neighbouring columns reading the same piece of their
+  // rows collide in the LDS banks.  Odd columns read their second piece
+  // first: acc[t] then holds token t ^ 8 of the lane's 16, for the whole
+  // kernel, so each sum keeps its order and the result is unchanged.
+  const int swp = NT == 16 ? ((threadIdx.x / LPC) & 1) * 8 : 0;
+  const _Float16* zl0 = zt + sub * NT + swp;
+  const _Float16* zl1 = zt + sub * NT + (8 - swp);
   const uint32_t len = (uint32_t)(e - s);
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int pb) {
     // A batch that lies inside every active lane's column (all but the
@@ -172,7 +181,8 @@ __global__ __launch_bounds__(spmm_threads<VT>()) void spmm_csc_kernel(ZcLaunch a
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           ZRow<NT> z;
-          z.read(zl + ic[u].get(i) * TT);
+          const uint32_t ro = ic[u].get(i) * TT;
+          z.read(zl0 + ro, zl1 + ro);
           const float v = vu.get(i);
 #pragma unroll
           for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(z.get(t), v, acc[t]);
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(spmm_threads<VT>()) void spmm_csc_kernel(ZcLaunch a
         const uint32_t r = ok ? ic[u].get(i) : (uint32_t)k;
         const float v = ok ? vu.get(i) : 0.0f;
         ZRow<NT> z;
-        z.read(zl + r * TT);
+        z.read(zl0 + r * TT, zl1 + r * TT);
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(z.get(t), v, acc[t]);
       }
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(spmm_threads<VT>()) void spmm_csc_kernel(ZcLaunch a
     if constexpr (VT == DFS_NVFP4) ts = *a.vts[layer];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const int t = sub * NT + i;
+      const int t = sub * NT + (i ^ swp);
       if (t < rows) {
         const int64_t o = (int64_t)(t0 + t) * a.ldy + col;
         const float out = acc[i] * ts;

@@ -92,20 +92,23 @@ __device__ __forceinline__ void stage_zh(_Float16* zh, const void* Z, int64_t ro
 }
 
 // TT f16 tokens of one staged Z row (16-byte pieces; 8 bytes for TT = 4).
+// For TT = 16 the two pieces come from `p0` and `p1`: the row's first and
+// second 8 tokens, or the other way round (see the piece order in the
+// kernel); `p1` is unused for TT < 16.
 template <int TT>
 struct ZRowH {
   h8 v[TT / 8];
-  __device__ __forceinline__ void read(const _Float16* row) {
-#pragma unroll
-    for (int j = 0; j < TT / 8; ++j) v[j] = reinterpret_cast<const h8*>(row)[j];
+  __device__ __forceinline__ void read(const _Float16* p0, const _Float16* p1) {
+    v[0] = *reinterpret_cast<const h8*>(p0);
+    if constexpr (TT == 16) v[1] = *reinterpret_cast<const h8*>(p1);
   }
   __device__ __forceinline__ float get(int t) const { return (float)v[t / 8][t % 8]; }
 };
 template <>
 struct ZRowH<4> {
   h4 v;
-  __device__ __forceinline__ void read(const _Float16* row) {
-    v = *reinterpret_cast<const h4*>(row);
+  __device__ __forceinline__ void read(const _Float16* p0, const _Float16*) {
+    v = *reinterpret_cast<const h4*>(p0);
   }
   __device__ __forceinline__ float get(int t) const { return (float)v[t]; }
 };
@@ -193,6 +196,13 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
   const uint8_t* vsc = a.vscales[layer];
   float ts = 1.0f;
   if constexpr (VT == DFS_NVFP4) ts = *a.vts[layer];
+  // Piece order of the 16-token f16 rows.  The lanes of a row gather rows
+  // at random atoms, and a row's LDS bank window depends only on the atom's
+  // low bits, so lanes reading the same piece collide in the banks.  Odd
+  // lanes read the second piece first; their acc[t] then holds token t ^ 8
+  // until the halves are swapped back before the reduction, so every sum
+  // keeps its order.
+  const int swp = (ZH && TT == 16) ? (g & 1) * 8 : 0;
 
   struct Col {
     int col, s, e, first;
@@ -255,7 +265,8 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
             if constexpr (ZH) {
               // masked entries read the zero row with a zero value
               ZRowH<TT> z;
-              z.read(zh + (ok ? ic[u].get(i) : (uint32_t)a.k) * TT);
+              const _Float16* zr = zh + (ok ? ic[u].get(i) : (uint32_t)a.k) * TT;
+              z.read(zr + swp, zr + (8 - swp));
 #pragma unroll
               for (int t = 0; t < TT; ++t) acc[t] = __builtin_fmaf(z.get(t), v, acc[t]);
             } else {
@@ -283,6 +294,14 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
       if (cg + 1 < gend) {
         n = col_of(cg + 1);
         load_batch(n, n.first);
+      }
+      if constexpr (ZH && TT == 16) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float lo = acc[t], hi = acc[t + 8];
+          acc[t] = swp ? hi : lo;
+          acc[t + 8] = swp ? lo : hi;
+        }
       }
       float out = 0.0f;
 #pragma unroll

@@ -48,7 +48,8 @@ typedef enum {
   DFS_OK = 0,
   DFS_E_INVALID = 1,     /* null pointer, bad dimension or leading dim, NaN/Inf input */
   DFS_E_UNSUPPORTED = 2, /* dtype combination or layout the library does not run */
-  DFS_E_RANGE = 3,       /* k > 65536, nnz >= 2^31, capacity too small, > 16 layers */
+  DFS_E_RANGE = 3,       /* k > 65536 (forward: k > 16384), nnz >= 2^31, capacity too small,
+                            > 16 layers */
   DFS_E_ALIGN = 4,       /* a base pointer or leading dimension is misaligned */
   DFS_E_WORKSPACE = 5,   /* workspace missing or too small */
   DFS_E_HIP = 6          /* the HIP runtime returned an error */
@@ -237,7 +238,9 @@ dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, c
 /* One factored projection, Eq. (1): Z = X D_g, Y = Z C_l.
  *   X: T x d_in row-major, leading dimension ldx, dtype F16 or F32.
  *   Y: T x d_out row-major, leading dimension ldy, dtype F16 or F32.
- *   T = 0 is a no-op.  The intermediate Z (T x k) lives in the workspace. */
+ *   T = 0 is a no-op.  The intermediate Z (T x k) lives in the workspace.
+ *   k <= 16384 (the product kernels stage Z tiles of every atom in LDS);
+ *   a larger k gives DFS_E_RANGE.  The same limit holds for every forward call. */
 dfs_status dict_proj_forward(const void* X, int32_t xdt, int32_t T, int64_t ldx, const dfs_dict* D,
                              const dfs_csc* C, void* Y, int32_t ydt, int64_t ldy, void* ws,
                              size_t ws_bytes, void* stream);

@@ -70,6 +70,7 @@ def test_group_forward_validation():
     assert _group(T=0) == OK                         # empty batch: nothing to do
     assert _group(D=_dict(d_in=0)) == INVALID
     assert _group(D=_dict(k=20000)) == RANGE        # Z must fit in LDS
+    assert _group(D=_dict(k=16385)) == RANGE        # one past the largest forward k
     assert _group(D=_dict(data=None)) == INVALID
     assert _group(D=_dict(data=P + 4)) == ALIGN
     assert _group(D=_dict(ldd=100)) == INVALID      # ldd < d_in

@@ -200,6 +200,32 @@ def test_sixteen_layer_group():
         assert_close(Ys[l], ref, f"16-layer group layer {l}")
 
 
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_largest_forward_k(T):
+    """k = 16384, the most atoms a forward call accepts.  Entries at atom
+    16383 and atom 0 in every tenth column reach both ends of the staged Z
+    tile.  T = 1: decode; T = 5: VALU dot products and SpMV (10 stacked rows);
+    T = 40: MFMA GEMM and SpMM (80 stacked rows)."""
+    say(f"case: k=16384, d_in=128, d_out=200, 2 layers, T={T}")
+    rng = np.random.default_rng(16384 + T)
+    d_in, d_out, k, n = 128, 200, 16384, 2
+    Dn = synth.dictionary(rng, d_in, k, "gauss", np.float16)
+    Cs = []
+    for _ in range(n):
+        Cd = synth.coefficients(rng, k, d_out, 0.01, np.float16)
+        Cd[k - 1, ::10] = np.float16(0.5)
+        Cd[0, 5::10] = np.float16(-0.5)
+        Cs.append(Cd)
+    Xs = [rng.standard_normal((T, d_in)).astype(np.float16) for _ in range(n)]
+    D = B.DeviceDict(d_in, k, data=torch.from_numpy(Dn).to(DEV))
+    Ys = B.dict_group_forward([torch.from_numpy(X).to(DEV) for X in Xs], D,
+                              [B.to_device_csc(Cd, DEV) for Cd in Cs])
+    torch.cuda.synchronize()
+    refs = O.group_forward(Xs, Dn, d_in, [O.pack_csc(Cd) for Cd in Cs])
+    for l in range(n):
+        assert_close(Ys[l], refs[l], f"k=16384 T={T} layer {l}")
+
+
 def test_zero_tokens_is_a_no_op():
     say("case: T=0")
     g = synth.make_group("tiny", T=1)
