@@ -223,9 +223,16 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
     c.lastc = last_chunk(c.e);
     return c;
   };
-  IdxChunk ic[U];
-  ValChunk<VT> vc[U];
-  auto load_batch = [&](const Col& c, int p0) {
+  // Batches of coefficient chunks in registers.  The 16-token f16 tile
+  // (one chunk per batch) keeps two batches in flight: the next batch is
+  // loaded (clamped to the column's last chunk, masked on use) while the
+  // current one is consumed, so a column's batches do not each wait a full
+  // memory round trip.  The other forms hold several chunks per batch and
+  // one batch.
+  constexpr bool kTwo = ZH && TT >= 16;
+  IdxChunk ia[U], ib[kTwo ? U : 1];
+  ValChunk<VT> va[U], vb[kTwo ? U : 1];
+  auto load_batch = [&](IdxChunk* ic, ValChunk<VT>* vc, const Col& c, int p0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t p = min<int64_t>(p0 + 128 * u, c.lastc);
@@ -236,7 +243,7 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
 
   for (int t0 = 0; t0 < a.T; t0 += TT) {
     Col c = col_of(gb);
-    load_batch(c, c.first);  // does not depend on Z: in flight while Z is staged
+    load_batch(ia, va, c, c.first);  // does not depend on Z: in flight while Z is staged
     if (t0 > 0) __syncthreads();
     const int rows = a.T - t0 < TT ? a.T - t0 : TT;
     if constexpr (ZH)
@@ -250,18 +257,18 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
 #pragma unroll
       for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
       const uint32_t len = (uint32_t)(c.e - c.s);
-      int p0 = c.first;
-      while (p0 < c.e) {
+      auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vcb, int p0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          vc[u].touch();
+          ValChunk<VT> vu = vcb[u];
+          vu.touch();
           const int base = p0 + 128 * u - c.s;
           // entries outside [s, e) are masked without a branch, so the LDS
           // gathers of a chunk issue back to back
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const bool ok = (uint32_t)(base + i) < len;
-            const float v = ok ? vc[u].get(i) : 0.0f;
+            const float v = ok ? vu.get(i) : 0.0f;
             if constexpr (ZH) {
               // masked entries read the zero row with a zero value
               ZRowH<TT> z;
@@ -286,14 +293,35 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
             }
           }
         }
-        p0 += 128 * U;
-        if (p0 < c.e) load_batch(c, p0);
+      };
+      int p0 = c.first;
+      if constexpr (kTwo) {
+        // the next batch is loaded before this one is consumed and moved
+        // into place after it (a loop-exit branch between the two halves of
+        // an unrolled pair would let the compiler sink the load past the
+        // first consume)
+        while (p0 < c.e) {
+          load_batch(ib, vb, c, p0 + 128 * U);
+          consume(ia, va, p0);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            ia[u] = ib[u];
+            va[u] = vb[u];
+          }
+          p0 += 128 * U;
+        }
+      } else {
+        while (p0 < c.e) {
+          consume(ia, va, p0);
+          p0 += 128 * U;
+          if (p0 < c.e) load_batch(ia, va, c, p0);
+        }
       }
       // the next group's first batch goes out before this group's reduction
       Col n = c;
       if (cg + 1 < gend) {
         n = col_of(cg + 1);
-        load_batch(n, n.first);
+        load_batch(ia, va, n, n.first);
       }
       if constexpr (ZH && TT == 16) {
 #pragma unroll

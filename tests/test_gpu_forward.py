@@ -200,19 +200,15 @@ def test_sixteen_layer_group():
         assert_close(Ys[l], ref, f"16-layer group layer {l}")
 
 
-@pytest.mark.parametrize("T", [1, 5, 40])
-def test_largest_forward_k(T):
-    """k = 16384, the most atoms a forward call accepts.  Entries at atom
-    16383 and atom 0 in every tenth column reach both ends of the staged Z
-    tile.  T = 1: decode; T = 5: VALU dot products and SpMV (10 stacked rows);
-    T = 40: MFMA GEMM and SpMM (80 stacked rows)."""
-    say(f"case: k=16384, d_in=128, d_out=200, 2 layers, T={T}")
-    rng = np.random.default_rng(16384 + T)
-    d_in, d_out, k, n = 128, 200, 16384, 2
+def _wide_dictionary_group(seed, d_in, d_out, k, T, n, density):
+    """A group with more atoms than input features (Gaussian atoms), f16
+    factors and activations.  Entries at atom k - 1 and atom 0 in every
+    tenth column reach both ends of the staged Z tile."""
+    rng = np.random.default_rng(seed)
     Dn = synth.dictionary(rng, d_in, k, "gauss", np.float16)
     Cs = []
     for _ in range(n):
-        Cd = synth.coefficients(rng, k, d_out, 0.01, np.float16)
+        Cd = synth.coefficients(rng, k, d_out, density, np.float16)
         Cd[k - 1, ::10] = np.float16(0.5)
         Cd[0, 5::10] = np.float16(-0.5)
         Cs.append(Cd)
@@ -223,7 +219,26 @@ def test_largest_forward_k(T):
     torch.cuda.synchronize()
     refs = O.group_forward(Xs, Dn, d_in, [O.pack_csc(Cd) for Cd in Cs])
     for l in range(n):
-        assert_close(Ys[l], refs[l], f"k=16384 T={T} layer {l}")
+        assert_close(Ys[l], refs[l], f"k={k} T={T} layer {l}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_largest_forward_k(T):
+    """k = 16384, the most atoms a forward call accepts.  T = 1: decode;
+    T = 5: VALU dot products and SpMV (10 stacked rows); T = 40: MFMA GEMM
+    and SpMM (80 stacked rows, 4-token tiles)."""
+    say(f"case: k=16384, d_in=128, d_out=200, 2 layers, T={T}")
+    _wide_dictionary_group(16384 + T, 128, 200, 16384, T, 2, 0.01)
+
+
+@pytest.mark.parametrize("k", [3072, 4607, 4608])
+def test_prefill_token_tile_sizes(k):
+    """The SpMM's token tile follows k: 16 tokens with one lane per column
+    (odd and even columns read the two halves of a Z row in opposite order)
+    up to k = 4607, 8 tokens from k = 4608.  T = 40 leaves a ragged tile and
+    d_out = 301 an odd last column."""
+    say(f"case: prefill SpMM token tiles, k={k}, d_in=256, d_out=301, 2 x T=40")
+    _wide_dictionary_group(k, 256, 301, k, 40, 2, 0.05)
 
 
 def test_zero_tokens_is_a_no_op():
