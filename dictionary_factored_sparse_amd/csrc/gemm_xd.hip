@@ -313,38 +313,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_xd_kernel(XdLaunch a, int ks
 
   // Accumulator layout of a 32 x 32 block: lane l holds column l % 32 and
   // rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
-  if constexpr (ZT == DFS_F16) {
-    // f16 Z, whole rows of 16-byte pieces: the tile is staged in LDS (free
-    // once every wave has read the last K tile) and written out in 16-byte
-    // pieces, whole rows per wave, instead of 2-byte stores scattered over
-    // the tile's rows.  Rows are padded by 16 bytes so that the two row
-    // groups a wave writes at once fall into different banks.
-    const bool staged = ks == 1 && N % 8 == 0 && (((uintptr_t)a.Z) & 15) == 0;
-    if (staged) {
-      constexpr int RS = BN * 2 + 16;  // bytes per staged row
-      static_assert((size_t)BM * RS <= (size_t)kStages * kStageBytes, "tile fits the stages");
-      __syncthreads();
+  // The tile leaves through LDS when its rows are whole 16-byte pieces (f16
+  // Z, fp32 Z, or the fp32 partial of a K slice): the stages are free once
+  // every wave has read the last K tile, the waves write their accumulators
+  // there in the output's type, and the workgroup stores 16-byte pieces,
+  // whole rows per wave, instead of 2- or 4-byte stores scattered over the
+  // tile's rows.  Rows are padded by 16 bytes so that the two row groups a
+  // wave writes at once fall into different banks.
+  auto staged_store = [&](auto tag, void* base) {
+    using E = decltype(tag);
+    constexpr int kPer = 16 / (int)sizeof(E);
+    constexpr int RS = BN * (int)sizeof(E) + 16;  // bytes per staged row
+    static_assert((size_t)BM * RS <= (size_t)kStages * kStageBytes, "tile fits the stages");
+    __syncthreads();
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int c = wn + 32 * j + (lane & 31);
+      for (int j = 0; j < NJ; ++j) {
+        const int c = wn + 32 * j + (lane & 31);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            *reinterpret_cast<_Float16*>(smem + r * RS + c * 2) = (_Float16)acc[i][j][v];
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          *reinterpret_cast<E*>(smem + r * RS + c * (int)sizeof(E)) = (E)acc[i][j][v];
         }
-      __syncthreads();
-      constexpr int kPieces = BM * BN / 8, kRowPieces = BN / 8;
-#pragma unroll 4
-      for (int q = tid; q < kPieces; q += kThreads) {
-        const int r = q / kRowPieces, c = q - r * kRowPieces;
-        const int m = m0 + r, n = n0 + 8 * c;
-        if (m < M && n < N)
-          *reinterpret_cast<u4*>((_Float16*)a.Z + (int64_t)m * N + n) =
-              *reinterpret_cast<const u4*>(smem + r * RS + c * 16);
       }
+    __syncthreads();
+    constexpr int kRowPieces = BN / kPer, kPieces = BM * kRowPieces;
+#pragma unroll 4
+    for (int q = tid; q < kPieces; q += kThreads) {
+      const int r = q / kRowPieces, c = q - r * kRowPieces;
+      const int m = m0 + r, n = n0 + kPer * c;
+      if (m < M && n < N)
+        *reinterpret_cast<u4*>((E*)base + (int64_t)m * N + n) =
+            *reinterpret_cast<const u4*>(smem + r * RS + c * 16);
+    }
+  };
+  auto aligned = [](const void* p) { return (((uintptr_t)p) & 15) == 0; };
+  if (ks > 1) {
+    float* zp = a.zpart + (int64_t)split * M * N;
+    if (N % 4 == 0 && aligned(zp)) {
+      staged_store(0.0f, zp);
+      return;
+    }
+  } else if constexpr (ZT == DFS_F16) {
+    if (N % 8 == 0 && aligned(a.Z)) {
+      staged_store((_Float16)0.0f, a.Z);
+      return;
+    }
+  } else {
+    if (N % 4 == 0 && aligned(a.Z)) {
+      staged_store(0.0f, a.Z);
       return;
     }
   }
