@@ -592,6 +592,44 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_xd_wide_kernel(XdLaunch a)
     mma(fa1, fb1);
   }
 
+  // f16 Z with whole 16-byte pieces per row leaves through LDS, half a tile
+  // (one row of waves) per pass, as in gemm_xd_kernel: 2-byte stores
+  // scattered over the tile's rows would sit at the end of every workgroup.
+  if constexpr (ZT == DFS_F16) {
+    if (N % 8 == 0 && (((uintptr_t)a.Z) & 15) == 0) {
+      constexpr int HR = WBM / 2;       // rows per pass
+      constexpr int RS = WBN * 2 + 16;  // bytes per staged row, padded
+      static_assert((size_t)HR * RS <= WT::kSmemBytes, "half a tile fits the stages");
+      constexpr int kRowPieces = WBN / 8, kPieces = HR * kRowPieces;
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        __syncthreads();
+        if ((wave >> 1) == pass) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const int c = wn + 32 * j + (lane & 31);
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int r = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                *reinterpret_cast<_Float16*>(smem + r * RS + c * 2) = (_Float16)acc[i][j][v];
+              }
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int q = tid; q < kPieces; q += kThreads) {
+          const int r = q / kRowPieces, c = q - r * kRowPieces;
+          const int m = m0 + pass * HR + r, n = n0 + 8 * c;
+          if (m < M && n < N)
+            *reinterpret_cast<u4*>((_Float16*)a.Z + (int64_t)m * N + n) =
+                *reinterpret_cast<const u4*>(smem + r * RS + c * 16);
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
