@@ -268,6 +268,26 @@ def test_xd_and_zc_entry_points():
             assert_close(Ys[l], ref, f"zc layer {l} {zdt}")
 
 
+@pytest.mark.parametrize("d_in,k,T", [(512, 200, 150), (512, 202, 150), (1032, 264, 40),
+                                      (1032, 262, 40)])
+def test_mfma_output_tile_forms(d_in, k, T):
+    """Z = X D on the MFMA path in f32 and f16.  2 x 150 rows take the
+    256 x 128 tile (a ragged last row tile); 2 x 40 rows take 64 x 64 tiles
+    with K split in four, whose fp32 partials are summed by a second kernel.
+    Tiles whose rows are whole 16-byte pieces (k = 200, 264) leave through
+    LDS; k = 202 and 262 keep the element stores."""
+    say(f"case: MFMA Z tiles, d_in={d_in}, k={k}, 2 x T={T}, f32 and f16 Z")
+    g = synth.make_group("qproj", d_in=d_in, d_out=64, k=k, T=T, n_layers=2)
+    D, _, Xs = device_group(g)
+    eye = O.pack_csc(np.eye(g.k, dtype=np.float32))
+    zrefs = [O.forward(g.Xs[l], g.D, g.d_in, eye) for l in range(2)]
+    for zdt in (torch.float32, torch.float16):
+        Z = B.dict_xd_forward(Xs, D, zdtype=zdt)
+        torch.cuda.synchronize()
+        for l in range(2):
+            assert_close(Z[l * T:(l + 1) * T], zrefs[l], f"Z layer {l} {zdt}")
+
+
 def test_repeat_runs_are_bitwise_identical():
     say("case: determinism")
     for wl, T in (("qproj", 1), ("qproj", 64)):
