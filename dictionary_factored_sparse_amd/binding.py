@@ -47,7 +47,8 @@ class Dict(C.Structure):
 class Csc(C.Structure):
     _fields_ = [("k", C.c_int32), ("d_out", C.c_int32), ("nnz", C.c_int64), ("dtype", C.c_int32),
                 ("block_rows", C.c_int32), ("colptr", C.c_void_p), ("rowidx", C.c_void_p),
-                ("vals", C.c_void_p), ("nv", NV), ("col_scale", C.c_void_p)]
+                ("vals", C.c_void_p), ("nv", NV), ("col_scale", C.c_void_p),
+                ("capacity", C.c_int64)]
 
 
 class DfsError(RuntimeError):
@@ -194,17 +195,30 @@ class DeviceCSC:
     code_kind: str | None = None           # "fp8" or "int8"
     block_rows: int = 0                    # 8: colptr/nnz count blocks of 8 atoms
 
+    @property
+    def capacity(self) -> int:
+        """Entries (blocks, for block_rows = 8) that rowidx and the values
+        are allocated for: the smallest of the arrays' lengths."""
+        cap = self.rowidx.numel()
+        if self.nv is not None:
+            cap = min(cap, 2 * self.nv.codes.numel(), 16 * self.nv.scales.numel())
+        elif self.codes8 is not None:
+            cap = min(cap, self.codes8.numel())
+        else:
+            cap = min(cap, self.vals.numel() // (self.block_rows or 1))
+        return cap
+
     def desc(self) -> Csc:
         if self.nv is not None:
             return Csc(self.k, self.d_out, self.nnz, DFS_NVFP4, 0, self.colptr.data_ptr(),
-                       self.rowidx.data_ptr(), None, self.nv.nv(), None)
+                       self.rowidx.data_ptr(), None, self.nv.nv(), None, self.capacity)
         if self.codes8 is not None:
             return Csc(self.k, self.d_out, self.nnz, CODE8[self.code_kind], 0,
                        self.colptr.data_ptr(), self.rowidx.data_ptr(), self.codes8.data_ptr(),
-                       NV(), self.col_scale.data_ptr())
+                       NV(), self.col_scale.data_ptr(), self.capacity)
         return Csc(self.k, self.d_out, self.nnz, _dt(self.vals), self.block_rows,
                    self.colptr.data_ptr(), self.rowidx.data_ptr(), self.vals.data_ptr(), NV(),
-                   None)
+                   None, self.capacity)
 
     @property
     def fmt(self) -> str:
@@ -332,14 +346,16 @@ def dict_workspace_size(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC) -> 
 
 
 def workspace(n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC, device) -> torch.Tensor:
-    """Forward workspace.  Zeroed: its first 4096 bytes are the control block
-    the library requires to be zero before first use."""
+    """Forward workspace, zeroed: the library requires the whole workspace
+    to be zero before its first use (the calls leave the control block and
+    the tagged Z words zero again)."""
     return torch.zeros(dict_workspace_size(n_layers, T, D, Cs), dtype=torch.uint8, device=device)
 
 
 def workspace_error_word(ws: torch.Tensor) -> int:
-    """Word 32 of the control block: non-zero if a one-launch decode timed
-    out waiting for a Z word (results of that call are invalid)."""
+    """Word 32 of the control block: non-zero once a one-launch decode gave
+    up waiting for a published Z word and computed it itself (a diagnostic:
+    the results are still right)."""
     return int(ws[128:132].view(torch.int32).item())
 
 
@@ -367,8 +383,8 @@ def dict_group_forward(Xs, D: DeviceDict, Cs, Ys=None, ydtype=torch.float16, ws=
 
 def multi_workspace(n_dicts: int, n_layers: int, T: int, D: DeviceDict, Cs: DeviceCSC,
                     device) -> torch.Tensor:
-    """Workspace of dict_multi_forward, zeroed (its first 4096 bytes are the
-    control block, zero before first use)."""
+    """Workspace of dict_multi_forward, zeroed (the library requires the
+    whole workspace to be zero before its first use)."""
     n = C.c_size_t(0)
     d, c = D.desc(), Cs.desc()
     _check("dict_multi_workspace_size",

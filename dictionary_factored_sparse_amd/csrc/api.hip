@@ -76,6 +76,8 @@ dfs_status check_csc(const dfs_csc* C, int32_t k, int32_t d_out) {
   if (C->nnz > 0) {
     if (!C->rowidx) return DFS_E_INVALID;
     if (!aligned16(C->rowidx)) return DFS_E_ALIGN;
+    // the kernels read whole 8-entry chunks
+    if (C->capacity < dict_csc_capacity(C->nnz)) return DFS_E_RANGE;
   }
   if (C->block_rows != 0 && C->block_rows != 8) return DFS_E_UNSUPPORTED;
   if (C->block_rows == 8 && !is_act_dtype(C->dtype)) return DFS_E_UNSUPPORTED;
@@ -226,6 +228,28 @@ bool fused_allowed() {
 }
 
 constexpr size_t kCtrlBytes = kCtrlBlockBytes;  // control block at the start of the workspace
+
+// Layout of a forward workspace, one definition for the size query and the
+// calls: the control block; the tagged Z words of the one-launch decode
+// (fixed size for the dictionary's k, so no other path ever writes there);
+// the plain Z rows of the two-launch paths (fp32 on the dot-product path,
+// f16 on the MFMA path); the MFMA path's own workspace.
+struct FwdLayout {
+  size_t zwords, zplain, xd, total;
+};
+FwdLayout fwd_layout(int64_t rows, int32_t xdt, const dfs_dict* D) {
+  FwdLayout w;
+  w.zwords = round256(fused_z_words_bytes(D->k));
+  w.zplain = round256((size_t)rows * D->k * (mfma_path(rows, xdt, D) ? 2 : 4));
+  w.xd = xd_ws_bytes(rows, xdt, D);
+  w.total = kCtrlBytes + w.zwords + w.zplain + w.xd;
+  return w;
+}
+// The size query knows no activation dtype: the larger of the two layouts.
+size_t fwd_ws_bytes(int64_t rows, const dfs_dict* D) {
+  const size_t a = fwd_layout(rows, DFS_F16, D).total, b = fwd_layout(rows, DFS_F32, D).total;
+  return a > b ? a : b;
+}
 
 constexpr int32_t kMaxProducerK = 8192;  // the pruning kernel keeps a column's sort keys in LDS
 size_t gram_ws_bytes(const dfs_dict* D) {
@@ -503,9 +527,7 @@ dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, c
   if (n_layers > kMaxLayers) return DFS_E_RANGE;
   DFS_TRY(check_dict(D));
   if (!C || C->k != D->k || C->d_out <= 0) return DFS_E_INVALID;
-  const int64_t rows = (int64_t)n_layers * T;
-  const size_t per = rows <= kGemvMaxRows ? 8 : 4;  // decode: (epoch, value) words
-  *bytes = kCtrlBytes + round256((size_t)rows * D->k * per) + xd_ws_bytes(rows, DFS_F16, D);
+  *bytes = fwd_ws_bytes((int64_t)n_layers * T, D);
   return DFS_OK;
 }
 
@@ -586,20 +608,19 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
   const int64_t rows = (int64_t)n_layers * T;
   const bool mfma = mfma_path(rows, xdt, D);
   const int32_t zdt = mfma ? DFS_F16 : DFS_F32;
-  // the one-launch decode hands Z over as 8-byte (epoch, value) words
-  const size_t zbytes = round256((size_t)rows * D->k * (mfma ? 2 : 8));
-  const size_t need = kCtrlBytes + zbytes + xd_ws_bytes(rows, xdt, D);
-  if (!ws || ws_bytes < need) return DFS_E_WORKSPACE;
+  const FwdLayout w = fwd_layout(rows, xdt, D);
+  if (!ws || ws_bytes < w.total) return DFS_E_WORKSPACE;
   if (!aligned16(ws)) return DFS_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* ctrl = (uint32_t*)ws;
-  void* Z = (char*)ws + kCtrlBytes;
-  void* xws = (char*)Z + zbytes;
+  uint8_t* tagged = (uint8_t*)ws + kCtrlBytes;
+  void* Z = (char*)ws + kCtrlBytes + w.zwords;
+  void* xws = (char*)Z + w.zplain;
   if (!mfma && fused_allowed()) {
     XdLaunch xa = make_xd(n_layers, X, xdt, T, ldx, D, Z, zdt);
     ZcLaunch za = make_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy);
     if (fused_decode_supported(xa, za)) {
-      DFS_HIP(launch_fused_decode(xa, za, (float*)Z, ctrl, s));
+      DFS_HIP(launch_fused_decode(xa, za, tagged, ctrl, s));
       return DFS_OK;
     }
   }
@@ -611,13 +632,9 @@ dfs_status dict_multi_workspace_size(int32_t n_dicts, int32_t n_layers, int32_t 
                                      const dfs_dict* D, const dfs_csc* C, size_t* bytes) {
   if (!bytes || !D || !C || n_dicts <= 0) return DFS_E_INVALID;
   if (n_dicts > kMaxMultiDicts) return DFS_E_RANGE;
-  size_t one = 0;
-  DFS_TRY(dict_workspace_size(n_layers, T, D, C, &one));  // one group at a time
-  const int64_t rows = (int64_t)n_layers * T;
-  size_t all = 0;  // the one-launch decode: (epoch, value) words of every unit
-  if (rows <= kGemvMaxRows) all = kCtrlBytes + round256((size_t)n_dicts * rows * D->k * 8);
-  *bytes = one > all ? one : all;
-  return DFS_OK;
+  // one group at a time; the tagged Z words of the one-launch decode hold
+  // every (dictionary, layer) unit it runs
+  return dict_workspace_size(n_layers, T, D, C, bytes);
 }
 
 dfs_status dict_multi_forward(int32_t n_dicts, int32_t n_layers, const void* const* X,
@@ -649,14 +666,15 @@ dfs_status dict_multi_forward(int32_t n_dicts, int32_t n_layers, const void* con
   if (n_dicts > 1 && n_dicts <= kFusedMaxDicts && n_layers <= kFusedMaxLayers &&
       n_dicts * n_layers <= kFusedMaxUnits && fused_allowed()) {
     uint32_t* ctrl = (uint32_t*)ws;
-    void* Z = (char*)ws + kCtrlBytes;
+    uint8_t* tagged = (uint8_t*)ws + kCtrlBytes;
+    void* Z = (char*)ws + kCtrlBytes + round256(fused_z_words_bytes(D[0].k));
     XdLaunch xa = make_xd(n_layers, X, xdt, T, ldx, &D[0], Z, DFS_F32);
     xa.n_dicts = n_dicts;
     for (int d = 1; d < n_dicts; ++d)
       xa.more[d - 1] = {D[d].data, D[d].nv.codes, D[d].nv.scales, D[d].nv.tensor_scale};
     ZcLaunch za = make_zc(n_dicts * n_layers, Z, DFS_F32, T, C, Y, ydt, ldy);
     if (fused_decode_supported(xa, za)) {
-      DFS_HIP(launch_fused_decode(xa, za, (float*)Z, ctrl, s));
+      DFS_HIP(launch_fused_decode(xa, za, tagged, ctrl, s));
       return DFS_OK;
     }
   }

@@ -166,9 +166,14 @@ constexpr int kFusedMaxDicts = 3;
 constexpr int kFusedMaxUnits = 8;
 static_assert(kFusedMaxUnits <= kMaxLayers, "units fit the launch structs");
 constexpr int kCtrlBlockBytes = 4096;   // forward workspace control block
-constexpr int kMaxFusedGroups = 768;  // per-workgroup epoch words from byte 1024
+constexpr int kMaxFusedGroups = 1024;   // workgroups of the one-launch decode (one per CU)
 bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc);
-hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, float* zws,
+// Bytes of the tagged region of the one-launch decode (one epoch word per
+// workgroup, then kFusedMaxUnits rows of k tagged Z words), kept at a fixed
+// place after the control block: zero before first use, then kept by the
+// calls (no other path writes there).
+size_t fused_z_words_bytes(int32_t k);
+hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, uint8_t* tagged,
                                uint32_t* ctrl, hipStream_t s);
 
 hipError_t launch_gemv_xd(const XdLaunch& a, hipStream_t s);

@@ -15,8 +15,11 @@
 //      registers.
 // So the Z dependency costs one round trip through memory, hidden under the
 // C stream, instead of a second launch.  The grid never exceeds one
-// workgroup per CU, so every workgroup is resident; every wait is bounded
-// anyway (see receive_z), so the kernel always terminates.
+// workgroup per CU.  Should the grid still not be resident all at once
+// (other kernels holding CUs), a bounded wait gives up and the workgroup
+// computes the Z words it lacks itself, so the result stays right and the
+// kernel always terminates.
+#include <cstdlib>
 #include <type_traits>
 
 #include "csc_chunks.hpp"
@@ -51,13 +54,15 @@ struct LayerRow {
 // atomic store, so a reader that sees the current epoch also sees the value;
 // readers poll exactly the entries they need with agent-scope loads (these
 // bypass the non-coherent caches), so no cache-wide fence is needed.
-// Control block (caller's workspace, zero before first use): error word at
-// byte 128; from byte 1024 one epoch word per workgroup.  Workgroup w reads
-// its word, uses epoch + 1 and stores it back; every launch advances every
-// word once, so all workgroups of a launch agree on the epoch.  Polls are
-// bounded by spin_limit: a workgroup that gives up sets the error word and
-// continues, so the kernel always terminates.
-constexpr int kCtrlErr = 32, kCtrlEpochs = 256;  // in 32-bit words
+// The tagged region (caller's workspace after the control block, zero before
+// first use and kept by the calls): one epoch word per workgroup, then the
+// tagged Z words.  Workgroup w reads its epoch word, uses epoch + 1 and
+// stores it back; every launch advances every word once, so all workgroups
+// of a launch agree on the epoch, and every word a call reads carries its
+// epoch only once this call has published it.  The control block holds only
+// the diagnostic word at byte 128 (set when a wait gave up), so re-zeroing
+// it between calls is harmless.
+constexpr int kCtrlErr = 32;  // in 32-bit words
 
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
@@ -71,39 +76,6 @@ __device__ __forceinline__ uint64_t ld_agent64(const uint64_t* p) {
 }
 __device__ __forceinline__ void st_agent64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Copy the n tagged Z entries from zz into LDS zs as fp32 once each carries
-// `epoch`; 16 entries per thread are polled at a time.
-__device__ void receive_z(float* zs, const uint64_t* zz, int n, uint32_t epoch, uint32_t* err,
-                          uint32_t spin_limit) {
-  constexpr int kPer = 16;
-  for (int base = 0; base < n; base += kFT * kPer) {
-    uint32_t pending = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (base + j * kFT + (int)threadIdx.x < n) pending |= 1u << j;
-    uint32_t it = 0;
-    while (pending) {
-      uint64_t w[kPer];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (pending & (1u << j)) w[j] = ld_agent64(zz + base + j * kFT + threadIdx.x);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if ((pending & (1u << j)) && (uint32_t)(w[j] >> 32) == epoch) {
-          zs[base + j * kFT + threadIdx.x] = __uint_as_float((uint32_t)w[j]);
-          pending &= ~(1u << j);
-        }
-      if (pending) {
-        if (++it > spin_limit) {
-          st_agent(err, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-  }
 }
 
 // Launder a kernel-argument pointer through SGPRs so that a lane-dependent
@@ -162,17 +134,14 @@ struct FusedArgs {
   void* Y[NU];
   int64_t nnz[NU];
   const float* dts;
-  uint64_t* zz;    // n_layers x k epoch-tagged Z words
-  uint32_t* ctrl;  // control block
+  uint64_t* zz;        // units x k epoch-tagged Z words
+  uint32_t* epochs;    // one epoch word per workgroup
+  uint32_t* ctrl;      // control block (diagnostic word)
   int32_t n_layers, d_out, ydt;
-  uint32_t spin_limit;
+  uint32_t spin_limit;  // polls of one Z word before it is computed locally
   int32_t col_bytes;
   int32_t G;  // workgroups in the grid
-  // Byte offset of the received Z from the X rows in LDS.  0: Z overlays X
-  // (when both do not fit side by side), so the waves of a workgroup meet at
-  // a barrier before any of them writes Z: a wave that has finished its dot
-  // products would otherwise overwrite X under a wave still reading it.
-  int32_t z_off;
+  int32_t z_off;  // byte offset of the received Z from the X rows in LDS
   // several dictionaries over the same X rows: their count, and the codes,
   // block scales and tensor scale of dictionaries 1 and 2 (same d_in, k, ldd
   // and dtype as dictionary 0)
@@ -228,7 +197,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   const int d_in = f.d_in, k = f.k, d_out = f.d_out, nl = f.n_layers;
   if constexpr (Q8)  // the column scales are read with the column bounds
     asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
-                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
+                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.epochs), "s"(f.colptr[0]), "s"(f.colptr[1]),
                  "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G), "s"(f.vts[0]),
                  "s"(f.vts[1]), "s"(f.vts[2]), "s"(f.vts[3]));
   else if constexpr (DT == DFS_NVFP4)
@@ -237,12 +206,12 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
     // coefficient loads) shows in the step: fetch every line up front
     // (measured 0.2-0.3 us faster; no gain with an f16 dictionary)
     asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
-                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
+                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.epochs), "s"(f.colptr[0]), "s"(f.colptr[1]),
                  "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G), "s"(f.vals[0]),
                  "s"(f.vts[0]), "s"(f.z_off));
   else
     asm volatile("" ::"s"(d_in), "s"(k), "s"(d_out), "s"(nl), "s"(f.D), "s"(f.ldd), "s"(f.X[0]),
-                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.ctrl), "s"(f.colptr[0]), "s"(f.colptr[1]),
+                 "s"(f.X[RT > 1 ? 1 : 0]), "s"(f.epochs), "s"(f.colptr[0]), "s"(f.colptr[1]),
                  "s"(f.colptr[2]), "s"(f.colptr[3]), "s"(f.col_bytes), "s"(f.G));
   if constexpr (ND > 1)
     asm volatile("" ::"s"(f.Dx[0]), "s"(f.Dx[ND > 2 ? 1 : 0]), "s"(f.dscalesx[0]),
@@ -280,7 +249,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   const int c1 = (int)((blockIdx.x + 1) * NC / (uint32_t)f.G);
   const int ncols = c1 - c0;  // <= kFT (checked on the host)
   const int rounds = (ncols + kSlots - 1) / kSlots;
-  const uint32_t epoch_old = ld_agent(f.ctrl + kCtrlEpochs + blockIdx.x);
+  const uint32_t epoch_old = ld_agent(f.epochs + blockIdx.x);
   // this lane's columns in the first NB rounds (16 lanes per column)
   const int slot = wave * 4 + (lane >> 4);
   int rs_raw[NB], re_raw[NB], rl[NB];
@@ -417,9 +386,14 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
     }
   }
 
-  // Z overlays X: every wave's reads of X have returned (its published sums
-  // used them), so a barrier here is enough before Z is written.
-  if (f.z_off == 0) asm volatile("s_barrier" ::: "memory");
+  // Groups of 4 layers: the waves meet once every one has issued its Z
+  // stores, before any coefficient load of the workgroup goes out.  The
+  // stores then leave the CU ahead of that stream instead of queueing behind
+  // it; with 4 layers the C stream is large and a late publication delays
+  // every workgroup's receive (MLP gate group 34.5 -> 32.0 us, down 30.9 ->
+  // 30.0 us).  For smaller groups the receive waits for the coefficients
+  // either way, and the barrier only delays them.
+  if constexpr (ND == 1 && RT == 4) asm volatile("s_barrier" ::: "memory");
 
   // ---- 7. the column ranges into LDS; the first NB rounds of C in flight (their
   // bounds are older than D, so nothing here waits)
@@ -484,15 +458,84 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
     }
   };
 
-  // ---- 8. receive the Z rows of this workgroup's layers into LDS
+  // ---- 8. receive the Z rows of this workgroup's units into LDS, 16 words
+  // per thread at a time.  A word still missing after spin_limit polls is
+  // computed here from the X rows in LDS and D_g (same definition, another
+  // summation order), and the diagnostic word is set.
   {
     const int l_first = c0 / d_out, l_last = (c1 - 1) / d_out;
-    receive_z(zs + l_first * k, f.zz + (int64_t)l_first * k, (l_last - l_first + 1) * k, epoch,
-              f.ctrl + kCtrlErr, f.spin_limit);
+    const int n = (l_last - l_first + 1) * k;
+    const uint64_t* zsrc = f.zz + (int64_t)l_first * k;
+    float* zdst = zs + l_first * k;
+    auto local_z = [&](int idx) {
+      const int u = l_first + idx / k, atom = idx - (idx / k) * k;
+      const int dd = ND == 1 ? 0 : u / nl;
+      const void* Dd = f.D;
+      const uint8_t* Sd = f.dscales;
+      if constexpr (ND > 1) {
+        Dd = dd == 1 ? f.Dx[0] : Dd;
+        Sd = dd == 1 ? f.dscalesx[0] : Sd;
+      }
+      if constexpr (ND > 2) {
+        Dd = dd == 2 ? f.Dx[1] : Dd;
+        Sd = dd == 2 ? f.dscalesx[1] : Sd;
+      }
+      const _Float16* x = xs + (u - dd * nl) * ld;
+      float acc = 0.0f;
+#pragma unroll 1
+      for (int e0 = 0; e0 < d_in; e0 += CE) {
+        u4 dv;
+        uint32_t sc = 0u;
+        if constexpr (DT == DFS_NVFP4) {
+          const int64_t el = (int64_t)atom * d_in + e0;
+          dv = ld16<u4>((const uint8_t*)Dd + el / 2);
+          sc = (uint32_t)gptr(Sd)[el / 16] | ((uint32_t)gptr(Sd)[el / 16 + 1] << 8);
+        } else {
+          dv = ld16<u4>((const _Float16*)Dd + (int64_t)atom * f.ldd + e0);
+        }
+        acc = dot_chunk<DT, true, _Float16>(dv, sc, x + e0, acc);
+      }
+      float ts = dts[0];
+#pragma unroll
+      for (int d = 1; d < ND; ++d) ts = dd == d ? dts[d] : ts;
+      return acc * ts;
+    };
+    constexpr int kPer = 16;
+    for (int base = 0; base < n; base += kFT * kPer) {
+      uint32_t pending = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (base + j * kFT + tid < n) pending |= 1u << j;
+      uint32_t it = 0;
+      while (pending) {
+        uint64_t w[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if (pending & (1u << j)) w[j] = ld_agent64(zsrc + base + j * kFT + tid);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if ((pending & (1u << j)) && (uint32_t)(w[j] >> 32) == epoch) {
+            zdst[base + j * kFT + tid] = __uint_as_float((uint32_t)w[j]);
+            pending &= ~(1u << j);
+          }
+        if (pending) {
+          if (it >= f.spin_limit) {
+            st_agent(f.ctrl + kCtrlErr, 1u);
+#pragma unroll 1
+            for (int j = 0; j < kPer; ++j)
+              if (pending & (1u << j)) zdst[base + j * kFT + tid] = local_z(base + j * kFT + tid);
+            pending = 0;
+          } else {
+            ++it;
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+      }
+    }
   }
   __syncthreads();
   // every wave has published and received: advance this workgroup's epoch
-  if (tid == 0) st_agent(f.ctrl + kCtrlEpochs + blockIdx.x, epoch);
+  if (tid == 0) st_agent(f.epochs + blockIdx.x, epoch);
 
   // ---- 9. the columns, NB rounds in flight
   auto consume = [&](const IdxChunk* ic, const ValChunk<VT>* vc, int r) {
@@ -579,11 +622,26 @@ int device_cus() {
   return g_cus[dev];
 }
 
+// Polls of one Z word before a workgroup computes it itself: 2^20 polls of
+// about a microsecond each, unless DFS_SPIN_LIMIT sets another count (0 makes
+// every word that is not already published at the first poll local).
+uint32_t spin_limit() {
+  const char* v = std::getenv("DFS_SPIN_LIMIT");
+  if (v && *v) {
+    char* end = nullptr;
+    const unsigned long n = std::strtoul(v, &end, 10);
+    if (end && *end == '\0') return n > 0xFFFFFFFFul ? 0xFFFFFFFFu : (uint32_t)n;
+  }
+  return 1u << 20;
+}
+
+constexpr size_t kEpochBytes = (size_t)kMaxFusedGroups * 4;  // one epoch word per workgroup
+
 struct Plan {
   int G, A, RT, NX;  // NX = RT, 2 * RT or 3 * RT (X passes per row)
   int ND;            // dictionaries over the X rows
   size_t col_bytes, smem;
-  int z_off;         // 0 when Z overlays X
+  int z_off;         // byte offset of Z from the X rows in LDS
 };
 
 bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
@@ -625,17 +683,13 @@ bool plan(const XdLaunch& xd, const ZcLaunch& zc, Plan* p) {
   p->NX = NX;
   p->ND = nd;
   p->col_bytes = ((size_t)max_cols * (q8 ? 16 : 8) + 15) / 16 * 16;
-  // X and Z side by side when they fit, else Z over X (with a barrier)
-  constexpr size_t kMaxSmem = 144 * 1024;
+  // X rows and Z side by side in LDS (X stays readable for a Z word that a
+  // workgroup computes itself)
+  constexpr size_t kMaxSmem = 160 * 1024;
   const size_t table = nd == 1 ? table_bytes_of<1>() : table_bytes_of<2>();
   const size_t xalign = (xbytes + 15) / 16 * 16;
-  if (table + p->col_bytes + xalign + zbytes <= kMaxSmem) {
-    p->z_off = (int)xalign;
-    p->smem = table + p->col_bytes + xalign + zbytes;
-  } else {
-    p->z_off = 0;
-    p->smem = table + p->col_bytes + (xbytes > zbytes ? xbytes : zbytes);
-  }
+  p->z_off = (int)xalign;
+  p->smem = table + p->col_bytes + xalign + zbytes;
   return p->smem <= kMaxSmem;
 }
 
@@ -712,7 +766,7 @@ hipError_t mlaunch2(ArgsFor<ND> f, const Plan& p, int vdt, hipStream_t s) {
 }
 
 template <int ND>
-ArgsFor<ND> make_args(const XdLaunch& xd, const ZcLaunch& zc, float* zws, uint32_t* ctrl) {
+ArgsFor<ND> make_args(const XdLaunch& xd, const ZcLaunch& zc, uint8_t* tagged, uint32_t* ctrl) {
   ArgsFor<ND> f = {};
   f.D = xd.ddt == DFS_NVFP4 ? (const void*)xd.dcodes : xd.D;
   f.dscales = xd.dscales;
@@ -730,12 +784,13 @@ ArgsFor<ND> make_args(const XdLaunch& xd, const ZcLaunch& zc, float* zws, uint32
     f.nnz[u] = zc.nnz[u];
   }
   f.dts = xd.dts;
-  f.zz = reinterpret_cast<uint64_t*>(zws);
+  f.epochs = reinterpret_cast<uint32_t*>(tagged);
+  f.zz = reinterpret_cast<uint64_t*>(tagged + kEpochBytes);
   f.ctrl = ctrl;
   f.n_layers = xd.n_layers;
   f.d_out = zc.d_out;
   f.ydt = zc.ydt;
-  f.spin_limit = 1u << 22;
+  f.spin_limit = spin_limit();
   f.col_bytes = 0;
   f.n_dicts = ND;
   for (int d = 1; d < ND; ++d) {
@@ -762,22 +817,24 @@ bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc) {
   return plan(xd, zc, &p);
 }
 
-hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, float* zws,
+size_t fused_z_words_bytes(int32_t k) { return kEpochBytes + (size_t)kFusedMaxUnits * k * 8; }
+
+hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, uint8_t* tagged,
                                uint32_t* ctrl, hipStream_t s) {
   Plan p;
   if (!plan(xd, zc, &p)) return hipErrorInvalidValue;
   const bool nv = xd.ddt == DFS_NVFP4;
   switch (p.ND) {
     case 1: {
-      const ArgsFor<1> f = make_args<1>(xd, zc, zws, ctrl);
+      const ArgsFor<1> f = make_args<1>(xd, zc, tagged, ctrl);
       return nv ? launch1<DFS_NVFP4>(f, p, zc.vdt, s) : launch1<DFS_F16>(f, p, zc.vdt, s);
     }
     case 2: {
-      const ArgsFor<2> f = make_args<2>(xd, zc, zws, ctrl);
+      const ArgsFor<2> f = make_args<2>(xd, zc, tagged, ctrl);
       return nv ? mlaunch2<DFS_NVFP4, 2>(f, p, zc.vdt, s) : mlaunch2<DFS_F16, 2>(f, p, zc.vdt, s);
     }
     default: {
-      const ArgsFor<3> f = make_args<3>(xd, zc, zws, ctrl);
+      const ArgsFor<3> f = make_args<3>(xd, zc, tagged, ctrl);
       return nv ? mlaunch2<DFS_NVFP4, 3>(f, p, zc.vdt, s) : mlaunch2<DFS_F16, 3>(f, p, zc.vdt, s);
     }
   }

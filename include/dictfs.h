@@ -32,7 +32,11 @@
  *   - Accumulation is always fp32.  Results are deterministic run to run
  *     (no floating-point atomics).
  *   - Thread safety: calls hold no mutable global state beyond a per-thread
- *     last-HIP-error code; concurrent calls on different streams are safe.
+ *     last-HIP-error code; concurrent calls on different streams are safe
+ *     when they do not share a workspace.  The one-launch decode runs one
+ *     workgroup per CU and hands Z between them; if two such launches (or
+ *     other kernels) share the GPU, the bounded waits described under
+ *     dict_workspace_size keep the results right, at a cost in time.
  */
 #ifndef DICTFS_H
 #define DICTFS_H
@@ -107,8 +111,10 @@ typedef struct {
  * of 8 entries, so rowidx and vals must be allocated for
  * dict_csc_capacity(nnz) entries (NVFP4 codes: half that many bytes; block
  * scales: ceil(nnz / 16) bytes; FP8/INT8 codes: that many bytes).  Entries
- * past nnz are never used and may hold anything.  The caller owns all
- * arrays.
+ * past nnz are never used and may hold anything.  `capacity` states the
+ * entries (blocks, with block_rows = 8) that rowidx and the values are
+ * allocated for; every call that reads the arrays rejects capacity <
+ * dict_csc_capacity(nnz) with DFS_E_RANGE.  The caller owns all arrays.
  * Block-structured support (block_rows = 8; 0 means one entry per stored
  * element): each column keeps whole blocks of 8 consecutive atoms (the
  * variant of "DictLLM: Shared Dictionaries for Post-Training Compression",
@@ -130,6 +136,7 @@ typedef struct {
   const void* vals;
   dfs_nvfp4 nv;
   const float* col_scale; /* FP8 / INT8 only: one scale per column */
+  int64_t capacity;       /* entries (blocks) rowidx and the values hold */
 } dfs_csc;
 
 /* ---------------------------------------------------------------------- */
@@ -223,15 +230,26 @@ dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream);
  * (dict_proj_forward: n_layers = 1).  D and C describe the shapes and dtypes
  * (C may point at any one layer's descriptor; only k/d_out/dtype are read).
  *
- * Forward workspace contract: its first 4096 bytes are a control block that
- * must be ZERO before the first forward call that uses the workspace (e.g.
- * hipMemset once after allocation); later calls keep it consistent (it holds
- * the per-workgroup epoch words of the one-launch decode, whose workgroups
- * hand Z to each other as epoch-tagged words instead of meeting at a grid
- * barrier).  Calls sharing one workspace must not run concurrently.  After a
- * call, the 32-bit word at byte offset 128 is non-zero only if the one-launch
- * decode path (T = 1, <= 4 layers) gave up waiting for a Z word (a bounded
- * wait), in which case that call's outputs are invalid. */
+ * The size does not depend on the activation dtype (the larger of the f16
+ * and f32 layouts), so a workspace of this size serves either.
+ *
+ * Forward workspace contract: the whole workspace must be ZERO before the
+ * first forward call that uses it (e.g. hipMemset once after allocation).
+ * It starts with a 4096-byte control block followed by 64 * k bytes of
+ * tagged Z words through which the workgroups of the one-launch decode hand
+ * Z to each other instead of meeting at a grid barrier; every call leaves
+ * both zero again when it completes (so zeroing them again between calls,
+ * all or in part, is harmless).  The rest is scratch for the call.  Calls
+ * sharing one workspace must not run concurrently.  The 32-bit word at byte
+ * offset 128 becomes non-zero when a workgroup of the one-launch decode
+ * (T = 1, <= 4 layers) gave up waiting for a published Z word after a
+ * bounded number of polls and computed the missing words itself from X and
+ * D_g, which happens when its grid is not resident all at once (for
+ * instance, while other kernels hold some CUs).  The outputs are right
+ * either way; the word is a diagnostic that stays set until the caller
+ * clears it.  The bound is 2^20 polls of about a microsecond, or the value
+ * of the environment variable DFS_SPIN_LIMIT (0: compute every word that is
+ * not published at the first poll), read at each call. */
 dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, const dfs_csc* C,
                                size_t* bytes);
 

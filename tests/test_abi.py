@@ -50,8 +50,9 @@ def _dict(d_in=256, k=128, dtype=B.DFS_F16, data=P, ldd=None, nv=None):
 
 
 def _csc(k=128, d_out=64, nnz=100, dtype=B.DFS_F16, colptr=P, rowidx=P, vals=P, nv=None,
-         col_scale=None):
-    return B.Csc(k, d_out, nnz, dtype, 0, colptr, rowidx, vals, nv or B.NV(), col_scale)
+         col_scale=None, capacity=None):
+    cap = (nnz + 7) // 8 * 8 if capacity is None else capacity
+    return B.Csc(k, d_out, nnz, dtype, 0, colptr, rowidx, vals, nv or B.NV(), col_scale, cap)
 
 
 def _group(n=1, X=P, xdt=B.DFS_F16, T=1, ldx=256, D=None, Cs=None, Y=P, ydt=B.DFS_F16, ldy=64,
@@ -260,12 +261,12 @@ def test_producer_validation():
 def test_block_csc_validation():
     L = B.lib()
     assert _group(Cs=[_csc(dtype=B.DFS_F16)]) != UNSUPPORTED
-    blk = B.Csc(128, 64, 100, B.DFS_F16, 8, P, P, P, B.NV(), None)
+    blk = B.Csc(128, 64, 100, B.DFS_F16, 8, P, P, P, B.NV(), None, 104)
     assert _group(Cs=[blk], T=0) == OK
     assert _group(Cs=[blk], T=17) == UNSUPPORTED          # decode / small batch only
-    bad = B.Csc(128, 64, 100, B.DFS_F16, 4, P, P, P, B.NV(), None)
+    bad = B.Csc(128, 64, 100, B.DFS_F16, 4, P, P, P, B.NV(), None, 104)
     assert _group(Cs=[bad]) == UNSUPPORTED                # blocks of 8 only
-    nvb = B.Csc(128, 64, 100, B.DFS_NVFP4, 8, P, P, None, B.NV(P, P, P), None)
+    nvb = B.Csc(128, 64, 100, B.DFS_NVFP4, 8, P, P, None, B.NV(P, P, P), None, 104)
     assert _group(Cs=[nvb]) == UNSUPPORTED
     assert _group(n=2, Cs=[_csc(), blk]) == UNSUPPORTED   # one format per group
     nb = C.c_int64(0)
@@ -321,3 +322,44 @@ def test_multi_forward_validation():
 
 def L_size(nd, n, T, d, c, out):
     return B.lib().dict_multi_workspace_size(nd, n, T, C.byref(d), C.byref(c), C.byref(out))
+
+
+def test_csc_capacity_is_checked():
+    # rowidx / vals hold whole 8-entry chunks: capacity >= nnz rounded up to 8
+    assert _group(Cs=[_csc(nnz=100, capacity=100)]) == RANGE
+    assert _group(Cs=[_csc(nnz=100, capacity=103)]) == RANGE
+    assert _group(Cs=[_csc(nnz=100, capacity=104)], ws=P + 8) == ALIGN  # passes the check
+    assert _group(Cs=[_csc(nnz=1, capacity=7)]) == RANGE
+    assert _group(Cs=[_csc(nnz=0, capacity=0)], ws=P + 8) == ALIGN     # nothing is read
+    # the same check guards the half entry point and the multi-dictionary call
+    cs = (B.Csc * 1)(_csc(nnz=100, capacity=96))
+    yp = (C.c_void_p * 1)(P)
+    assert B.lib().dict_zc_forward(1, P, B.DFS_F32, 1, cs, yp, B.DFS_F16, 64, None) == RANGE
+
+
+@pytest.mark.parametrize("xdt,ddt,T,n", [(B.DFS_F32, B.DFS_F32, 32, 2), (B.DFS_F32, B.DFS_F16, 32, 2),
+                                         (B.DFS_F16, B.DFS_F16, 32, 2), (B.DFS_F16, B.DFS_F32, 9, 2),
+                                         (B.DFS_F16, B.DFS_F16, 1, 4), (B.DFS_F32, B.DFS_F16, 1, 3),
+                                         (B.DFS_F16, B.DFS_F16, 2048, 2)])
+def test_workspace_query_serves_the_forward(xdt, ddt, T, n):
+    # the size the query returns is enough for the forward of any activation
+    # dtype (the call then fails on the misaligned workspace, after the size
+    # check and before any launch), and one byte less is not
+    L = B.lib()
+    D = _dict(d_in=256, k=128, dtype=ddt, ldd=256)
+    c = _csc(k=128, d_out=64)
+    nb = C.c_size_t(0)
+    assert L.dict_workspace_size(n, T, C.byref(D), C.byref(c), C.byref(nb)) == OK
+    ldx = 256
+    assert _group(n=n, xdt=xdt, T=T, ldx=ldx, D=D, Cs=[c] * n, ws=P + 8, ws_bytes=nb.value) == ALIGN
+    # the forward's own need for these dtypes is at most the query's
+    assert _group(n=n, xdt=xdt, T=T, ldx=ldx, D=D, Cs=[c] * n, ws=P + 8,
+                  ws_bytes=nb.value - 1) in (ALIGN, WORKSPACE)
+    ms = C.c_size_t(0)
+    cs = (B.Csc * (2 * n))(*([c] * (2 * n)))
+    Ds = (B.Dict * 2)(D, D)
+    assert L.dict_multi_workspace_size(2, n, T, Ds, cs, C.byref(ms)) == OK
+    xp = (C.c_void_p * n)(*([P] * n))
+    yp = (C.c_void_p * (2 * n))(*([P] * (2 * n)))
+    assert L.dict_multi_forward(2, n, xp, xdt, T, ldx, Ds, cs, yp, B.DFS_F16, 64, P + 8,
+                                ms.value, None) == ALIGN

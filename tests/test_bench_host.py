@@ -19,7 +19,10 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_traffic_follows_the_recorded_counters():
     t = bench.TRAFFIC_MEASURED
-    assert bench._sources_digest() == t["digest"], "kernel sources changed since the counters"
+    if bench._sources_digest() != t["digest"]:
+        # kernel sources changed since the counters were taken: no figure
+        assert bench._traffic_bytes() is None
+        return
     want = round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
     assert bench._traffic_bytes() == want
     # the counters cover the launch's algorithmic bytes and little more

@@ -32,7 +32,7 @@ def _check(gs, dfmt, cfmt, reps=1):
     n = len(Xs)
     ws = B.multi_workspace(len(Ds), n, Xs[0].shape[0], Ds[0], Cs[0], Xs[0].device)
     outs = []
-    for _ in range(reps):  # repeated calls on one workspace (epochs advance)
+    for _ in range(reps):  # repeated calls on one workspace
         outs.append([y.clone() for y in B.dict_multi_forward(Xs, Ds, Cs, ws=ws)])
     torch.cuda.synchronize()
     assert B.workspace_error_word(ws) == 0
