@@ -459,9 +459,10 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   };
 
   // ---- 8. receive the Z rows of this workgroup's units into LDS, 16 words
-  // per thread at a time.  A word still missing after spin_limit polls is
-  // computed here from the X rows in LDS and D_g (same definition, another
-  // summation order), and the diagnostic word is set.
+  // per thread at a time.  A word still missing after spin_limit polls (at
+  // once when spin_limit is 0) is computed here from the X rows in LDS and
+  // D_g (same definition, another summation order), and the diagnostic word
+  // is set.
   {
     const int l_first = c0 / d_out, l_last = (c1 - 1) / d_out;
     const int n = (l_last - l_first + 1) * k;
@@ -506,8 +507,15 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
         if (base + j * kFT + tid < n) pending |= 1u << j;
-      uint32_t it = 0;
-      while (pending) {
+      for (uint32_t it = 0; pending; ++it) {
+        if (it >= f.spin_limit) {
+          st_agent(f.ctrl + kCtrlErr, 1u);
+#pragma unroll 1
+          for (int j = 0; j < kPer; ++j)
+            if (pending & (1u << j)) zdst[base + j * kFT + tid] = local_z(base + j * kFT + tid);
+          break;
+        }
+        if (it > 0) __builtin_amdgcn_s_sleep(1);
         uint64_t w[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
@@ -518,18 +526,6 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
             zdst[base + j * kFT + tid] = __uint_as_float((uint32_t)w[j]);
             pending &= ~(1u << j);
           }
-        if (pending) {
-          if (it >= f.spin_limit) {
-            st_agent(f.ctrl + kCtrlErr, 1u);
-#pragma unroll 1
-            for (int j = 0; j < kPer; ++j)
-              if (pending & (1u << j)) zdst[base + j * kFT + tid] = local_z(base + j * kFT + tid);
-            pending = 0;
-          } else {
-            ++it;
-            __builtin_amdgcn_s_sleep(1);
-          }
-        }
       }
     }
   }
@@ -623,8 +619,8 @@ int device_cus() {
 }
 
 // Polls of one Z word before a workgroup computes it itself: 2^20 polls of
-// about a microsecond each, unless DFS_SPIN_LIMIT sets another count (0 makes
-// every word that is not already published at the first poll local).
+// about a microsecond each, unless DFS_SPIN_LIMIT sets another count (0: no
+// poll, every workgroup computes every Z word it needs).
 uint32_t spin_limit() {
   const char* v = std::getenv("DFS_SPIN_LIMIT");
   if (v && *v) {

@@ -248,8 +248,8 @@ dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream);
  * instance, while other kernels hold some CUs).  The outputs are right
  * either way; the word is a diagnostic that stays set until the caller
  * clears it.  The bound is 2^20 polls of about a microsecond, or the value
- * of the environment variable DFS_SPIN_LIMIT (0: compute every word that is
- * not published at the first poll), read at each call. */
+ * of the environment variable DFS_SPIN_LIMIT, read at each call (0: no poll
+ * at all, every workgroup computes every Z word it needs: slow, for tests). */
 dfs_status dict_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, const dfs_csc* C,
                                size_t* bytes);
 

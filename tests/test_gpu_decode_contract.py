@@ -3,8 +3,9 @@ between workgroups as tagged words in the workspace), on the GPU:
 
 * when a workgroup's bounded wait for a published Z word gives up, it computes
   the word itself from X and D_g, so Y still matches the oracle; the host
-  forces that path by setting the poll bound to 0 (every kernel still runs to
-  its end: nothing waits without a bound);
+  forces that path by setting the poll bound to 0, which makes every
+  workgroup compute every word it needs without polling (every kernel runs
+  to its end: nothing waits without a bound);
 * the control block holds only a diagnostic word (the epochs of the Z hand-off
   live in the tagged region after it), so a caller that re-zeroes the control
   block (or nothing) between calls on one workspace gets right results;
@@ -56,8 +57,7 @@ def test_decode_computes_z_itself_when_waits_give_up(wl, ptype, n, dfmt, cfmt):
     with _spin_limit(0):
         Ys = B.dict_group_forward(Xs, D, Cs, ws=ws)
         torch.cuda.synchronize()
-    # 256 workgroups polling right after their own publication: some find
-    # words missing, compute them and say so
+    # no poll: every workgroup computed its Z words itself and said so
     assert B.workspace_error_word(ws) == 1
     refs = oracle_group(g, dfmt=dfmt, cfmt=cfmt)
     for l, ref in enumerate(refs):
