@@ -32,7 +32,7 @@ SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspac
            "dict_csc_quantize8_workspace_size", "dict_csc_quantize8",
            "dict_gram_inverse_workspace_size", "dict_gram_inverse", "dict_obs_prune",
            "dict_refit_workspace_size", "dict_refit", "dict_pack_bcsc", "dfs_probe_mfma",
-           "dict_multi_workspace_size", "dict_multi_forward")
+           "dict_multi_workspace_size", "dict_multi_forward", "dict_group_forward_noalloc")
 
 
 class NV(C.Structure):
@@ -102,6 +102,8 @@ def lib():
             "dict_multi_workspace_size": [i32, i32, i32, C.POINTER(Dict), C.POINTER(Csc), psz],
             "dict_multi_forward": [i32, i32, C.POINTER(vp), i32, i32, i64, C.POINTER(Dict),
                                    C.POINTER(Csc), C.POINTER(vp), i32, i64, vp, sz, vp],
+            "dict_group_forward_noalloc": [i32, C.POINTER(vp), i32, i32, i64, C.POINTER(Dict),
+                                           C.POINTER(Csc), C.POINTER(vp), i32, i64, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -378,6 +380,21 @@ def dict_group_forward(Xs, D: DeviceDict, Cs, Ys=None, ydtype=torch.float16, ws=
            lib().dict_group_forward(n, xp, _dt(Xs[0]), T, Xs[0].stride(0), C.byref(d), cs, yp,
                                     _dt(Ys[0]), Ys[0].stride(0), ws.data_ptr(), ws.numel(),
                                     _stream(stream)))
+    return Ys
+
+
+def dict_group_forward_noalloc(Xs, D: DeviceDict, Cs, Ys, stream=None):
+    """dict_group_forward on the library's own workspace (no allocation in
+    the call; Ys must be given)."""
+    n = len(Xs)
+    T = Xs[0].shape[0]
+    xp = (C.c_void_p * n)(*[x.data_ptr() for x in Xs])
+    yp = (C.c_void_p * n)(*[y.data_ptr() for y in Ys])
+    cs = (Csc * n)(*[c.desc() for c in Cs])
+    d = D.desc()
+    _check("dict_group_forward_noalloc",
+           lib().dict_group_forward_noalloc(n, xp, _dt(Xs[0]), T, Xs[0].stride(0), C.byref(d), cs,
+                                            yp, _dt(Ys[0]), Ys[0].stride(0), _stream(stream)))
     return Ys
 
 

@@ -8,6 +8,7 @@
 // before anything is enqueued.
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "dfs_internal.hpp"
 
@@ -595,6 +596,52 @@ dfs_status check_group(int32_t n_layers, const void* const* X, int32_t xdt, int3
 }
 
 constexpr int32_t kMaxMultiDicts = 8;
+
+// ---- the workspace of dict_group_forward_noalloc: a file-scope device
+// array, one copy per GPU the library runs on, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is ever passed on.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+bool g_scratch_zeroed[kMaxDevices];
+
+// Zeroes the control block and the tagged region (the part of a forward
+// workspace that must start at zero) without a memset, so that a call under
+// graph capture records a kernel node.
+__global__ void zero_words(u4* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u4{0u, 0u, 0u, 0u};
+}
+
+// Device address of the current device's `scratch`; on the first call for a
+// device, also enqueues on `s` the zeroing of the part that must start at 0.
+dfs_status scratch_of_current_device(void** out, hipStream_t s) {
+  int dev = -1;
+  DFS_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return DFS_E_RANGE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DFS_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return DFS_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  if (!g_scratch_zeroed[dev]) {
+    const size_t zero_bytes = kCtrlBytes + round256(fused_z_words_bytes(kMaxKForward));
+    hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, s, (u4*)g_scratch_ptr[dev],
+                       (int64_t)(zero_bytes / 16));
+    DFS_HIP(hipGetLastError());
+    g_scratch_zeroed[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return DFS_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -682,6 +729,18 @@ dfs_status dict_multi_forward(int32_t n_dicts, int32_t n_layers, const void* con
     DFS_TRY(dict_group_forward(n_layers, X, xdt, T, ldx, &D[d], C + (size_t)d * n_layers,
                                Y + (size_t)d * n_layers, ydt, ldy, ws, ws_bytes, stream));
   return DFS_OK;
+}
+
+dfs_status dict_group_forward_noalloc(int32_t n_layers, const void* const* X, int32_t xdt,
+                                      int32_t T, int64_t ldx, const dfs_dict* D, const dfs_csc* C,
+                                      void* const* Y, int32_t ydt, int64_t ldy, void* stream) {
+  DFS_TRY(check_group(n_layers, X, xdt, T, ldx, D, C, Y, ydt, ldy));
+  if (T == 0) return DFS_OK;
+  if (fwd_layout((int64_t)n_layers * T, xdt, D).total > kScratchBytes) return DFS_E_WORKSPACE;
+  void* ws = nullptr;
+  DFS_TRY(scratch_of_current_device(&ws, (hipStream_t)stream));
+  return dict_group_forward(n_layers, X, xdt, T, ldx, D, C, Y, ydt, ldy, ws, kScratchBytes,
+                            stream);
 }
 
 dfs_status dict_proj_forward(const void* X, int32_t xdt, int32_t T, int64_t ldx, const dfs_dict* D,

@@ -279,6 +279,21 @@ dfs_status dict_group_forward(int32_t n_layers, const void* const* X, int32_t xd
                               int64_t ldx, const dfs_dict* D, const dfs_csc* C, void* const* Y,
                               int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
 
+/* dict_group_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and results, with no workspace
+ * argument.  Its workspace is a 64 MiB array inside the library, one per GPU
+ * the library runs on, held until the process ends; shapes whose workspace
+ * (dict_workspace_size) exceeds 64 MiB give DFS_E_WORKSPACE.  The call itself
+ * allocates nothing; on its first use on a device it enqueues the zeroing of
+ * the part of the array that must start at zero.  Every call on a GPU shares
+ * that GPU's array, so calls that overlap in time on one GPU (other streams,
+ * other threads) race and must not be made.  Arguments and errors as for
+ * dict_group_forward. */
+dfs_status dict_group_forward_noalloc(int32_t n_layers, const void* const* X, int32_t xdt,
+                                      int32_t T, int64_t ldx, const dfs_dict* D, const dfs_csc* C,
+                                      void* const* Y, int32_t ydt, int64_t ldy, void* stream);
+
 /* Several layer groups that read the same activations, one dictionary each
  * (as the q, k and v projections of the same layers do; each group is the
  * factored projection of Eq. (1) with its own D_g, Figure 2):

@@ -363,3 +363,26 @@ def test_workspace_query_serves_the_forward(xdt, ddt, T, n):
     yp = (C.c_void_p * (2 * n))(*([P] * (2 * n)))
     assert L.dict_multi_forward(2, n, xp, xdt, T, ldx, Ds, cs, yp, B.DFS_F16, 64, P + 8,
                                 ms.value, None) == ALIGN
+
+
+def test_noalloc_entry_point_rejects_before_any_launch():
+    # dict_group_forward_noalloc: the same argument checks as the group
+    # forward, then the workspace the shape needs against the library's
+    # 64 MiB array -- both on the host, before anything is enqueued
+    L = B.lib()
+
+    def na(n=1, T=1, D=None, Cs=None, X=P, ldx=256, xdt=B.DFS_F16):
+        D = D or _dict()
+        Cs = Cs or [_csc() for _ in range(n)]
+        xp = (C.c_void_p * n)(*([X] * n))
+        yp = (C.c_void_p * n)(*([P] * n))
+        cs = (B.Csc * n)(*Cs)
+        return L.dict_group_forward_noalloc(n, xp, xdt, T, ldx, C.byref(D), cs, yp, B.DFS_F16,
+                                            64, None)
+    assert na(T=0) == OK
+    assert na(X=0) == INVALID
+    assert na(D=_dict(k=20000)) == RANGE
+    assert na(Cs=[_csc(nnz=100, capacity=96)]) == RANGE
+    # 16 layers x 2048 tokens against k = 16384 atoms: a 1 GiB Z tile
+    big = _dict(d_in=4096, k=16384, ldd=4096)
+    assert na(n=16, T=2048, D=big, Cs=[_csc(k=16384) for _ in range(16)], ldx=4096) == WORKSPACE
