@@ -17,7 +17,9 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdictfs.so")
+# DFS_LIB_PATH selects another build of the same library (the host-sanitized
+# build used by the CPU sanitizer test); there is no fallback when it is missing
+LIB_PATH = os.environ.get("DFS_LIB_PATH") or os.path.join(_PKG, "libdictfs.so")
 
 DFS_F32, DFS_F16, DFS_NVFP4, DFS_FP8, DFS_INT8 = 0, 1, 2, 3, 4
 CODE8 = {"fp8": DFS_FP8, "int8": DFS_INT8}

@@ -71,5 +71,38 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "san", "libdictfs.so")
+# host code only: every -fsanitize= applies to the host pass (-Xarch_host);
+# device code is unchanged
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+            "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """A copy of the library whose host code (the C ABI's argument checks,
+    plans and launches, all in api.hip) is built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, for CPU tests (load it with DFS_LIB_PATH and
+    clang's ASan runtime preloaded).  Reuses the other objects of build()."""
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    others = [os.path.join(BUILD, os.path.basename(f) + ".o")
+              for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+              if os.path.basename(f) != "api.hip"]
+    if not all(os.path.exists(o) for o in others):
+        build(verbose)
+    obj = os.path.join(os.path.dirname(SAN_LIB), "api.hip.o")
+    cmd = [_hipcc(), *COMMON, *SAN_HOST, "-c", os.path.join(CSRC, "api.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on api.hip (sanitized):\n{r.stderr}")
+    r = subprocess.run([_hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", SAN_LIB + ".tmp", obj,
+                        *others], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build_host_sanitized(verbose=True) if "--sanitize" in sys.argv
+          else build(verbose="-v" in sys.argv))

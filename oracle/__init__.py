@@ -37,7 +37,8 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# DFS_ORACLE_LIB selects another build of oracle.c (the sanitizer build)
+_LIB_PATH = os.environ.get("DFS_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 DT_F32, DT_F16, DT_NVFP4, DT_FP8, DT_INT8 = 0, 1, 2, 3, 4   # element types of oracle.c
 
@@ -289,6 +290,8 @@ def forward(X: np.ndarray, D, d_in: int, c: CSC) -> np.ndarray:
     Y = np.zeros((T, c.d_out), np.float64)
     rc = lib().orc_forward(T, C.byref(tx), d_in, d_in, c.k, C.byref(td), d_in, c.d_out,
                            _ptr(colptr), _ptr(rowidx), C.byref(tc), _ptr(Y))
+    if rc == -2:
+        raise ValueError("oracle forward: not a CSC (colptr or a row index out of range)")
     if rc != 0:
         raise MemoryError("oracle forward: allocation failed")
     return Y
@@ -350,6 +353,8 @@ def forward_bcsc(X: np.ndarray, D, d_in: int, b: BCSC) -> np.ndarray:
     Y = np.zeros((T, b.d_out), np.float64)
     rc = lib().orc_forward_bcsc(T, C.byref(tx), d_in, d_in, b.k, C.byref(td), d_in, b.d_out,
                                 _ptr(colptr), _ptr(bidx), C.byref(tc), _ptr(Y))
+    if rc == -2:
+        raise ValueError("oracle forward_bcsc: not a block CSC (colptr or a block index out of range)")
     if rc != 0:
         raise MemoryError("oracle forward_bcsc: allocation failed")
     return Y

@@ -16,15 +16,25 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC",
-           "-shared", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer (CPU only); a UB report aborts
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Build liboracle.so, or with sanitize=True liboracle_san.so (load it
+    with DFS_ORACLE_LIB pointing at it and gcc's libasan preloaded)."""
+    out = SAN_LIB if sanitize else LIB
+    cmd = ["gcc", "-std=c11", "-O1" if sanitize else "-O2", "-fopenmp", "-ffp-contract=off",
+           "-fPIC", "-shared", "-Wall", "-Wextra", *(SAN_FLAGS if sanitize else []),
+           "-o", out + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv)

@@ -323,6 +323,18 @@ int64_t orc_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out,
 
 /* Z = X D in float64 (T x k row-major), Eq. (1) of [Review], i ascending.
  * Returns a malloc'ed array, or NULL on allocation failure. */
+/* A column-compressed index: colptr[0] = 0, colptr non-decreasing, and
+ * every stored row (or block of `rows_per` rows) below k. */
+static int csc_valid(int32_t k, int32_t d_out, const int32_t* colptr, const uint16_t* rowidx,
+                     int32_t rows_per) {
+  if (d_out < 0 || colptr[0] != 0) return 0;
+  for (int32_t j = 0; j < d_out; ++j)
+    if (colptr[j + 1] < colptr[j]) return 0;
+  for (int32_t p = 0; p < colptr[d_out]; ++p)
+    if ((int64_t)rowidx[p] * rows_per >= k) return 0;
+  return 1;
+}
+
 static double* compute_z(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_in, int32_t k,
                          const orc_tensor* D, int64_t ldd) {
   double* Z = (double*)malloc(sizeof(double) * (size_t)T * (size_t)k);
@@ -362,11 +374,14 @@ static double* compute_z(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_
  * (element (i,a) at flat index a*ldd + i).  C: k x d_out in CSC; with 8-bit
  * codes C_p = value(code_p) * col_scale[j], exact in float64.
  * Y: T x d_out row-major float64, leading dimension d_out.
- * Returns 0, or -1 on allocation failure. */
+ * Returns 0; -1 on allocation failure; -2 (nothing computed) if the CSC is
+ * not one: colptr[0] != 0, colptr decreasing somewhere, or a row index >= k.
+ */
 int orc_forward(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_in,
                 int32_t k, const orc_tensor* D, int64_t ldd, int32_t d_out,
                 const int32_t* colptr, const uint16_t* rowidx,
                 const orc_tensor* C, double* Y) {
+  if (!csc_valid(k, d_out, colptr, rowidx, 1)) return -2;
   if (T <= 0) return 0;
   double* Z = compute_z(T, X, ldx, d_in, k, D, ldd);
   if (!Z) return -1;
@@ -436,10 +451,13 @@ int64_t orc_pack_bcsc(const void* C, int32_t dtype, int32_t k, int32_t d_out, in
  *   Y[t,j] = sum over the kept blocks b of column j (ascending), over
  *            e = 0..7 with 8b+e < k, of Z[t, 8b+e] * vals[8 q + e]
  * (zeros inside a kept block included).  Z as in orc_forward.  C: the
- * values tensor (F32 or F16, 8 per kept block).  Returns 0 or -1. */
+ * values tensor (F32 or F16, 8 per kept block).  Returns 0, -1 on
+ * allocation failure, -2 if the block index is not one (as orc_forward,
+ * with block indices: 8 * bidx[q] < k). */
 int orc_forward_bcsc(int32_t T, const orc_tensor* X, int64_t ldx, int32_t d_in, int32_t k,
                      const orc_tensor* D, int64_t ldd, int32_t d_out, const int32_t* bcolptr,
                      const uint16_t* bidx, const orc_tensor* C, double* Y) {
+  if (!csc_valid(k, d_out, bcolptr, bidx, 8)) return -2;
   if (T <= 0) return 0;
   double* Z = compute_z(T, X, ldx, d_in, k, D, ldd);
   if (!Z) return -1;

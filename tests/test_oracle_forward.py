@@ -140,3 +140,21 @@ def test_zero_tokens():
     c = O.pack_csc(np.eye(4, dtype=np.float32))
     Y = O.forward(np.zeros((0, 8), np.float32), np.ones((4, 8), np.float32), 8, c)
     assert Y.shape == (0, 4)
+
+
+def test_forward_rejects_an_index_that_is_not_a_csc():
+    # The oracle indexes Z by the stored row: a row >= k, a decreasing
+    # colptr or colptr[0] != 0 is refused before anything is read.
+    rng = np.random.default_rng(7)
+    k, d_out, d_in = 16, 4, 32
+    D = rng.standard_normal((k, d_in)).astype(np.float32)
+    X = rng.standard_normal((2, d_in)).astype(np.float32)
+    good = O.CSC(k, d_out, np.array([0, 1, 2, 3, 4], np.int32), np.array([0, 5, 15, 3], np.uint16),
+                 np.ones(4, np.float32))
+    O.forward(X, D, d_in, good)  # the valid index runs
+    bad_row = O.CSC(k, d_out, good.colptr, np.array([0, 5, 16, 3], np.uint16), good.vals)
+    bad_order = O.CSC(k, d_out, np.array([0, 2, 1, 3, 4], np.int32), good.rowidx, good.vals)
+    bad_start = O.CSC(k, d_out, np.array([1, 1, 2, 3, 4], np.int32), good.rowidx, good.vals)
+    for c in (bad_row, bad_order, bad_start):
+        with pytest.raises(ValueError):
+            O.forward(X, D, d_in, c)
