@@ -38,19 +38,18 @@ N_REPLAYS = 11  # timed graph replays of the K steps; the headline is their medi
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 
 # HBM traffic of one launch of the dominant kernel, from two rocprofv3 --pmc passes over
-# `bench.py --steps 20 --warmup 2 --no-cpu --no-prefill --copy-calibration-mib 256`
+# `bench.py --steps 20 --warmup 2 --no-cpu --no-prefill --no-extras --copy-calibration-mib 256`
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the kernel's dispatches).
 # Each counter is scaled by what it reads for the plain 256 MiB device copy in the same
-# run (FETCH_SIZE reads 131087 KiB for 262144 KiB fetched: x2.0; WRITE_SIZE reads 262144
-# KiB: x1.0).  The figure holds only for the kernel source it was taken on: the digest
-# of the sources below must match, otherwise traffic is reported as null.
+# run (FETCH_SIZE reads 131086.5 KiB for 262144 KiB fetched: x1.99978; WRITE_SIZE reads
+# 262144 KiB: x1.0).  The figure holds only for the kernel source it was taken on: the
+# digest of the sources below must match, otherwise traffic is reported as null.
 TRAFFIC_SOURCES = ("dictionary_factored_sparse_amd/csrc/fused_decode.hip",
                    "dictionary_factored_sparse_amd/csrc/csc_chunks.hpp",
                    "dictionary_factored_sparse_amd/csrc/gemv_common.hpp",
-                   "dictionary_factored_sparse_amd/csrc/dfs_internal.hpp",
-                   "include/dictfs.h")
-TRAFFIC_MEASURED = {"digest": "d280bbd5ebbdb39678149db4b84540534e08699f7639c252ca58b5c5bcd1ef46",
-                    "fetch_kib": 18405.32, "write_kib": 152.0,
+                   "dictionary_factored_sparse_amd/csrc/dfs_internal.hpp")
+TRAFFIC_MEASURED = {"digest": "35e7300f8e80ba1d641f8b35d8436178728c3152b5981870e2466a1bf7782188",
+                    "fetch_kib": 18404.41, "write_kib": 152.0,
                     "fetch_scale": 1.99978, "write_scale": 1.0}
 
 
@@ -93,7 +92,95 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--profile-decode", default=None, metavar="D/C",
+                    help="only time the q_proj decode group with factors stored as D/C (f16, "
+                         "nvfp4; C also fp8, int8) and print one JSON line (for counter passes)")
     return ap.parse_args()
+
+
+def profile_decode(args):
+    """The q_proj decode group (one launch of the one-launch decode) with the
+    factor formats args.profile_decode, K graph-replayed steps over replicas
+    > 1.2 GB, N_REPLAYS timed replays; prints one JSON line.  Used by the
+    counter passes of other instantiations than the headline's."""
+    import numpy as np
+    import torch
+
+    from dictionary_factored_sparse_amd import binding as B
+    from dictionary_factored_sparse_amd import ledger as L
+    from dictionary_factored_sparse_amd import synth
+
+    dfmt, cfmt = args.profile_decode.split("/")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = synth.make_group("qproj")
+    D = B.to_device_dict(g.D, dev, nvfp4=dfmt == "nvfp4")
+    Cs = [B.to_device_csc(c, dev, fmt=None if cfmt == "f16" else cfmt) for c in g.Cs]
+    nb = L.group_bytes(d_in=g.d_in, d_out=g.d_out, k=g.k, T=1, nnzs=[c.nnz for c in Cs],
+                       wdtype=dfmt, cdtype=cfmt, xdtype="f16", ydtype="f16")
+    R = max(2, math.ceil(1.2e9 / nb))
+    reps = [(D, Cs)]
+    for _ in range(R - 1):
+        if D.nv is not None:
+            Dr = B.DeviceDict(D.d_in, D.k, nv=B.DeviceNVFP4(D.nv.codes.clone(), D.nv.scales.clone(),
+                                                            D.nv.ts.clone(), D.nv.n))
+        else:
+            Dr = B.DeviceDict(D.d_in, D.k, data=D.data.clone())
+        Cr = []
+        for c in Cs:
+            if c.nv is not None:
+                Cr.append(B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
+                                      nv=B.DeviceNVFP4(c.nv.codes.clone(), c.nv.scales.clone(),
+                                                       c.nv.ts.clone(), c.nv.n)))
+            elif c.codes8 is not None:
+                Cr.append(B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
+                                      codes8=c.codes8.clone(), col_scale=c.col_scale.clone(),
+                                      code_kind=c.code_kind))
+            else:
+                Cr.append(B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
+                                      vals=c.vals.clone()))
+        reps.append((Dr, Cr))
+    Xs = [torch.from_numpy(X).to(dev) for X in g.Xs]
+    Ys = [torch.empty(1, g.d_out, dtype=torch.float16, device=dev) for _ in Xs]
+    ws = B.workspace(2, 1, D, Cs[0], dev)
+
+    def step(i):
+        B.dict_group_forward(Xs, reps[i % R][0], reps[i % R][1], Ys=Ys, ws=ws)
+    K = args.steps
+    gr = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        for i in range(K):
+            step(i)
+    for _ in range(max(1, args.warmup // max(K, 1) + 1)):
+        gr.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    us = []
+    for _ in range(N_REPLAYS):
+        torch.cuda.synchronize()
+        e0.record()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) / K * 1e3)
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    med = float(np.median(us))
+    print(json.dumps({"profile_decode": args.profile_decode, "workload": "q_proj decode group",
+                      "bytes_per_launch": nb, "us_median": round(med, 3),
+                      "us_p10": round(float(np.percentile(us, 10)), 3),
+                      "us_p90": round(float(np.percentile(us, 90)), 3),
+                      "GBs": round(nb / med / 1e3, 1), "replays": N_REPLAYS, "steps_each": K}),
+          flush=True)
 
 
 def _log(*a):
@@ -107,6 +194,10 @@ def main():
         print("bench.py runs on exactly one GPU: the factored projection is measured on one "
               "MI355X, and no multi-GPU path is built; --gpus must be 1.", flush=True)
         sys.exit(2)
+
+    if args.profile_decode:
+        profile_decode(args)
+        return
 
     import numpy as np
     import torch
