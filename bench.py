@@ -666,19 +666,43 @@ def main():
 
         def zc_b(i):
             B.dict_zc_forward(Z, 1, rpb[i % nrep_b][1], Ys=Ydb)
-        t_b = timed_graph(step_b, K)
+        t_b = timed_graph(step_b, K)  # one launch (the block consume path)
+        os.environ["DFS_DECODE_PATH"] = "two"
+        t_b2 = timed_graph(step_b, K)
+        os.environ.pop("DFS_DECODE_PATH")
         t_zb = timed_graph(zc_b, K)
+        assert B.workspace_error_word(wsb) == 0, "Z hand-off wait gave up"
+        # prefill at the same shape, 2 x 2048 tokens: the block SpMM alone
+        # (f16 Z) and the whole group forward (MFMA X D, then the SpMM)
+        Tp, nrp = 2048, min(nrep_b, 8)
+        Zpb = torch.randn(2 * Tp, g.k, dtype=torch.float16, device=dev) * 0.05
+        Xpb = [torch.randn(Tp, g.d_in, dtype=torch.float16, device=dev) for _ in range(2)]
+        Ypb = [torch.empty(Tp, g.d_out, dtype=torch.float16, device=dev) for _ in range(2)]
+        wspb = B.workspace(2, Tp, D0, Cbd[0], dev)
+
+        def zc_pb(i):
+            B.dict_zc_forward(Zpb, Tp, rpb[i % nrp][1], Ys=Ypb)
+
+        def fw_pb(i):
+            B.dict_group_forward(Xpb, rpb[i % nrp][0], rpb[i % nrp][1], Ys=Ypb, ws=wspb)
+        t_spmm_b = timed_graph(zc_pb, 10)
+        t_fw_b = timed_graph(fw_pb, 10)
+        nvals_b = 8 * sum(c.nnz for c in Cbd)  # values multiplied, zeros inside blocks included
         extras["block8_equal_bytes_qproj_group"] = {
             "block_density": round(qb, 4),
             "retained_values_vs_csc": round(qb * 8 * (g.k // 8) / (0.3 * g.k), 3),
             "csc": {"MB": round(step_bytes / 1e6, 2), "one_launch_us": round(ms_step * 1e3, 2),
                     "two_launch_us": round(us_two, 2), "zc_us": round(kern["spmv_csc"]["us"], 2)},
-            "block8": {"MB": round(byt_b / 1e6, 2), "two_launch_us": round(t_b, 2),
-                       "zc_us": round(t_zb, 2),
+            "block8": {"MB": round(byt_b / 1e6, 2), "one_launch_us": round(t_b, 2),
+                       "two_launch_us": round(t_b2, 2), "zc_us": round(t_zb, 2),
                        "zc_GB/s": round((byt_b - L.dict_bytes(g.d_in, g.k, "f16") - 2 * 2 * g.d_in)
-                                        / (t_zb * 1e-6) / 1e9, 1)},
+                                        / (t_zb * 1e-6) / 1e9, 1),
+                       "prefill_T2048_spmm_us": round(t_spmm_b, 1),
+                       "prefill_T2048_spmm_TFLOPs_stored_values": round(
+                           2 * Tp * nvals_b / (t_spmm_b * 1e-6) / 1e12, 2),
+                       "prefill_T2048_group_forward_us": round(t_fw_b, 1)},
         }
-        del rpb, Cbd
+        del rpb, Cbd, Zpb, Xpb, Ypb, wspb
         torch.cuda.empty_cache()
         _log(f"block8 at equal bytes: {extras['block8_equal_bytes_qproj_group']}")
 

@@ -213,8 +213,10 @@ dfs_status run_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64
 dfs_status run_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc* C,
                   void* const* Y, int32_t ydt, int64_t ldy, hipStream_t s) {
   ZcLaunch a = make_zc(n, Z, zdt, T, C, Y, ydt, ldy);
-  if (a.block_rows != 0)
-    DFS_HIP(launch_spmv_bcsc(a, s));  // T <= kGemvMaxRows (checked by the callers)
+  if (a.block_rows != 0 && T <= kGemvMaxRows)
+    DFS_HIP(launch_spmv_bcsc(a, s));
+  else if (a.block_rows != 0)
+    DFS_HIP(launch_spmm_bcsc(a, s));
   else if (T <= kGemvMaxRows)
     DFS_HIP(launch_spmv_csc(a, s));
   else
@@ -564,7 +566,6 @@ dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t
       return DFS_E_UNSUPPORTED;
   }
   if (!is_act_dtype(ydt)) return DFS_E_UNSUPPORTED;
-  if (C[0].block_rows != 0 && T > kGemvMaxRows) return DFS_E_UNSUPPORTED;
   if (T == 0) return DFS_OK;
   DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
   if (!Z) return DFS_E_INVALID;
@@ -587,8 +588,6 @@ dfs_status check_group(int32_t n_layers, const void* const* X, int32_t xdt, int3
       return DFS_E_UNSUPPORTED;
   }
   if (!is_act_dtype(xdt) || !is_act_dtype(ydt)) return DFS_E_UNSUPPORTED;
-  // block-structured coefficients: decode and small batches only
-  if (C[0].block_rows != 0 && (int64_t)n_layers * T > kGemvMaxRows) return DFS_E_UNSUPPORTED;
   if (T == 0) return DFS_OK;  // no rows: the activation pointers may be null
   DFS_TRY(check_x(X, n_layers, xdt, ldx, D->d_in));
   DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));

@@ -139,4 +139,25 @@ struct ValChunk<DFS_INT8> {
   }
 };
 
+// Block-structured support with f16 values (blocks of 8 consecutive atoms,
+// see dfs_csc): in the one-launch decode a lane's unit of the coefficient
+// stream is one kept block, its 16-bit block index and its 8 values.
+// kBlockF16 is a value-type code used only inside the kernels.
+constexpr int kBlockF16 = 16;
+
+template <>
+struct ValChunk<kBlockF16> {
+  u4 w;
+  uint32_t b;
+  __device__ __forceinline__ void load_block(const uint16_t* bidx, const void* vals, int64_t q) {
+    b = *gptr(bidx + q);
+    w = ld16<u4>((const uint16_t*)vals + 8 * q);
+  }
+  __device__ __forceinline__ void touch() {}
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+  }
+};
+
 }  // namespace dfs

@@ -200,8 +200,10 @@ hipError_t launch_pack_csc_count(const void* C, int32_t dtype, int32_t k, int32_
 hipError_t launch_pack_csc_scatter(const void* C, int32_t dtype, int32_t k, int32_t d_out,
                                    int64_t ldc, uint16_t* rowidx, void* vals, const void* ws,
                                    hipStream_t s, int block_rows = 0);
-// Y_l = Z_l C_l for block-structured C (T <= 16 tokens per layer)
+// Y_l = Z_l C_l for block-structured C: T <= 16 tokens per layer (SpMV),
+// and any T with the Z tile staged as f16 (SpMM)
 hipError_t launch_spmv_bcsc(const ZcLaunch& a, hipStream_t s);
+hipError_t launch_spmm_bcsc(const ZcLaunch& a, hipStream_t s);
 
 // 8-bit coefficient codes (FP8 / INT8), one scale per column
 size_t quant8_ws_bytes(int32_t d_out);

@@ -115,6 +115,24 @@ __device__ __forceinline__ float gather_chunk(const float* zl, IdxChunk ic, ValC
   return sum;
 }
 
+// sum += Z[8b .. 8b + 7] . v for one kept block at position q of a column
+// whose blocks lie in [s, e) (block-structured coefficients): the block's 8
+// Z words are contiguous in LDS, two 16-byte reads.  A block outside the
+// column (or not loaded) reads block 0 and adds nothing.
+__device__ __forceinline__ float gather_block(const float* zl, const ValChunk<kBlockF16>& vc,
+                                              int q, int s, int e, float sum) {
+  const bool ok = (uint32_t)(q - s) < (uint32_t)(e - s);
+  const float* zb = zl + 8 * (ok ? vc.b : 0u);
+  const f4 z0 = *reinterpret_cast<const f4*>(zb);
+  const f4 z1 = *reinterpret_cast<const f4*>(zb + 4);
+  float d = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d = __builtin_fmaf(z0[i], vc.get(i), d);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d = __builtin_fmaf(z1[i], vc.get(4 + i), d);
+  return sum + (ok ? d : 0.0f);
+}
+
 // Kernel arguments, compact so that they fit a few scalar-cache lines: the
 // first line holds everything the first loads need.  NU units (the outputs:
 // one coefficient matrix and Y each), 4 for one dictionary (one unit per
@@ -173,6 +191,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   using Cf = Cfg<DT, DFS_F16, RT>;
   using CE_t = ColEntry<VT>;
   constexpr bool Q8 = kIsCode8<VT>;
+  constexpr bool BLK = VT == kBlockF16;  // 8-atom blocks: a lane's unit is one block
   constexpr int CE = Cf::CE, SEGC = Cf::SEGC, SEG = Cf::SEG;
   constexpr int NU = units_of<ND>(), kTable = table_bytes_of<ND>();
   // Rounds of columns in flight before Z is received, and chunks per lane
@@ -180,7 +199,10 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   // over two layers: three rounds), so all three go out ahead, with batches
   // of 5 chunks (640 entries per column) to fit the registers.
   constexpr int NB = ND > 1 ? 3 : 2;
-  constexpr int KU = ND > 1 ? 5 : kU;
+  // 8-atom blocks: 9 blocks per lane per batch (the registers of 6 chunks)
+  constexpr int KU = BLK ? 9 : (ND > 1 ? 5 : kU);
+  // positions a lane's batch entries are apart, and the lane's first one
+  constexpr int STEP = BLK ? 16 : 128;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   LayerRow* lt = reinterpret_cast<LayerRow*>(smem);            // [NU]
   CE_t* cse = reinterpret_cast<CE_t*>(smem + kTable);          // [ncols]
@@ -410,15 +432,20 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
   // an exact count of these loads (the Z polls issued after them wait for
   // all of them), and skipping the lanes past the column's end saves their
   // share of the memory pipeline.
+  auto lane_first = [&](int s0) -> int { return BLK ? s0 + g : (s0 & ~7) + g * 8; };
   auto load_chunks = [&](IdxChunk* ic, ValChunk<VT>* vc, int s0, int e0, const uint16_t* rowidx,
                          const void* vals, const uint8_t* vsc) {
-    const int p0 = (s0 & ~7) + g * 8;
+    const int p0 = lane_first(s0);
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int p = p0 + 128 * u;
+      const int p = p0 + STEP * u;
       if (p < e0) {
-        ic[u].load(rowidx, p);
-        vc[u].load(vals, vsc, p);
+        if constexpr (BLK) {
+          vc[u].load_block(rowidx, vals, p);
+        } else {
+          ic[u].load(rowidx, p);
+          vc[u].load(vals, vsc, p);
+        }
       }
     }
   };
@@ -547,11 +574,17 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
     }
     const float* zl = zs + l * k;
     float sum = 0.0f;
-    int p0 = (s & ~7) + g * 8;
+    int p0 = lane_first(s);
+    auto gather = [&](const IdxChunk& ic1, const ValChunk<VT>& vc1, int p, float acc) {
+      if constexpr (BLK)
+        return gather_block(zl, vc1, p, s, e, acc);
+      else
+        return gather_chunk<VT>(zl, ic1, vc1, p, s, e, acc);
+    };
 #pragma unroll
-    for (int u = 0; u < KU; ++u) sum = gather_chunk<VT>(zl, ic[u], vc[u], p0 + 128 * u, s, e, sum);
+    for (int u = 0; u < KU; ++u) sum = gather(ic[u], vc[u], p0 + STEP * u, sum);
     // columns longer than one batch continue with plain loads
-    p0 += 128 * KU;
+    p0 += STEP * KU;
     if (p0 < e) {
       const LayerRow& L = lt[l];
       while (p0 < e) {
@@ -559,14 +592,17 @@ __global__ __launch_bounds__(kFT, 1) void fused_decode_kernel(FusedArgs<units_of
         ValChunk<VT> tv[KU];
 #pragma unroll
         for (int u = 0; u < KU; ++u)
-          if (p0 + 128 * u < e) {
-            tc[u].load(L.rowidx, p0 + 128 * u);
-            tv[u].load(L.vals, L.vsc, p0 + 128 * u);
+          if (p0 + STEP * u < e) {
+            if constexpr (BLK) {
+              tv[u].load_block(L.rowidx, L.vals, p0 + STEP * u);
+            } else {
+              tc[u].load(L.rowidx, p0 + STEP * u);
+              tv[u].load(L.vals, L.vsc, p0 + STEP * u);
+            }
           }
 #pragma unroll
-        for (int u = 0; u < KU; ++u)
-          sum = gather_chunk<VT>(zl, tc[u], tv[u], p0 + 128 * u, s, e, sum);
-        p0 += 128 * KU;
+        for (int u = 0; u < KU; ++u) sum = gather(tc[u], tv[u], p0 + STEP * u, sum);
+        p0 += STEP * KU;
       }
     }
     sum = row16_sum(sum);
@@ -734,6 +770,7 @@ hipError_t launch2(ArgsFor<1> f, const Plan& p, hipStream_t s) {
 template <int DT>
 hipError_t launch1(ArgsFor<1> f, const Plan& p, int vdt, hipStream_t s) {
   switch (vdt) {
+    case kBlockF16: return launch2<DT, kBlockF16>(f, p, s);
     case DFS_NVFP4: return launch2<DT, DFS_NVFP4>(f, p, s);
     case DFS_FP8: return launch2<DT, DFS_FP8>(f, p, s);
     case DFS_INT8: return launch2<DT, DFS_INT8>(f, p, s);
@@ -801,7 +838,10 @@ ArgsFor<ND> make_args(const XdLaunch& xd, const ZcLaunch& zc, uint8_t* tagged, u
 
 bool fused_decode_supported(const XdLaunch& xd, const ZcLaunch& zc) {
   if (xd.T != 1 || zc.T != 1) return false;
-  if (zc.block_rows != 0) return false;  // block-structured C: two-launch path
+  // block-structured C: f16 values, 8-atom blocks that never cross k
+  if (zc.block_rows != 0 && (zc.block_rows != 8 || zc.vdt != DFS_F16 || xd.k % 8 != 0 ||
+                             xd.n_dicts > 1))
+    return false;
   if (xd.n_layers < 1 || xd.n_layers > kFusedMaxLayers) return false;
   if (zc.n_layers < 1 || zc.n_layers > kFusedMaxUnits) return false;
   if (xd.xdt != DFS_F16) return false;
@@ -823,7 +863,8 @@ hipError_t launch_fused_decode(const XdLaunch& xd, const ZcLaunch& zc, uint8_t* 
   switch (p.ND) {
     case 1: {
       const ArgsFor<1> f = make_args<1>(xd, zc, tagged, ctrl);
-      return nv ? launch1<DFS_NVFP4>(f, p, zc.vdt, s) : launch1<DFS_F16>(f, p, zc.vdt, s);
+      const int vt = zc.block_rows != 0 ? kBlockF16 : zc.vdt;
+      return nv ? launch1<DFS_NVFP4>(f, p, vt, s) : launch1<DFS_F16>(f, p, vt, s);
     }
     case 2: {
       const ArgsFor<2> f = make_args<2>(xd, zc, tagged, ctrl);

@@ -11,6 +11,14 @@
 // Mapping as in the unstructured SpMV: a 16-lane DPP row per column, lane g
 // taking the column's blocks g, g + 16, ...; a workgroup stages a token tile
 // of Z (fp32, [k8][TT], rows past k zero) once for a run of column groups.
+//
+// Many tokens (prefill, spmm_bcsc_kernel) map as in the unstructured SpMM: a
+// workgroup owns a tile of up to 32 tokens and a block of columns, staged as
+// f16 Z [k8 + 8][TT] (rows from k on are zero; block k8 / 8 is all zero and
+// serves masked blocks); LPC lanes per column, each with NT = TT / LPC of the
+// tokens.  For every kept block a lane reads its NT tokens of the block's 8
+// contiguous Z rows and does 8 NT multiply-adds (f16 Z, f32 value and sum):
+// 2 bytes of LDS per multiply-add, and no index per entry.
 #include "dfs_internal.hpp"
 
 namespace dfs {
@@ -174,10 +182,209 @@ hipError_t launch1(const ZcLaunch& a, hipStream_t s) {
   return a.zdt == DFS_F32 ? launch2<VT, DFS_F32>(a, s) : launch2<VT, DFS_F16>(a, s);
 }
 
+// ---------------------------------------------------------------- many tokens
+
+constexpr int kThM = 1024;  // threads of the block SpMM (four waves per SIMD)
+constexpr int kUM = 4;      // blocks per batch, two batches in flight
+
+template <int TT>
+struct BSplit {
+  static constexpr int LPC = TT > 16 ? TT / 16 : 1;  // lanes per column
+  static constexpr int NT = TT / LPC;                // tokens per lane
+  static constexpr int CPB = kThM / LPC;             // columns per workgroup
+};
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+// NT f16 tokens of one Z row from LDS (16-byte pieces; 8 bytes for NT = 4)
+template <int NT>
+struct ZTok {
+  h8 v[NT / 8];
+  __device__ __forceinline__ void read(const _Float16* p) {
+#pragma unroll
+    for (int i = 0; i < NT / 8; ++i) v[i] = *reinterpret_cast<const h8*>(p + 8 * i);
+  }
+  __device__ __forceinline__ float get(int t) const { return (float)v[t / 8][t % 8]; }
+};
+template <>
+struct ZTok<4> {
+  h4 v;
+  __device__ __forceinline__ void read(const _Float16* p) { v = *reinterpret_cast<const h4*>(p); }
+  __device__ __forceinline__ float get(int t) const { return (float)v[t]; }
+};
+
+// Z rows [row0, row0 + rows) (tokens) into the f16 tile [k8 + 8][TT]; atoms
+// from k on, and tokens past `rows`, are zero.
+template <int ZT, int TT>
+__device__ __forceinline__ void stage_zb(_Float16* zt, const void* Z, int64_t row0, int rows,
+                                         int k, int k8) {
+  constexpr int kGroups = kThM / TT;
+  const int t = threadIdx.x % TT;
+  const bool live = t < rows;
+  const int64_t zrow = (row0 + (live ? t : 0)) * k;
+  if (k % 8 == 0) {
+    for (int a0 = (threadIdx.x / TT) * 8; a0 < k; a0 += kGroups * 8) {
+      float v[8];
+      if constexpr (ZT == DFS_F32) {
+        const u4 w0 = ld16<u4>((const float*)Z + zrow + a0);
+        const u4 w1 = ld16<u4>((const float*)Z + zrow + a0 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = __uint_as_float(w0[i]);
+          v[4 + i] = __uint_as_float(w1[i]);
+        }
+      } else {
+        const h8 h = __builtin_bit_cast(h8, ld16<u4>((const _Float16*)Z + zrow + a0));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zt[(a0 + i) * TT + t] = live ? (_Float16)v[i] : (_Float16)0.0f;
+    }
+  } else {
+    for (int a = threadIdx.x / TT; a < k; a += kGroups) {
+      const float v = ZT == DFS_F32 ? ((const float*)Z)[zrow + a] : (float)((const _Float16*)Z)[zrow + a];
+      zt[a * TT + t] = live ? (_Float16)v : (_Float16)0.0f;
+    }
+  }
+  for (int i = threadIdx.x; i < (k8 + 8 - k) * TT; i += kThM) zt[k * TT + i] = (_Float16)0.0f;
+}
+
+template <int VT, int ZT, int TT>
+__global__ __launch_bounds__(kThM) void spmm_bcsc_kernel(ZcLaunch a) {
+  constexpr int LPC = BSplit<TT>::LPC, NT = BSplit<TT>::NT, CPB = BSplit<TT>::CPB;
+  extern __shared__ __attribute__((aligned(16))) char zraw[];
+  _Float16* zt = reinterpret_cast<_Float16*>(zraw);
+  const int layer = blockIdx.z;
+  const int t0 = blockIdx.y * TT;
+  const int k = a.k, k8 = (k + 7) / 8 * 8;
+  const int rows = a.T - t0 < TT ? a.T - t0 : TT;
+  const int sub = threadIdx.x % LPC;
+  const int col = blockIdx.x * CPB + threadIdx.x / LPC;
+  const bool col_ok = col < a.d_out;
+  const int64_t nblk = a.nnz[layer];
+  int s = 0, e = 0;
+  if (col_ok) {  // clamped to [0, nblk], as in the SpMV
+    s = (int)min<int64_t>(max(a.colptr[layer][col], 0), nblk);
+    e = (int)min<int64_t>(max(a.colptr[layer][col + 1], s), nblk);
+  }
+  const uint16_t* bidx = a.rowidx[layer];
+  const void* vals = a.vals[layer];
+  // lanes past their column's end reload its last block, masked (the arrays
+  // hold at least 8 blocks, so block 0 serves empty columns)
+  const int64_t lastb = e > 0 ? e - 1 : 0;
+  const uint32_t zero_blk = (uint32_t)(k8 / 8);  // rows k8 .. k8 + 7: all zero
+
+  uint32_t ba[kUM], bb[kUM];
+  BlockVals<VT> va[kUM], vb[kUM];
+  auto load = [&](uint32_t* b, BlockVals<VT>* v, int p) {
+#pragma unroll
+    for (int u = 0; u < kUM; ++u) {
+      const int64_t q = min<int64_t>(p + u, lastb);
+      b[u] = *gptr(bidx + q);
+      v[u].load(vals, q);
+    }
+  };
+  int p = s;
+  load(ba, va, p);  // in flight while the tile is staged
+  stage_zb<ZT, TT>(zt, a.Z, (int64_t)layer * a.T + t0, rows, k, k8);
+  __syncthreads();
+
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+  const _Float16* zl = zt + sub * NT;
+  auto consume = [&](const uint32_t* b, const BlockVals<VT>* v, int pb) {
+#pragma unroll
+    for (int u = 0; u < kUM; ++u) {
+      const bool ok = pb + u < e;
+      // a block index past the last block reads the zero block
+      const uint32_t blk = ok ? min(b[u], zero_blk) : zero_blk;
+      const _Float16* zr = zl + blk * 8 * TT;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        ZTok<NT> z;
+        z.read(zr + r * TT);
+        const float c = ok ? v[u].get(r) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(z.get(t), c, acc[t]);
+      }
+    }
+  };
+  // two register buffers with static names: the next batch is in flight
+  // while the current one is consumed
+  while (p < e) {
+    load(bb, vb, p + kUM);
+    consume(ba, va, p);
+    p += kUM;
+    if (p >= e) break;
+    load(ba, va, p + kUM);
+    consume(bb, vb, p);
+    p += kUM;
+  }
+  if (col_ok) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int t = sub * NT + i;
+      if (t < rows) {
+        const int64_t o = (int64_t)(t0 + t) * a.ldy + col;
+        if (a.ydt == DFS_F16)
+          ((_Float16*)a.Y[layer])[o] = (_Float16)acc[i];
+        else
+          ((float*)a.Y[layer])[o] = acc[i];
+      }
+    }
+  }
+}
+
+template <int VT, int ZT, int TT>
+hipError_t launch_m3(const ZcLaunch& a, hipStream_t s) {
+  const int k8 = (a.k + 7) / 8 * 8;
+  const size_t smem = (size_t)(k8 + 8) * TT * 2;
+  auto kern = spmm_bcsc_kernel<VT, ZT, TT>;
+  if (smem > 64 * 1024) {
+    hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (err != hipSuccess) return err;
+  }
+  constexpr int CPB = BSplit<TT>::CPB;
+  dim3 grid((a.d_out + CPB - 1) / CPB, (a.T + TT - 1) / TT, a.n_layers);
+  hipLaunchKernelGGL(kern, grid, dim3(kThM), smem, s, a);
+  return hipGetLastError();
+}
+
+// Largest token tile (32, 16, 8 or 4) whose f16 Z tile [k8 + 8][TT] fits in
+// 144 KiB (k <= 16384 fits at TT = 4).
+int bcsc_mm_token_tile(int k) {
+  const int k8 = (k + 7) / 8 * 8;
+  int tt = 32;
+  while (tt > 4 && (size_t)(k8 + 8) * tt * 2 > 144 * 1024) tt /= 2;
+  return tt;
+}
+
+template <int VT, int ZT>
+hipError_t launch_m2(const ZcLaunch& a, hipStream_t s) {
+  switch (bcsc_mm_token_tile(a.k)) {
+    case 32: return launch_m3<VT, ZT, 32>(a, s);
+    case 16: return launch_m3<VT, ZT, 16>(a, s);
+    case 8: return launch_m3<VT, ZT, 8>(a, s);
+    default: return launch_m3<VT, ZT, 4>(a, s);
+  }
+}
+
+template <int VT>
+hipError_t launch_m1(const ZcLaunch& a, hipStream_t s) {
+  return a.zdt == DFS_F32 ? launch_m2<VT, DFS_F32>(a, s) : launch_m2<VT, DFS_F16>(a, s);
+}
+
 }  // namespace
 
 hipError_t launch_spmv_bcsc(const ZcLaunch& a, hipStream_t s) {
   return a.vdt == DFS_F32 ? launch1<DFS_F32>(a, s) : launch1<DFS_F16>(a, s);
+}
+
+hipError_t launch_spmm_bcsc(const ZcLaunch& a, hipStream_t s) {
+  return a.vdt == DFS_F32 ? launch_m1<DFS_F32>(a, s) : launch_m1<DFS_F16>(a, s);
 }
 
 }  // namespace dfs

@@ -263,7 +263,7 @@ def test_block_csc_validation():
     assert _group(Cs=[_csc(dtype=B.DFS_F16)]) != UNSUPPORTED
     blk = B.Csc(128, 64, 100, B.DFS_F16, 8, P, P, P, B.NV(), None, 104)
     assert _group(Cs=[blk], T=0) == OK
-    assert _group(Cs=[blk], T=17) == UNSUPPORTED          # decode / small batch only
+    assert _group(Cs=[blk], T=17, ws=P + 8) == ALIGN      # any batch: SpMV or SpMM
     bad = B.Csc(128, 64, 100, B.DFS_F16, 4, P, P, P, B.NV(), None, 104)
     assert _group(Cs=[bad]) == UNSUPPORTED                # blocks of 8 only
     nvb = B.Csc(128, 64, 100, B.DFS_NVFP4, 8, P, P, None, B.NV(P, P, P), None, 104)
