@@ -41,15 +41,15 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0
 # `bench.py --steps 20 --warmup 2 --no-cpu --no-prefill --no-extras --copy-calibration-mib 256`
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the kernel's dispatches).
 # Each counter is scaled by what it reads for the plain 256 MiB device copy in the same
-# run (FETCH_SIZE reads 131086.5 KiB for 262144 KiB fetched: x1.99978; WRITE_SIZE reads
+# run (FETCH_SIZE reads 131086.5 KiB for 262144 KiB fetched: x1.99979; WRITE_SIZE reads
 # 262144 KiB: x1.0).  The figure holds only for the kernel source it was taken on: the
 # digest of the sources below must match, otherwise traffic is reported as null.
 TRAFFIC_SOURCES = ("dictionary_factored_sparse_amd/csrc/fused_decode.hip",
                    "dictionary_factored_sparse_amd/csrc/csc_chunks.hpp",
                    "dictionary_factored_sparse_amd/csrc/gemv_common.hpp",
                    "dictionary_factored_sparse_amd/csrc/dfs_internal.hpp")
-TRAFFIC_MEASURED = {"digest": "35e7300f8e80ba1d641f8b35d8436178728c3152b5981870e2466a1bf7782188",
-                    "fetch_kib": 18404.41, "write_kib": 152.0,
+TRAFFIC_MEASURED = {"digest": "94ea249bef712e79a7bec97e67276523acc46fea39b06d5a942cdb44f900e925",
+                    "fetch_kib": 18421.90, "write_kib": 152.0,
                     "fetch_scale": 1.99978, "write_scale": 1.0}
 
 

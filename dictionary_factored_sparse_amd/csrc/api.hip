@@ -213,11 +213,15 @@ dfs_status run_xd(int32_t n, const void* const* X, int32_t xdt, int32_t T, int64
 dfs_status run_zc(int32_t n, const void* Z, int32_t zdt, int32_t T, const dfs_csc* C,
                   void* const* Y, int32_t ydt, int64_t ldy, hipStream_t s) {
   ZcLaunch a = make_zc(n, Z, zdt, T, C, Y, ydt, ldy);
-  if (a.block_rows != 0 && T <= kGemvMaxRows)
+  // fp32 Z (fp32 activations or dictionary) stays fp32 in LDS: the SpMVs,
+  // which pass over the tokens in fp32 tiles, serve any T; the SpMMs stage
+  // f16 tiles and take only f16 Z (the MFMA path's)
+  const bool spmv = T <= kGemvMaxRows || zdt == DFS_F32;
+  if (a.block_rows != 0 && spmv)
     DFS_HIP(launch_spmv_bcsc(a, s));
   else if (a.block_rows != 0)
     DFS_HIP(launch_spmm_bcsc(a, s));
-  else if (T <= kGemvMaxRows)
+  else if (spmv)
     DFS_HIP(launch_spmv_csc(a, s));
   else
     DFS_HIP(launch_spmm_csc(a, s));

@@ -185,8 +185,9 @@ int gemm_split_k(int64_t rows, int n_atoms, int d_in);
 hipError_t launch_nvfp4_to_f16(const uint8_t* codes, const uint8_t* scales, const float* ts,
                                int64_t n, _Float16* out, hipStream_t s);
 hipError_t launch_spmv_csc(const ZcLaunch& a, hipStream_t s);
-// Tokens per LDS pass of the SpMV (power of two, <= 16, Z tile <= 64 KiB).
-int spmv_token_tile(int T, int k, bool* half);
+// Tokens per LDS pass of the SpMV (power of two, <= 16); *half: the tile is
+// f16 (never for fp32 Z).
+int spmv_token_tile(int T, int k, bool fp32_z, bool* half);
 hipError_t launch_spmm_csc(const ZcLaunch& a, hipStream_t s);
 // Tokens per workgroup tile of the SpMM (32, 16, 8 or 4; f16 Z tile <= 128 KiB).
 int spmm_token_tile(int k);

@@ -14,7 +14,8 @@
 // lane issuing the same loads (past its column it reloads the column's last
 // chunk, masked).  The first batch is issued before Z is staged into
 // LDS (C does not depend on Z).  The Z tile is [k][TT] fp32 (TT tokens per
-// pass), or f16 [k + 1][TT] when fp32 would not fit (see spmv_token_tile),
+// pass), or f16 [k + 1][TT] when fp32 would not fit and Z is f16 already
+// (see spmv_token_tile),
 // so that up to 16 tokens take one pass over C; the partial sums are
 // reduced over the 16 lanes of the row with DPP, in a fixed order.  A
 // workgroup serves a run of 16-column groups (about 512 workgroups per
@@ -378,7 +379,7 @@ hipError_t launch3(const ZcLaunch& a, hipStream_t s) {
 template <int VT, int ZT>
 hipError_t launch2(const ZcLaunch& a, hipStream_t s) {
   bool half = false;
-  const int tt = spmv_token_tile(a.T, a.k, &half);
+  const int tt = spmv_token_tile(a.T, a.k, ZT == DFS_F32, &half);
   switch (tt) {
     case 1:
       return launch3<VT, ZT, 1, false>(a, s);
@@ -403,8 +404,10 @@ hipError_t launch1(const ZcLaunch& a, hipStream_t s) {
 // Token tile of the SpMV: the smallest power of two covering T (at most 16),
 // staged as fp32 when that fits in 64 KiB of LDS, else as f16 (with a zero
 // row) when that fits in 144 KiB, else a smaller tile (fp32 at TT = 1 holds
-// any k <= 16384).
-int spmv_token_tile(int T, int k, bool* half) {
+// any k <= 16384).  fp32 Z (fp32 activations or dictionary) always keeps an
+// fp32 tile, so that such callers get Z unrounded: a smaller tile, and more
+// passes over C.
+int spmv_token_tile(int T, int k, bool fp32_z, bool* half) {
   int tt = 1;
   while (tt < T && tt < 16) tt *= 2;
   for (;;) {
@@ -412,7 +415,7 @@ int spmv_token_tile(int T, int k, bool* half) {
       *half = false;
       return tt;
     }
-    if (tt >= 4 && (size_t)(k + 1) * tt * 2 <= 144 * 1024) {
+    if (!fp32_z && tt >= 4 && (size_t)(k + 1) * tt * 2 <= 144 * 1024) {
       *half = true;
       return tt;
     }

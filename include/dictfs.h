@@ -30,7 +30,12 @@
  *     activations must be multiples of 8 elements and of f32 ones multiples of
  *     4, so that every row stays 16-byte aligned.
  *   - Accumulation is always fp32.  Results are deterministic run to run
- *     (no floating-point atomics).
+ *     (no floating-point atomics).  The intermediate Z = X D_g is held in
+ *     fp32 whenever X or D_g is fp32 (every path keeps it unrounded then);
+ *     with f16 X and an f16 or NVFP4 dictionary it is rounded to f16 where a
+ *     path stages it so: the MFMA product for more than 16 stacked rows, and
+ *     the f16 Z tiles the coefficient kernels use when an fp32 tile would
+ *     not fit their LDS.
  *   - Thread safety: calls hold no mutable global state beyond a per-thread
  *     last-HIP-error code; concurrent calls on different streams are safe
  *     when they do not share a workspace.  The one-launch decode runs one

@@ -129,3 +129,21 @@ def test_fp32_above_16_rows_with_the_queried_workspace(xdt, wdt):
     torch.cuda.synchronize()
     for l, ref in enumerate(oracle_group(g)):
         assert_close(Ys[l], ref, f"layer {l}")
+
+
+@pytest.mark.parametrize("d_in,k,T", [(256, 128, 32), (2048, 2048, 16), (2048, 2048, 40)])
+def test_fp32_z_keeps_its_range(d_in, k, T):
+    # fp32 activations scaled so that |Z| runs far above the f16 range
+    # (65504): every path keeps fp32 Z unrounded, in fp32 LDS tiles (T > 16,
+    # and T = 16 at k = 2048 where an f16 tile would otherwise be chosen)
+    say(f"case: fp32 group, |Z| > 65504, d_in={d_in} k={k} T={T}")
+    g = synth.make_group("tiny", d_in=d_in, k=k, T=T)
+    g.Xs = [np.ascontiguousarray(X * np.float32(1e5)) for X in g.Xs]
+    D, Cs, Xs = device_group(g)
+    ws = B.workspace(2, T, D, Cs[0], DEV)
+    Ys = B.dict_group_forward(Xs, D, Cs, ws=ws, ydtype=torch.float32)
+    torch.cuda.synchronize()
+    zmax = max(float(np.abs(X.astype(np.float64) @ g.D.astype(np.float64).T).max()) for X in g.Xs)
+    assert zmax > 65504.0
+    for l, ref in enumerate(oracle_group(g)):
+        assert_close(Ys[l], ref, f"layer {l}")
