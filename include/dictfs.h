@@ -211,8 +211,12 @@ dfs_status dict_pack_bcsc(const void* C, int32_t dtype, int32_t k, int32_t d_out
 /* Workspace bytes nvfp4_pack needs for n elements. */
 dfs_status nvfp4_pack_workspace_size(int64_t n, size_t* bytes);
 
-/* Quantise x[0..n) (fp32, device) to NVFP4 (see dfs_nvfp4).  Recipe, applied
- * with correctly rounded fp32 operations:
+/* Quantise x[0..n) (fp32, device) to NVFP4 (see dfs_nvfp4): 4-bit values
+ * with one 8-bit scale per block of sixteen ("DictLLM: Shared Dictionaries
+ * for Post-Training Compression", "From retained values to measured
+ * decoding"; the all-NVFP4 rows of the figures and tables page, Table 4).
+ * The pages do not print the scale recipe; the one used here, applied with
+ * correctly rounded fp32 operations:
  *   amax = max|x|;  ts = amax / 2688 (= 6 * 448), or 1 if that is 0;
  *   per block b: sf = amax_b / (6 * ts); scale code = E4M3 nearest to sf,
  *     ties to even, saturating at 448; s = its value; denom = s * ts;
@@ -223,8 +227,11 @@ dfs_status nvfp4_pack_workspace_size(int64_t n, size_t* bytes);
 dfs_status nvfp4_pack(const float* x, int64_t n, dfs_nvfp4 out, void* ws, size_t ws_bytes,
                       void* stream);
 
-/* Decode n NVFP4 elements to fp32: y[i] = (e2m1 * e4m3) * tensor_scale, one
- * fp32 rounding (the first product is exact). */
+/* Decode n NVFP4 elements to fp32 (the inverse of nvfp4_pack's encoding,
+ * same passages): y[i] = (e2m1(code_i) * e4m3(scale_{i/16})) * tensor_scale,
+ * one fp32 rounding (the first product is exact).  n = 0 is a no-op and
+ * n < 0 gives DFS_E_INVALID; in and y are device pointers owned by the
+ * caller; enqueued on `stream`. */
 dfs_status nvfp4_unpack(dfs_nvfp4 in, int64_t n, float* y, void* stream);
 
 /* ---------------------------------------------------------------------- */
