@@ -95,14 +95,20 @@ def _parse():
     ap.add_argument("--profile-decode", default=None, metavar="D/C",
                     help="only time the q_proj decode group with factors stored as D/C (f16, "
                          "nvfp4; C also fp8, int8) and print one JSON line (for counter passes)")
+    ap.add_argument("--profile-mlp", default=None, choices=("gate", "up", "down"),
+                    help="only time the MLP group of this projection type at 16 tokens and print "
+                         "one JSON line (for counter passes)")
     return ap.parse_args()
 
 
-def profile_decode(args):
-    """The q_proj decode group (one launch of the one-launch decode) with the
-    factor formats args.profile_decode, K graph-replayed steps over replicas
-    > 1.2 GB, N_REPLAYS timed replays; prints one JSON line.  Used by the
-    counter passes of other instantiations than the headline's."""
+def profile_group(args):
+    """One group forward, timed alone for the counter passes of kernels other
+    than the headline's: --profile-decode D/C times the q_proj decode group
+    (one launch of the one-launch decode) with the factors stored as D/C;
+    --profile-mlp P times the MLP group of projection type P (gate, up or
+    down; four layers, f16) at 16 tokens (split-K GEMM, its slice sum, the
+    16-token SpMV).  K graph-replayed steps over replicas > 1.2 GB, N_REPLAYS
+    timed replays; prints one JSON line."""
     import numpy as np
     import torch
 
@@ -110,13 +116,22 @@ def profile_decode(args):
     from dictionary_factored_sparse_amd import ledger as L
     from dictionary_factored_sparse_amd import synth
 
-    dfmt, cfmt = args.profile_decode.split("/")
+    if args.profile_decode:
+        dfmt, cfmt = args.profile_decode.split("/")
+        g, T = synth.make_group("qproj"), 1
+        label = {"profile_decode": args.profile_decode, "workload": "q_proj decode group"}
+    else:
+        dfmt, cfmt = "f16", "f16"
+        T = 16
+        g = synth.make_group("mlp", ptype=args.profile_mlp, T=T)
+        label = {"profile_mlp": args.profile_mlp,
+                 "workload": f"MLP {args.profile_mlp} group of 4, 16 tokens"}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    g = synth.make_group("qproj")
     D = B.to_device_dict(g.D, dev, nvfp4=dfmt == "nvfp4")
     Cs = [B.to_device_csc(c, dev, fmt=None if cfmt == "f16" else cfmt) for c in g.Cs]
-    nb = L.group_bytes(d_in=g.d_in, d_out=g.d_out, k=g.k, T=1, nnzs=[c.nnz for c in Cs],
+    n = len(Cs)
+    nb = L.group_bytes(d_in=g.d_in, d_out=g.d_out, k=g.k, T=T, nnzs=[c.nnz for c in Cs],
                        wdtype=dfmt, cdtype=cfmt, xdtype="f16", ydtype="f16")
     R = max(2, math.ceil(1.2e9 / nb))
     reps = [(D, Cs)]
@@ -140,9 +155,9 @@ def profile_decode(args):
                 Cr.append(B.DeviceCSC(c.k, c.d_out, c.nnz, c.colptr.clone(), c.rowidx.clone(),
                                       vals=c.vals.clone()))
         reps.append((Dr, Cr))
-    Xs = [torch.from_numpy(X).to(dev) for X in g.Xs]
-    Ys = [torch.empty(1, g.d_out, dtype=torch.float16, device=dev) for _ in Xs]
-    ws = B.workspace(2, 1, D, Cs[0], dev)
+    Xs = [torch.from_numpy(np.ascontiguousarray(X[:T])).to(dev) for X in g.Xs]
+    Ys = [torch.empty(T, g.d_out, dtype=torch.float16, device=dev) for _ in Xs]
+    ws = B.workspace(n, T, D, Cs[0], dev)
 
     def step(i):
         B.dict_group_forward(Xs, reps[i % R][0], reps[i % R][1], Ys=Ys, ws=ws)
@@ -175,8 +190,7 @@ def profile_decode(args):
             dst.copy_(src)
         torch.cuda.synchronize()
     med = float(np.median(us))
-    print(json.dumps({"profile_decode": args.profile_decode, "workload": "q_proj decode group",
-                      "bytes_per_launch": nb, "us_median": round(med, 3),
+    print(json.dumps({**label, "bytes_per_launch": nb, "us_median": round(med, 3),
                       "us_p10": round(float(np.percentile(us, 10)), 3),
                       "us_p90": round(float(np.percentile(us, 90)), 3),
                       "GBs": round(nb / med / 1e3, 1), "replays": N_REPLAYS, "steps_each": K}),
@@ -195,8 +209,8 @@ def main():
               "MI355X, and no multi-GPU path is built; --gpus must be 1.", flush=True)
         sys.exit(2)
 
-    if args.profile_decode:
-        profile_decode(args)
+    if args.profile_decode or args.profile_mlp:
+        profile_group(args)
         return
 
     import numpy as np

@@ -18,9 +18,9 @@
 // (see spmv_token_tile),
 // so that up to 16 tokens take one pass over C; the partial sums are
 // reduced over the 16 lanes of the row with DPP, in a fixed order.  A
-// workgroup serves a run of 16-column groups (about 512 workgroups per
-// launch), so one staging of Z serves many columns.
-// grid = (ceil(groups / groups per workgroup), n_layers).
+// workgroup serves an equal run of 4-column quads (256 or 512 workgroups
+// per launch), so one staging of Z serves many columns.
+// grid = (workgroups per layer, n_layers).
 #include "csc_chunks.hpp"
 
 namespace dfs {
@@ -177,7 +177,7 @@ __device__ __forceinline__ void stage_z(float* zs, const void* Z, int64_t row0, 
 template <int VT, int ZT, int TT, bool ZH>
 __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaunch a) {
   constexpr int NTH = threads_of<ZH, TT>();
-  constexpr int CPG = NTH / 16;  // columns per group: 4 per wave, one per DPP row
+  constexpr int NW = NTH / kWave;  // waves; each serves 4 columns (a quad) at a time
   constexpr int U = Unroll<VT, TT, ZH>::U;
   extern __shared__ __attribute__((aligned(16))) float zs[];  // [k][TT] fp32, or f16 (ZH)
   _Float16* zh = reinterpret_cast<_Float16*>(zs);
@@ -186,11 +186,16 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int g = lane & 15;
-  // this workgroup's run of column groups (CPG columns each), an equal share
-  // of the layer's groups: one staging of Z serves all of them
-  const int ngroups = (a.d_out + CPG - 1) / CPG;
-  const int gb = (int)((int64_t)blockIdx.x * ngroups / gridDim.x);
-  const int gend = (int)((int64_t)(blockIdx.x + 1) * ngroups / gridDim.x);
+  // this workgroup's run [qb, qe) of the layer's column quads, an equal
+  // share within one quad: one staging of Z serves all of them.  In step j
+  // wave w serves quad qb + j * NW + w, so the NW waves work on NW adjacent
+  // quads at a time, and in the last step only the waves with a quad left.
+  // (Whole groups of NW quads per workgroup gave some workgroups a third
+  // more quads than others: 48 against 32 in the MLP gate layer.)
+  const int nquads = (a.d_out + 3) / 4;
+  const int qb = (int)((int64_t)blockIdx.x * nquads / gridDim.x);
+  const int qe = (int)((int64_t)(blockIdx.x + 1) * nquads / gridDim.x);
+  const int nsteps = (qe - qb + NW - 1) / NW;
   const int64_t nnz = a.nnz[layer];
   const uint16_t* rowidx = a.rowidx[layer];
   const void* vals = a.vals[layer];
@@ -212,7 +217,8 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
   };
   auto col_of = [&](int cg) {
     Col c;
-    c.col = cg * CPG + wave * 4 + (lane >> 4);
+    const int quad = qb + cg * NW + wave;
+    c.col = quad < qe ? quad * 4 + (lane >> 4) : a.d_out;  // past the run: no column
     c.s = c.e = 0;
     c.cs = 1.0f;
     if (c.col < a.d_out) {  // clamp to [0, nnz]: a malformed colptr cannot index out of bounds
@@ -243,7 +249,7 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
   };
 
   for (int t0 = 0; t0 < a.T; t0 += TT) {
-    Col c = col_of(gb);
+    Col c = col_of(0);
     load_batch(ia, va, c, c.first);  // does not depend on Z: in flight while Z is staged
     if (t0 > 0) __syncthreads();
     const int rows = a.T - t0 < TT ? a.T - t0 : TT;
@@ -253,7 +259,7 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
       stage_z<ZT, TT>(zs, a.Z, (int64_t)layer * a.T + t0, rows, a.k);
     __syncthreads();
 
-    for (int cg = gb; cg < gend; ++cg) {
+    for (int cg = 0; cg < nsteps; ++cg) {
       float acc[TT];
 #pragma unroll
       for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
@@ -320,7 +326,7 @@ __global__ __launch_bounds__((threads_of<ZH, TT>())) void spmv_csc_kernel(ZcLaun
       }
       // the next group's first batch goes out before this group's reduction
       Col n = c;
-      if (cg + 1 < gend) {
+      if (cg + 1 < nsteps) {
         n = col_of(cg + 1);
         load_batch(ia, va, n, n.first);
       }
@@ -365,7 +371,7 @@ hipError_t launch3(const ZcLaunch& a, hipStream_t s) {
   }
   // a fixed number of workgroups (one per CU when the f16 tile limits the
   // CU to one workgroup, two per CU otherwise), split evenly over the
-  // layers; each stages Z once for an equal run of column groups
+  // layers; each stages Z once for an equal run of column quads
   constexpr int NTH = threads_of<ZH, TT>();
   const int ngroups = (a.d_out + NTH / 16 - 1) / (NTH / 16);
   const int target = ZH ? 256 : 512;
