@@ -311,7 +311,45 @@ def main():
     copy_gbs = 2 * (1 << 30) * 5 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
-    _log(f"step spread {step_stats}; 1 GiB copy {copy_gbs:.0f} GB/s")
+    # and its read rate (the decode only reads): the read probe over 1 GiB,
+    # two buffers in turn so that each read misses the caches, and over
+    # slices of one step's size, rotated through 2 GiB so that every slice is
+    # cold, captured and replayed like the step
+    rbuf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    rbuf.fill_(1)
+    pblocks = 1024
+    pout = torch.empty(pblocks * 256, dtype=torch.int32, device=dev)
+    halves = (rbuf[:1 << 30], rbuf[1 << 30:])
+    B.probe_read(halves[1], pblocks, out=pout)
+    rts = []
+    for i in range(10):
+        ev0.record()
+        B.probe_read(halves[i % 2], pblocks, out=pout)
+        ev1.record()
+        torch.cuda.synchronize()
+        rts.append(ev0.elapsed_time(ev1))
+    read_gbs = (1 << 30) / (float(np.median(rts)) * 1e-3) / 1e9
+    slice_b = (step_bytes + 4095) // 4096 * 4096
+    nslices = (2 << 30) // slice_b
+
+    def read_slice(i):
+        j = i % nslices
+        B.probe_read(rbuf[j * slice_b:(j + 1) * slice_b], pblocks, out=pout)
+    g_read = capture(read_slice, nslices)
+    g_read.replay()
+    slice_us = []
+    for _ in range(N_REPLAYS):
+        torch.cuda.synchronize()
+        ev0.record()
+        g_read.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        slice_us.append(ev0.elapsed_time(ev1) / nslices * 1e3)
+    read_slice_us = float(np.median(slice_us))
+    del g_read, rbuf, halves, pout
+    torch.cuda.empty_cache()
+    _log(f"step spread {step_stats}; 1 GiB copy {copy_gbs:.0f} GB/s; 1 GiB read {read_gbs:.0f} "
+         f"GB/s; step-sized read {read_slice_us:.2f} us")
 
     # eager launches (host launch path included), for information
     for i in range(W):
@@ -880,7 +918,13 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "us_per_launch": round(d["us"], 3), "bytes_per_launch": d["bytes"],
                      "measured_copy_GBs": round(copy_gbs, 1),
-                     "frac_of_measured_copy": round(d["gbs"] / copy_gbs, 4)},
+                     "frac_of_measured_copy": round(d["gbs"] / copy_gbs, 4),
+                     "measured_read_GBs": round(read_gbs, 1),
+                     "frac_of_measured_read": round(d["gbs"] / read_gbs, 4),
+                     "step_sized_read_us": round(read_slice_us, 3),
+                     "step_sized_read_bytes": slice_b,
+                     "frac_of_step_sized_read": round(read_slice_us * step_bytes / slice_b
+                                                      / d["us"], 4)},
         "step_stats": step_stats,
         "kernels": {n: {"us_per_launch": round(v["us"], 3), "GB/s": round(v["gbs"], 1)}
                     for n, v in kern.items()},

@@ -34,6 +34,7 @@ SYMBOLS = ("dict_pack_csc_workspace_size", "dict_pack_csc", "nvfp4_pack_workspac
            "dict_csc_quantize8_workspace_size", "dict_csc_quantize8",
            "dict_gram_inverse_workspace_size", "dict_gram_inverse", "dict_obs_prune",
            "dict_refit_workspace_size", "dict_refit", "dict_pack_bcsc", "dfs_probe_mfma",
+           "dfs_probe_read",
            "dict_multi_workspace_size", "dict_multi_forward", "dict_group_forward_noalloc")
 
 
@@ -101,6 +102,7 @@ def lib():
             "dict_refit_workspace_size": [i32, i32, psz],
             "dict_refit": [i32, i32, i32, vp, i64, vp, i64, C.c_float, vp, i64, vp, sz, vp],
             "dfs_probe_mfma": [i32, i32, vp, vp],
+            "dfs_probe_read": [vp, i64, i32, vp, vp],
             "dict_multi_workspace_size": [i32, i32, i32, C.POINTER(Dict), C.POINTER(Csc), psz],
             "dict_multi_forward": [i32, i32, C.POINTER(vp), i32, i32, i64, C.POINTER(Dict),
                                    C.POINTER(Csc), C.POINTER(vp), i32, i64, vp, sz, vp],
@@ -577,3 +579,16 @@ def probe_mfma(blocks: int, iters: int, device="cuda:0", out=None, stream=None):
 
 def probe_mfma_flop(blocks: int, iters: int) -> float:
     return float(blocks) * 4 * iters * 8 * 32768
+
+
+def probe_read(buf, blocks: int, out=None, stream=None):
+    """HBM read probe: reads every byte of the device tensor `buf` once
+    (blocks x 256 threads, grid-strided 16-byte words).  Returns the
+    per-thread XORs (blocks * 256 uint32 as int32); their XOR is the XOR of
+    every dword of buf."""
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
+    _check("dfs_probe_read", lib().dfs_probe_read(buf.data_ptr(), nbytes, blocks, out.data_ptr(),
+                                                  _stream(stream)))
+    return out

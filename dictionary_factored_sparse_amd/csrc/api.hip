@@ -303,6 +303,15 @@ dfs_status dfs_probe_mfma(int32_t blocks, int32_t iters, float* out, void* strea
   return DFS_OK;
 }
 
+dfs_status dfs_probe_read(const void* buf, int64_t bytes, int32_t blocks, uint32_t* out,
+                          void* stream) {
+  if (!buf || !out || blocks <= 0 || bytes <= 0) return DFS_E_INVALID;
+  if ((uintptr_t)buf % 16 != 0 || bytes % 16 != 0) return DFS_E_ALIGN;
+  if (blocks > (1 << 20)) return DFS_E_RANGE;
+  DFS_HIP(launch_read_probe(buf, bytes / 16, blocks, out, (hipStream_t)stream));
+  return DFS_OK;
+}
+
 int64_t dict_csc_capacity(int64_t nnz) {
   if (nnz < 8) return 8;
   return (nnz + 7) / 8 * 8;

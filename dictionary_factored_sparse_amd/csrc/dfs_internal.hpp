@@ -223,6 +223,8 @@ hipError_t launch_gemm_nt_f32(const float* A, int64_t lda, const float* B, int64
 size_t spd_inverse_ws_bytes(int n);
 // matrix-core probe (measurement support)
 hipError_t launch_mfma_peak(int32_t blocks, int32_t iters, float* out, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, int64_t n16, int32_t blocks, uint32_t* out,
+                             hipStream_t s);
 hipError_t launch_spd_inverse(float* A, int64_t lda, int n, void* ws, hipStream_t s);
 size_t obs_prune_smem(int k);
 hipError_t launch_obs_prune(const float* C, int64_t ldc, const float* P, int64_t ldp, int k,

@@ -425,6 +425,20 @@ int32_t dfs_version(void);
  * check it ran.  0 < blocks <= 2^20, iters > 0; enqueued on stream. */
 dfs_status dfs_probe_mfma(int32_t blocks, int32_t iters, float* out, void* stream);
 
+/* HBM read probe (measurement support, not a step of the method): reads the
+ * `bytes` bytes at buf (device memory, caller-owned, read only) once with
+ * blocks workgroups of 256 threads: thread t of the G = blocks * 256 threads
+ * reads the 16-byte words t, t + G, t + 2G, ..., and writes the XOR of the
+ * dwords it read to out[t] (device memory, G uint32, caller-owned; the XOR of
+ * all of out is the XOR of every dword of the buffer, which checks that each
+ * was read).  Timed by the caller on a buffer larger than the caches, it
+ * gives the rate at which the device reads HBM, the measured counterpart of
+ * the nominal 8 TB/s for the decode, which reads each factor byte once.
+ * buf 16-byte aligned, bytes a positive multiple of 16 (DFS_E_ALIGN),
+ * 0 < blocks <= 2^20; enqueued on stream. */
+dfs_status dfs_probe_read(const void* buf, int64_t bytes, int32_t blocks, uint32_t* out,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

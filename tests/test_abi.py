@@ -386,3 +386,15 @@ def test_noalloc_entry_point_rejects_before_any_launch():
     # 16 layers x 2048 tokens against k = 16384 atoms: a 1 GiB Z tile
     big = _dict(d_in=4096, k=16384, ldd=4096)
     assert na(n=16, T=2048, D=big, Cs=[_csc(k=16384) for _ in range(16)], ldx=4096) == WORKSPACE
+
+
+def test_read_probe_rejects_before_any_launch():
+    # dfs_probe_read checks its arguments on the host; none of these enqueue
+    L = B.lib()
+    assert L.dfs_probe_read(None, 4096, 4, P, None) == INVALID
+    assert L.dfs_probe_read(P, 4096, 4, None, None) == INVALID
+    assert L.dfs_probe_read(P, 0, 4, P, None) == INVALID
+    assert L.dfs_probe_read(P, 4096, 0, P, None) == INVALID
+    assert L.dfs_probe_read(P + 8, 4096, 4, P, None) == ALIGN
+    assert L.dfs_probe_read(P, 4100, 4, P, None) == ALIGN
+    assert L.dfs_probe_read(P, 4096, (1 << 20) + 1, P, None) == RANGE

@@ -25,3 +25,23 @@ def test_probe_mfma_runs_every_round(iters):
     assert torch.equal(out.double().sum(dim=1),
                        torch.full((6,), 196608.0 * iters, dtype=torch.float64, device=out.device))
     assert torch.equal(out, torch.full_like(out, 768.0 * iters))
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(16, 1), (4096, 3), (1 << 20, 64), ((1 << 20) + 48, 7)])
+def test_probe_read_reads_every_word(nbytes, blocks):
+    # the XOR of the per-thread outputs is the XOR of every dword of the
+    # buffer, so a word the probe skipped or read twice shows
+    say(f"case: read probe, {nbytes} bytes, {blocks} workgroups")
+    g = torch.Generator().manual_seed(nbytes + blocks)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int64, generator=g)
+    host = host.to(torch.int32)
+    buf = host.to("cuda:0")
+    out = B.probe_read(buf, blocks)
+    torch.cuda.synchronize()
+    got = 0
+    for v in out.cpu().numpy().view("uint32").tolist():
+        got ^= v
+    want = 0
+    for v in host.numpy().view("uint32").tolist():
+        want ^= v
+    assert got == want
