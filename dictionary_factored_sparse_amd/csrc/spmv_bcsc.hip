@@ -12,13 +12,19 @@
 // taking the column's blocks g, g + 16, ...; a workgroup stages a token tile
 // of Z (fp32, [k8][TT], rows past k zero) once for a run of column groups.
 //
-// Many tokens (prefill, spmm_bcsc_kernel) map as in the unstructured SpMM: a
-// workgroup owns a tile of up to 32 tokens and a block of columns, staged as
-// f16 Z [k8 + 8][TT] (rows from k on are zero; block k8 / 8 is all zero and
-// serves masked blocks); LPC lanes per column, each with NT = TT / LPC of the
-// tokens.  For every kept block a lane reads its NT tokens of the block's 8
-// contiguous Z rows and does 8 NT multiply-adds (f16 Z, f32 value and sum):
-// 2 bytes of LDS per multiply-add, and no index per entry.
+// Many tokens (prefill, spmm_bcsc_kernel): a workgroup owns a tile of up to
+// 32 tokens and a block of columns, staged token-major as f16 Z
+// [TT][k8 + 8] (atoms from k on are zero, so block k8 / 8 is all zero and
+// serves masked blocks); LPC lanes per column, each with NT = TT / LPC of
+// the tokens.  For every kept block a lane reads, for each of its tokens,
+// the block's 8 atoms as one 16-byte word and takes their dot product with
+// the block's 8 values: four v_dot2_f32_f16 (exact products, fp32 sum) for
+// f16 values, eight multiply-adds for f32.  2 bytes of LDS per
+// multiply-add, and no index per entry.  Token-major, the lanes of a wave
+// read at random block offsets of a row, so their 16-byte words spread over
+// the LDS banks; atom-major ([k8 + 8][TT], a block's 8 rows of 64 bytes at
+// a 512-byte aligned offset) the lanes' reads of one row fell into 2 of the
+// 16 bank windows.
 #include "dfs_internal.hpp"
 
 namespace dfs {
@@ -194,60 +200,47 @@ struct BSplit {
   static constexpr int CPB = kThM / LPC;             // columns per workgroup
 };
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-
-// NT f16 tokens of one Z row from LDS (16-byte pieces; 8 bytes for NT = 4)
-template <int NT>
-struct ZTok {
-  h8 v[NT / 8];
-  __device__ __forceinline__ void read(const _Float16* p) {
-#pragma unroll
-    for (int i = 0; i < NT / 8; ++i) v[i] = *reinterpret_cast<const h8*>(p + 8 * i);
-  }
-  __device__ __forceinline__ float get(int t) const { return (float)v[t / 8][t % 8]; }
-};
-template <>
-struct ZTok<4> {
-  h4 v;
-  __device__ __forceinline__ void read(const _Float16* p) { v = *reinterpret_cast<const h4*>(p); }
-  __device__ __forceinline__ float get(int t) const { return (float)v[t]; }
-};
-
-// Z rows [row0, row0 + rows) (tokens) into the f16 tile [k8 + 8][TT]; atoms
-// from k on, and tokens past `rows`, are zero.
+// Z rows [row0, row0 + rows) (tokens) into the f16 tile [TT][RS], RS = k8 + 8
+// atoms per token row; atoms from k on, and tokens past `rows`, are zero.
+// Thread i converts the 8 atoms i % (RS / 8) of token i / (RS / 8).
 template <int ZT, int TT>
-__device__ __forceinline__ void stage_zb(_Float16* zt, const void* Z, int64_t row0, int rows,
-                                         int k, int k8) {
-  constexpr int kGroups = kThM / TT;
-  const int t = threadIdx.x % TT;
-  const bool live = t < rows;
-  const int64_t zrow = (row0 + (live ? t : 0)) * k;
-  if (k % 8 == 0) {
-    for (int a0 = (threadIdx.x / TT) * 8; a0 < k; a0 += kGroups * 8) {
-      float v[8];
-      if constexpr (ZT == DFS_F32) {
-        const u4 w0 = ld16<u4>((const float*)Z + zrow + a0);
-        const u4 w1 = ld16<u4>((const float*)Z + zrow + a0 + 4);
+__device__ __forceinline__ void stage_zt(_Float16* zt, const void* Z, int64_t row0, int rows,
+                                         int k, int RS) {
+  const int G = RS / 8;  // 8-atom groups per token row
+  for (int i = threadIdx.x; i < TT * G; i += kThM) {
+    const int t = i / G, a0 = (i - t * G) * 8;
+    const int64_t zrow = (row0 + t) * k;
+    float v[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = __uint_as_float(w0[i]);
-          v[4 + i] = __uint_as_float(w1[i]);
+    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    if (t < rows && a0 < k) {
+      if (k % 8 == 0) {
+        if constexpr (ZT == DFS_F32) {
+          const u4 w0 = ld16<u4>((const float*)Z + zrow + a0);
+          const u4 w1 = ld16<u4>((const float*)Z + zrow + a0 + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = __uint_as_float(w0[j]);
+            v[4 + j] = __uint_as_float(w1[j]);
+          }
+        } else {
+          const h8 h = __builtin_bit_cast(h8, ld16<u4>((const _Float16*)Z + zrow + a0));
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = (float)h[j];
         }
       } else {
-        const h8 h = __builtin_bit_cast(h8, ld16<u4>((const _Float16*)Z + zrow + a0));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+        for (int j = 0; j < 8; ++j)
+          if (a0 + j < k)
+            v[j] = ZT == DFS_F32 ? ((const float*)Z)[zrow + a0 + j]
+                                 : (float)((const _Float16*)Z)[zrow + a0 + j];
       }
+    }
+    h8 h;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) zt[(a0 + i) * TT + t] = live ? (_Float16)v[i] : (_Float16)0.0f;
-    }
-  } else {
-    for (int a = threadIdx.x / TT; a < k; a += kGroups) {
-      const float v = ZT == DFS_F32 ? ((const float*)Z)[zrow + a] : (float)((const _Float16*)Z)[zrow + a];
-      zt[a * TT + t] = live ? (_Float16)v : (_Float16)0.0f;
-    }
+    for (int j = 0; j < 8; ++j) h[j] = (_Float16)v[j];
+    *reinterpret_cast<h8*>(zt + (int64_t)t * RS + a0) = h;
   }
-  for (int i = threadIdx.x; i < (k8 + 8 - k) * TT; i += kThM) zt[k * TT + i] = (_Float16)0.0f;
 }
 
 template <int VT, int ZT, int TT>
@@ -257,7 +250,7 @@ __global__ __launch_bounds__(kThM) void spmm_bcsc_kernel(ZcLaunch a) {
   _Float16* zt = reinterpret_cast<_Float16*>(zraw);
   const int layer = blockIdx.z;
   const int t0 = blockIdx.y * TT;
-  const int k = a.k, k8 = (k + 7) / 8 * 8;
+  const int k = a.k, k8 = (k + 7) / 8 * 8, RS = k8 + 8;
   const int rows = a.T - t0 < TT ? a.T - t0 : TT;
   const int sub = threadIdx.x % LPC;
   const int col = blockIdx.x * CPB + threadIdx.x / LPC;
@@ -287,27 +280,45 @@ __global__ __launch_bounds__(kThM) void spmm_bcsc_kernel(ZcLaunch a) {
   };
   int p = s;
   load(ba, va, p);  // in flight while the tile is staged
-  stage_zb<ZT, TT>(zt, a.Z, (int64_t)layer * a.T + t0, rows, k, k8);
+  stage_zt<ZT, TT>(zt, a.Z, (int64_t)layer * a.T + t0, rows, k, RS);
   __syncthreads();
 
   float acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-  const _Float16* zl = zt + sub * NT;
+  const _Float16* zl = zt + (int64_t)sub * NT * RS;
   auto consume = [&](const uint32_t* b, const BlockVals<VT>* v, int pb) {
 #pragma unroll
     for (int u = 0; u < kUM; ++u) {
       const bool ok = pb + u < e;
-      // a block index past the last block reads the zero block
+      // a block index past the last block reads the zero block, with zero
+      // values (the loaded ones may belong to another column)
       const uint32_t blk = ok ? min(b[u], zero_blk) : zero_blk;
-      const _Float16* zr = zl + blk * 8 * TT;
+      const _Float16* zr = zl + blk * 8;
+      if constexpr (VT == DFS_F16) {
+        h2 c[4];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        ZTok<NT> z;
-        z.read(zr + r * TT);
-        const float c = ok ? v[u].get(r) : 0.0f;
+        for (int q = 0; q < 4; ++q)
+          c[q] = __builtin_bit_cast(h2, ok ? v[u].w[q] : 0u);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(z.get(t), c, acc[t]);
+        for (int t = 0; t < NT; ++t) {
+          const h8 z = *reinterpret_cast<const h8*>(zr + t * RS);
+          float acc_t = acc[t];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc_t = __builtin_amdgcn_fdot2(h2{z[2 * q], z[2 * q + 1]}, c[q], acc_t, false);
+          acc[t] = acc_t;
+        }
+      } else {
+        float c[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) c[r] = ok ? v[u].get(r) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const h8 z = *reinterpret_cast<const h8*>(zr + t * RS);
+#pragma unroll
+          for (int r = 0; r < 8; ++r) acc[t] = __builtin_fmaf((float)z[r], c[r], acc[t]);
+        }
       }
     }
   };
@@ -340,7 +351,7 @@ __global__ __launch_bounds__(kThM) void spmm_bcsc_kernel(ZcLaunch a) {
 template <int VT, int ZT, int TT>
 hipError_t launch_m3(const ZcLaunch& a, hipStream_t s) {
   const int k8 = (a.k + 7) / 8 * 8;
-  const size_t smem = (size_t)(k8 + 8) * TT * 2;
+  const size_t smem = (size_t)TT * (k8 + 8) * 2;
   auto kern = spmm_bcsc_kernel<VT, ZT, TT>;
   if (smem > 64 * 1024) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -353,7 +364,7 @@ hipError_t launch_m3(const ZcLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Largest token tile (32, 16, 8 or 4) whose f16 Z tile [k8 + 8][TT] fits in
+// Largest token tile (32, 16, 8 or 4) whose f16 Z tile [TT][k8 + 8] fits in
 // 144 KiB (k <= 16384 fits at TT = 4).
 int bcsc_mm_token_tile(int k) {
   const int k8 = (k + 7) / 8 * 8;
