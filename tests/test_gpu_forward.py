@@ -289,6 +289,27 @@ def test_mfma_output_tile_forms(d_in, k, T):
             assert_close(Z[l * T:(l + 1) * T], zrefs[l], f"Z layer {l} {zdt}")
 
 
+@pytest.mark.parametrize("d_in,k,T,n", [(56, 40, 9, 2), (1032, 264, 20, 2), (2048, 2000, 32, 2),
+                                        (128, 100, 24, 2), (4104, 3072, 16, 4)])
+def test_mfma_few_rows(d_in, k, T, n):
+    """Z = X D on the MFMA path for 16 < n T <= 64 stacked rows: 64 x 64
+    tiles with K split into slices whose fp32 partials the slice sum adds (8
+    for k = 2000, none for d_in = 128, whose two K tiles make one slice).
+    Ragged atom tiles (k = 40, 100, 264, 2000), K tails of 8 (d_in = 56,
+    1032, 4104), f16 and f32 Z."""
+    say(f"case: MFMA Z for few rows, d_in={d_in}, k={k}, {n} x T={T}")
+    g = synth.make_group("qproj", d_in=d_in, d_out=64, k=k, T=T, n_layers=n)
+    assert g.k == k and g.D.shape == (k, d_in)
+    D, _, Xs = device_group(g)
+    eye = O.pack_csc(np.eye(g.k, dtype=np.float32))
+    zrefs = [O.forward(g.Xs[l], g.D, g.d_in, eye) for l in range(n)]
+    for zdt in (torch.float32, torch.float16):
+        Z = B.dict_xd_forward(Xs, D, zdtype=zdt)
+        torch.cuda.synchronize()
+        for l in range(n):
+            assert_close(Z[l * T:(l + 1) * T], zrefs[l], f"Z layer {l} {zdt}")
+
+
 def test_repeat_runs_are_bitwise_identical():
     say("case: determinism")
     for wl, T in (("qproj", 1), ("qproj", 64)):
