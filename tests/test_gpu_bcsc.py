@@ -114,12 +114,14 @@ def test_block_one_launch_decode(d_in, d_out, k, n):
                                                   (512, 300, 2048, 33, np.float16),
                                                   (256, 64, 72, 17, np.float32),
                                                   (2048, 512, 6000, 20, np.float16),
-                                                  (256, 100, 70, 20, np.float16)])
+                                                  (256, 100, 70, 20, np.float16),
+                                                  (256, 96, 16384, 20, np.float16)])
 def test_block_spmm_above_16_rows(d_in, d_out, k, T, dtype):
     # 2 x T stacked rows > 16: MFMA X D (f16 Z; VALU fp32 Z for f32 factors),
     # then the block SpMM over token tiles of up to 32 (ragged last tile;
-    # k = 6000 stages an 8-token tile; k = 70 ends in a block that reaches
-    # past k, whose atoms from k on are zero in the staged tile)
+    # k = 6000 stages an 8-token tile and k = 16384 a 4-token one; k = 70
+    # ends in a block that reaches past k, whose atoms from k on are zero in
+    # the staged tile)
     say(f"case: block-structured prefill d_in={d_in} d_out={d_out} k={k} T={T}")
     Dt, Cs, Xs = _group(d_in, d_out, k, T, 0.533, d_in + k + T, dtype=dtype)
     D = B.to_device_dict(Dt, DEV)

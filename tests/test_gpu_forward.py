@@ -223,6 +223,16 @@ def _wide_dictionary_group(seed, d_in, d_out, k, T, n, density):
         assert_close(Ys[l], refs[l], f"k={k} T={T} layer {l}")
 
 
+@pytest.mark.parametrize("d_out,T", [(1, 1), (3, 1), (1, 3), (5, 8), (3, 16), (7, 40)])
+def test_few_output_columns(d_out, T):
+    """Fewer output columns than workgroups: most workgroups of the SpMV get
+    an empty run of column quads (they stage Z and end) and the one quad is
+    partial; T = 1 runs the one-launch decode with most workgroups holding
+    no column, T = 3, 8 and 16 the SpMV's token tiles, T = 40 the SpMM."""
+    say(f"case: d_out={d_out}, d_in=256, k=128, 2 layers, T={T}")
+    _wide_dictionary_group(100 + 10 * d_out + T, 256, d_out, 128, T, 2, 0.25)
+
+
 @pytest.mark.parametrize("T", [1, 5, 40])
 def test_largest_forward_k(T):
     """k = 16384, the most atoms a forward call accepts.  T = 1: decode;
