@@ -298,7 +298,7 @@ def main():
                   "median_us": round(float(np.median(rep_us)), 3),
                   "p90_us": round(float(np.percentile(rep_us, 90)), 3)}
 
-    # the box's own streaming rate: a 1 GiB device-to-device copy (read + write bytes)
+    # the device's own streaming rate: a 1 GiB device-to-device copy (read + write bytes)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -422,7 +422,7 @@ def main():
         res, spread = {}, {}
         # each: the median (and p10, p90) of N_REPLAYS timed replays of nrep
         # launches; the MFMA-heavy GEMM varies by up to 15% from replay to
-        # replay on the box, so one replay is not enough
+        # replay on this device, so one replay is not enough
         for name, fn in (
                 ("gemm_xd_mfma", lambda i: B.dict_xd_forward(Xp, reps[i % reps_p][0], Z=Zp)),
                 ("spmm_csc", lambda i: B.dict_zc_forward(Zp, gp.T, reps[i % reps_p][1], Ys=Yp)),
