@@ -582,6 +582,7 @@ dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t
   if (T == 0) return DFS_OK;
   DFS_TRY(check_y(Y, n_layers, ydt, ldy, C[0].d_out));
   if (!Z) return DFS_E_INVALID;
+  if (!aligned16(Z)) return DFS_E_ALIGN;  // Z rows are staged in 16-byte pieces
   return run_zc(n_layers, Z, zdt, T, C, Y, ydt, ldy, (hipStream_t)stream);
 }
 

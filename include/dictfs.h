@@ -346,7 +346,8 @@ dfs_status dict_xd_forward(int32_t n_layers, const void* const* X, int32_t xdt, 
 dfs_status dict_xd_workspace_size(int32_t n_layers, int32_t T, const dfs_dict* D, size_t* bytes);
 
 /* The second half of Eq. (1) alone: Y[l] = Z_l C[l], Z as written by
- * dict_xd_forward (row l*T + t of a (n_layers*T) x k array, dtype zdt). */
+ * dict_xd_forward (row l*T + t of a (n_layers*T) x k array, dtype zdt,
+ * 16-byte aligned: DFS_E_ALIGN otherwise). */
 dfs_status dict_zc_forward(int32_t n_layers, const void* Z, int32_t zdt, int32_t T,
                            const dfs_csc* C, void* const* Y, int32_t ydt, int64_t ldy,
                            void* stream);

@@ -337,6 +337,21 @@ def test_csc_capacity_is_checked():
     assert B.lib().dict_zc_forward(1, P, B.DFS_F32, 1, cs, yp, B.DFS_F16, 64, None) == RANGE
 
 
+def test_zc_forward_validation():
+    # Z is read in 16-byte pieces: a Z that dict_xd_forward would refuse is
+    # refused here too, before any launch
+    L = B.lib()
+    cs = (B.Csc * 1)(_csc())
+    yp = (C.c_void_p * 1)(P)
+    assert L.dict_zc_forward(1, P + 4, B.DFS_F32, 1, cs, yp, B.DFS_F16, 64, None) == ALIGN
+    assert L.dict_zc_forward(1, P + 8, B.DFS_F16, 3, cs, yp, B.DFS_F32, 64, None) == ALIGN
+    assert L.dict_zc_forward(1, 0, B.DFS_F32, 1, cs, yp, B.DFS_F16, 64, None) == INVALID
+    assert L.dict_zc_forward(1, P + 4, B.DFS_F32, 0, cs, yp, B.DFS_F16, 64, None) == OK  # no rows
+    assert L.dict_zc_forward(1, P, B.DFS_NVFP4, 1, cs, yp, B.DFS_F16, 64, None) == UNSUPPORTED
+    assert L.dict_zc_forward(1, P, B.DFS_F32, 1, cs, yp, B.DFS_F16, 10, None) == INVALID
+    assert L.dict_zc_forward(0, P, B.DFS_F32, 1, cs, yp, B.DFS_F16, 64, None) == INVALID
+
+
 @pytest.mark.parametrize("xdt,ddt,T,n", [(B.DFS_F32, B.DFS_F32, 32, 2), (B.DFS_F32, B.DFS_F16, 32, 2),
                                          (B.DFS_F16, B.DFS_F16, 32, 2), (B.DFS_F16, B.DFS_F32, 9, 2),
                                          (B.DFS_F16, B.DFS_F16, 1, 4), (B.DFS_F32, B.DFS_F16, 1, 3),
