@@ -74,6 +74,7 @@ dfs_status check_csc(const dfs_csc* C, int32_t k, int32_t d_out) {
   if (C->nnz < 0) return DFS_E_INVALID;
   if (C->nnz >= kMaxNnz) return DFS_E_RANGE;
   if (!C->colptr) return DFS_E_INVALID;
+  if ((uintptr_t)C->colptr % 4 != 0) return DFS_E_ALIGN;
   if (C->nnz > 0) {
     if (!C->rowidx) return DFS_E_INVALID;
     if (!aligned16(C->rowidx)) return DFS_E_ALIGN;
@@ -110,8 +111,10 @@ dfs_status check_x(const void* const* X, int32_t n, int32_t xdt, int64_t ldx, in
 dfs_status check_y(void* const* Y, int32_t n, int32_t ydt, int64_t ldy, int32_t d_out) {
   if (!is_act_dtype(ydt)) return DFS_E_UNSUPPORTED;
   if (ldy < d_out) return DFS_E_INVALID;
-  for (int i = 0; i < n; ++i)
+  for (int i = 0; i < n; ++i) {
     if (!Y[i]) return DFS_E_INVALID;
+    if ((uintptr_t)Y[i] % esize(ydt) != 0) return DFS_E_ALIGN;  // element stores
+  }
   return DFS_OK;
 }
 
@@ -336,6 +339,9 @@ dfs_status dict_pack_csc(const void* C, int32_t dtype, int32_t k, int32_t d_out,
   if (k > kMaxK) return DFS_E_RANGE;
   if ((rowidx == nullptr) != (vals == nullptr)) return DFS_E_INVALID;
   if (capacity < 0) return DFS_E_INVALID;
+  // the layout every reader of the arrays takes (see check_csc)
+  if ((uintptr_t)colptr % 4 != 0) return DFS_E_ALIGN;
+  if (rowidx && (!aligned16(rowidx) || !aligned16(vals))) return DFS_E_ALIGN;
   if (!ws || ws_bytes < pack_csc_ws_bytes(k, d_out)) return DFS_E_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   DFS_HIP(launch_pack_csc_count(C, dtype, k, d_out, ldc, colptr, ws, s));
@@ -389,6 +395,9 @@ dfs_status dict_pack_bcsc(const void* C, int32_t dtype, int32_t k, int32_t d_out
   if (k > kMaxK) return DFS_E_RANGE;
   if ((bidx == nullptr) != (vals == nullptr)) return DFS_E_INVALID;
   if (capacity < 0) return DFS_E_INVALID;
+  // the layout every reader of the arrays takes (see check_csc)
+  if ((uintptr_t)colptr % 4 != 0) return DFS_E_ALIGN;
+  if (bidx && (!aligned16(bidx) || !aligned16(vals))) return DFS_E_ALIGN;
   if (!ws || ws_bytes < pack_csc_ws_bytes(k, d_out)) return DFS_E_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   DFS_HIP(launch_pack_csc_count(C, dtype, k, d_out, ldc, colptr, ws, s, 8));

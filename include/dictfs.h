@@ -25,10 +25,12 @@
  *     call returns a non-zero dfs_status and writes nothing.  No C++
  *     exception crosses this boundary.  DFS_E_HIP means the HIP runtime
  *     reported an error; dfs_last_hip_error() returns its hipError_t code.
- *   - Base pointers of X, Y, D data, CSC arrays and NVFP4 codes must be
- *     16-byte aligned (DFS_E_ALIGN otherwise); leading dimensions of f16
- *     activations must be multiples of 8 elements and of f32 ones multiples of
- *     4, so that every row stays 16-byte aligned.
+ *   - Base pointers of X, D data, CSC row indices and values and NVFP4
+ *     codes must be 16-byte aligned (DFS_E_ALIGN otherwise); leading
+ *     dimensions of f16 X and D must be multiples of 8 elements and of f32
+ *     ones multiples of 4, so that every row stays 16-byte aligned.  Y and
+ *     the CSC column pointers need only the alignment of their element type
+ *     (Y is written one element at a time; ldy is any value >= d_out).
  *   - Accumulation is always fp32.  Results are deterministic run to run
  *     (no floating-point atomics).  The intermediate Z = X D_g is held in
  *     fp32 whenever X or D_g is fp32 (every path keeps it unrounded then);

@@ -84,6 +84,12 @@ def test_group_forward_validation():
     assert _group(ydt=B.DFS_NVFP4) == UNSUPPORTED
     assert _group(ldy=10) == INVALID
     assert _group(Y=0) == INVALID
+    # Y and the column pointers need only their element's alignment
+    assert _group(Y=P + 1) == ALIGN
+    assert _group(Y=P + 2, ydt=B.DFS_F32) == ALIGN
+    assert _group(Y=P + 2, ws_bytes=16) == WORKSPACE              # f16 Y: passes
+    assert _group(Cs=[_csc(colptr=P + 2)]) == ALIGN
+    assert _group(Cs=[_csc(colptr=P + 4)], ws_bytes=16) == WORKSPACE
     assert _group(Cs=[_csc(k=64)]) == INVALID       # k mismatch with D
     assert _group(Cs=[_csc(nnz=-1)]) == INVALID
     assert _group(Cs=[_csc(nnz=1 << 31)]) == RANGE
@@ -170,8 +176,16 @@ def test_pack_csc_validation():
     assert call(ldc=10) == INVALID
     assert call(rowidx=0) == INVALID          # rowidx and vals both or neither
     assert call(cap=-1) == INVALID
+    assert call(colptr=P + 2) == ALIGN        # int32 column pointers
+    assert call(rowidx=P + 2) == ALIGN        # the forward reads 16-byte chunks
+    assert call(vals=P + 8) == ALIGN
+    assert call(colptr=P + 4, rowidx=P + 32, vals=P + 48, ws=0) == WORKSPACE  # passes
+    assert call(rowidx=0, vals=0, colptr=P + 4, ws=0) == WORKSPACE           # count only
     assert call(ws=0) == WORKSPACE
     assert call(wsb=8) == WORKSPACE
+    for ca, cb, cc in ((P + 2, P, P), (P, P + 2, P), (P, P, P + 4)):
+        assert L.dict_pack_bcsc(P, B.DFS_F16, 128, 64, 64, ca, cb, cc, 16, C.byref(nnz), P,
+                                1 << 20, None) == ALIGN
     n = C.c_size_t(0)
     assert L.dict_pack_csc_workspace_size(65536, 11008, C.byref(n)) == OK and n.value > 0
     assert L.dict_pack_csc_workspace_size(65537, 11008, C.byref(n)) == RANGE
