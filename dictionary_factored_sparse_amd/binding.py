@@ -141,6 +141,23 @@ def _dt(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _rows(ts, what: str, width: int | None = None) -> None:
+    """The C calls take one pointer per layer and ONE leading dimension and
+    dtype for all of them: every tensor must be a 2-D row-major view with
+    unit column stride, and all must agree in shape, stride, dtype and
+    device."""
+    t0 = ts[0]
+    for t in ts:
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError(f"{what}: 2-D row-major tensors with unit column stride required")
+        if (t.shape != t0.shape or t.stride(0) != t0.stride(0) or t.dtype != t0.dtype
+                or t.device != t0.device):
+            raise ValueError(f"{what}: every layer needs the same shape, row stride, dtype and "
+                             "device")
+    if width is not None and t0.shape[1] != width:
+        raise ValueError(f"{what}: {t0.shape[1]} columns, expected {width}")
+
+
 def _torch_dt(code: int):
     return {DFS_F16: torch.float16, DFS_F32: torch.float32}[code]
 
@@ -374,6 +391,10 @@ def dict_group_forward(Xs, D: DeviceDict, Cs, Ys=None, ydtype=torch.float16, ws=
     dev = Xs[0].device
     if Ys is None:
         Ys = [torch.empty(T, d_out, dtype=ydtype, device=dev) for _ in range(n)]
+    _rows(Xs, "X", D.d_in)
+    _rows(Ys, "Y", d_out)
+    if len(Ys) != n or len(Cs) != n or Ys[0].shape[0] != T:
+        raise ValueError("one X, one C and one Y of T rows per layer")
     if ws is None:
         ws = workspace(n, T, D, Cs[0], dev)
     xp = (C.c_void_p * n)(*[x.data_ptr() for x in Xs])
@@ -392,6 +413,10 @@ def dict_group_forward_noalloc(Xs, D: DeviceDict, Cs, Ys, stream=None):
     the call; Ys must be given)."""
     n = len(Xs)
     T = Xs[0].shape[0]
+    _rows(Xs, "X", D.d_in)
+    _rows(Ys, "Y", Cs[0].d_out)
+    if len(Ys) != n or len(Cs) != n or Ys[0].shape[0] != T:
+        raise ValueError("one X, one C and one Y of T rows per layer")
     xp = (C.c_void_p * n)(*[x.data_ptr() for x in Xs])
     yp = (C.c_void_p * n)(*[y.data_ptr() for y in Ys])
     cs = (Csc * n)(*[c.desc() for c in Cs])
@@ -424,6 +449,10 @@ def dict_multi_forward(Xs, Ds, Cs, Ys=None, ydtype=torch.float16, ws=None, strea
     dev = Xs[0].device
     if Ys is None:
         Ys = [torch.empty(T, Cs[0].d_out, dtype=ydtype, device=dev) for _ in range(n * nd)]
+    _rows(Xs, "X", Ds[0].d_in)
+    _rows(Ys, "Y", Cs[0].d_out)
+    if len(Ys) != n * nd or Ys[0].shape[0] != T:
+        raise ValueError("one Y of T rows per (dictionary, layer)")
     if ws is None:
         ws = multi_workspace(nd, n, T, Ds[0], Cs[0], dev)
     xp = (C.c_void_p * n)(*[x.data_ptr() for x in Xs])
@@ -442,6 +471,10 @@ def dict_proj_forward(X, D: DeviceDict, Cs: DeviceCSC, Y=None, ydtype=torch.floa
     T = X.shape[0]
     if Y is None:
         Y = torch.empty(T, Cs.d_out, dtype=ydtype, device=X.device)
+    _rows([X], "X", D.d_in)
+    _rows([Y], "Y", Cs.d_out)
+    if Y.shape[0] != T:
+        raise ValueError("Y needs the T rows of X")
     if ws is None:
         ws = workspace(1, T, D, Cs, X.device)
     d, c = D.desc(), Cs.desc()
@@ -457,6 +490,9 @@ def dict_xd_forward(Xs, D: DeviceDict, zdtype=torch.float32, Z=None, ws=None, st
     T = Xs[0].shape[0]
     if Z is None:
         Z = torch.empty(n * T, D.k, dtype=zdtype, device=Xs[0].device)
+    _rows(Xs, "X", D.d_in)
+    if not Z.is_contiguous() or Z.shape != (n * T, D.k):
+        raise ValueError(f"Z: a contiguous ({n * T}, {D.k}) tensor required")
     d = D.desc()
     need = C.c_size_t(0)
     _check("dict_xd_workspace_size",
@@ -476,6 +512,11 @@ def dict_zc_forward(Z, T: int, Cs, Ys=None, ydtype=torch.float16, stream=None):
     d_out = Cs[0].d_out
     if Ys is None:
         Ys = [torch.empty(T, d_out, dtype=ydtype, device=Z.device) for _ in range(n)]
+    _rows(Ys, "Y", d_out)
+    if len(Ys) != n or Ys[0].shape[0] != T:
+        raise ValueError("one Y of T rows per layer")
+    if not Z.is_contiguous() or Z.shape != (n * T, Cs[0].k):
+        raise ValueError(f"Z: a contiguous ({n * T}, {Cs[0].k}) tensor required")
     yp = (C.c_void_p * n)(*[y.data_ptr() for y in Ys])
     cs = (Csc * n)(*[c.desc() for c in Cs])
     _check("dict_zc_forward",

@@ -427,3 +427,31 @@ def test_read_probe_rejects_before_any_launch():
     assert L.dfs_probe_read(P + 8, 4096, 4, P, None) == ALIGN
     assert L.dfs_probe_read(P, 4100, 4, P, None) == ALIGN
     assert L.dfs_probe_read(P, 4096, (1 << 20) + 1, P, None) == RANGE
+
+
+def test_binding_rejects_layers_that_do_not_share_one_layout():
+    # the C calls take one leading dimension and dtype for every layer's X
+    # and Y: the binding refuses lists that disagree before any call
+    import types
+
+    import torch
+    D = B.DeviceDict(64, 16, data=torch.zeros(16, 64, dtype=torch.float16))
+    c = types.SimpleNamespace(d_out=32, k=16)
+    X = torch.zeros(2, 64, dtype=torch.float16)
+    Y = torch.zeros(2, 32, dtype=torch.float16)
+    bad_groups = [
+        ([X, torch.zeros(2, 72, dtype=torch.float16)[:, :64]], [Y, Y]),  # row strides differ
+        ([X, X.float()], [Y, Y]),                                         # dtypes differ
+        ([X, X[:1]], [Y, Y]),                                             # token counts differ
+        ([X, X], [Y, torch.zeros(32, 2, dtype=torch.float16).t()]),       # transposed view
+        ([X[:, :60], X[:, :60]], [Y, Y]),                                 # not d_in columns
+        ([X, X], [Y[:, :30], Y[:, :30]]),                                 # not d_out columns
+        ([X, X], [Y[:1], Y[:1]]),                                         # Y rows != T
+    ]
+    for Xs, Ys in bad_groups:
+        with pytest.raises(ValueError):
+            B.dict_group_forward(Xs, D, [c, c], Ys=Ys)
+    with pytest.raises(ValueError):
+        B.dict_zc_forward(torch.zeros(16, 4).t(), 2, [c, c], Ys=[Y, Y])   # Z not contiguous
+    with pytest.raises(ValueError):
+        B.dict_xd_forward([X, X], D, Z=torch.zeros(4, 8))                 # Z not (n*T, k)
