@@ -39,8 +39,10 @@
  *     the f16 Z tiles the coefficient kernels use when an fp32 tile would
  *     not fit their LDS.
  *   - Thread safety: calls hold no mutable global state beyond a per-thread
- *     last-HIP-error code; concurrent calls on different streams are safe
- *     when they do not share a workspace.  The one-launch decode runs one
+ *     last-HIP-error code and per-device facts looked up once (the CU count,
+ *     the address of the no-allocation workspace, under a lock); concurrent
+ *     calls on different streams are safe when they do not share a
+ *     workspace.  The one-launch decode runs one
  *     workgroup per CU and hands Z between them; if two such launches (or
  *     other kernels) share the GPU, the bounded waits described under
  *     dict_workspace_size keep the results right, at a cost in time.
