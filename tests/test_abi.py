@@ -455,3 +455,46 @@ def test_binding_rejects_layers_that_do_not_share_one_layout():
         B.dict_zc_forward(torch.zeros(16, 4).t(), 2, [c, c], Ys=[Y, Y])   # Z not contiguous
     with pytest.raises(ValueError):
         B.dict_xd_forward([X, X], D, Z=torch.zeros(4, 8))                 # Z not (n*T, k)
+
+
+C_USER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "dictfs.h"
+int main(void) {
+  size_t n = 0;
+  dfs_dict d;
+  dfs_csc c;
+  memset(&d, 0, sizeof d);
+  memset(&c, 0, sizeof c);
+  if (dfs_version() <= 0) return 1;
+  if (dict_csc_capacity(13) != 16 || dict_csc_capacity(0) != 8) return 2;
+  if (strcmp(dfs_status_str(DFS_E_ALIGN), "misaligned pointer or leading dimension") != 0) return 3;
+  /* validation fails before anything reaches a GPU */
+  if (dict_workspace_size(1, 1, &d, &c, &n) != DFS_E_INVALID) return 4;
+  if (dict_group_forward(0, NULL, DFS_F16, 1, 8, &d, &c, NULL, DFS_F16, 8, NULL, 0, NULL)
+      != DFS_E_INVALID) return 5;
+  printf("ok\n");
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # the boundary is a C ABI: a C99 program compiles against the header with
+    # every warning as an error, links the library and calls its host checks
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "use.c"
+    src.write_text(C_USER)
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(B.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", libdir, "-l:" + os.path.basename(B.LIB_PATH), "-Wl,-rpath," + libdir],
+                   check=True, capture_output=True, timeout=120)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
