@@ -279,6 +279,41 @@ def test_xd_and_zc_entry_points():
             assert_close(Ys[l], ref, f"zc layer {l} {zdt}")
 
 
+@pytest.mark.parametrize("k,T,cfmt", [(200, 40, "plain"), (203, 100, "plain"), (200, 40, "fp8"),
+                                      (203, 33, "nvfp4")])
+def test_zc_fp32_z_many_tokens(k, T, cfmt):
+    """Y = Z C from an fp32 Z of more than 16 tokens per layer: the SpMV
+    passes over the tokens in fp32 tiles (the SpMM takes f16 Z only);
+    k = 203 stages the Z rows element by element."""
+    say(f"case: dict_zc_forward, fp32 Z, k={k}, 2 x T={T}, C {cfmt}")
+    g = synth.make_group("qproj", d_in=512, d_out=300, k=k, T=T, n_layers=2)
+    D, Cs, Xs = device_group(g, cfmt=cfmt)
+    Z = B.dict_xd_forward(Xs, D, zdtype=torch.float32)
+    Ys = B.dict_zc_forward(Z, T, Cs, ydtype=torch.float32)
+    torch.cuda.synchronize()
+    for l, ref in enumerate(oracle_group(g, cfmt=cfmt)):
+        assert_close(Ys[l], ref, f"fp32 Z, k={k}, T={T}, C {cfmt}, layer {l}")
+
+
+def test_zc_fp32_z_block_coefficients_many_tokens():
+    # the same for block-structured C (8-atom blocks, the last one past k)
+    say("case: dict_zc_forward, fp32 Z, block-structured C, k=203, 2 x T=40")
+    rng = np.random.default_rng(41)
+    d_in, k, d_out, T = 256, 203, 150, 40
+    Qm, _ = np.linalg.qr(rng.standard_normal((d_in, k)))
+    Dt = np.ascontiguousarray((Qm.T * 64 / np.sqrt(d_in)).astype(np.float16))
+    Cs = [synth.block_coefficients(rng, k, d_out, 0.5, np.float16) for _ in range(2)]
+    Xs = [rng.standard_normal((T, d_in)).astype(np.float16) for _ in range(2)]
+    D = B.to_device_dict(Dt, DEV)
+    Z = B.dict_xd_forward([torch.from_numpy(x).to(DEV) for x in Xs], D, zdtype=torch.float32)
+    Cg = [B.dict_pack_bcsc(torch.from_numpy(c).to(DEV)) for c in Cs]
+    Ys = B.dict_zc_forward(Z, T, Cg, ydtype=torch.float32)
+    torch.cuda.synchronize()
+    for l in range(2):
+        ref = O.forward_bcsc(Xs[l], Dt, d_in, O.pack_bcsc(Cs[l]))
+        assert_close(Ys[l], ref, f"fp32 Z, block C, layer {l}")
+
+
 @pytest.mark.parametrize("d_in,k,T", [(512, 200, 150), (512, 202, 150), (1032, 264, 40),
                                       (1032, 262, 40)])
 def test_mfma_output_tile_forms(d_in, k, T):
