@@ -147,3 +147,32 @@ def test_fp32_z_keeps_its_range(d_in, k, T):
     assert zmax > 65504.0
     for l, ref in enumerate(oracle_group(g)):
         assert_close(Ys[l], ref, f"layer {l}")
+
+
+def test_two_decodes_on_two_streams():
+    # two one-launch decodes of the MLP gate group (about 82 KiB of LDS per
+    # workgroup: one workgroup per CU) issued on two streams, so that their
+    # grids may share the CUs and neither be resident whole.  A workgroup
+    # whose wait gives up (bound: 2000 polls, a few milliseconds) computes its
+    # Z words itself; every result matches the oracle either way.
+    say("case: two MLP gate decodes on two streams, poll bound 2000, 8 rounds")
+    gs = [synth.make_group("mlp", ptype="gate", group=g, T=1) for g in (0, 1)]
+    devs = [device_group(g) for g in gs]
+    wss = [B.workspace(4, 1, d[0], d[1][0], DEV) for d in devs]
+    refs = [oracle_group(g) for g in gs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    rounds = 8
+    Ys = [[[torch.empty(1, gs[0].d_out, dtype=torch.float16, device=DEV) for _ in range(4)]
+           for _ in range(2)] for _ in range(rounds)]
+    torch.cuda.synchronize()
+    with _spin_limit(2000):
+        for r in range(rounds):
+            for i in range(2):
+                D, Cs, Xs = devs[i]
+                B.dict_group_forward(Xs, D, Cs, Ys=Ys[r][i], ws=wss[i], stream=streams[i])
+        torch.cuda.synchronize()
+    say("diagnostic words: " + str([B.workspace_error_word(w) for w in wss]))
+    for r in range(rounds):
+        for i in range(2):
+            for l in range(4):
+                assert_close(Ys[r][i][l], refs[i][l], f"round {r} stream {i} layer {l}")
